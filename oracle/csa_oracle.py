@@ -1,0 +1,270 @@
+"""fp64 numpy oracle of the compressed attention layer forward.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU-baseline
+leg of the benchmark; never by the product path.
+
+Every function consumes float64 arrays (bf16 or fp32 inputs are upcast losslessly by
+the caller) and computes in float64.  No online softmax, no fusion, no blocking
+beyond looping over queries.  Sources, cited by page title and section:
+
+  [PR930] "fix(deepseek-v4): correct V4-Flash attention math, wire the MoE balance
+          loss", Part 1 "Attention correctness", items 1 (scale), 2 (compressed RoPE
+          positions and base), 3 (output de-rotation), 4 (indexer precision).
+  [BLOG]  "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+          Primus", section "The DeepSeek-V4-Flash architecture", subsection "Three
+          attention types, interleaved" (pooling, overlap, indexer, window), and
+          section "Kernel fusions" (compressor pooling, interleaved partial RoPE,
+          RMSNorm).
+
+Readings taken where the pages leave a step open (listed in the design doc as well):
+  * CSA entry 0 has no previous group: those slots get logit -inf.
+  * Bias row j is pooling slot j in token order (CSA: rows 0..r-1 are the previous
+    group read from the b projections, rows r..2r-1 the entry's own group read from
+    the a projections).
+  * Entry s is visible to query t iff its whole group is seen: (s+1)*r - 1 <= t.
+  * RMSNorm has weight 1 and eps 1e-6, applied before RoPE.
+  * RoPE is interleaved (adjacent pairs) on the last R dims, angle
+    P * theta**(-2i/R), no frequency interpolation.
+  * Window keys are the raw latents of tokens t-W+1..t (clipped at 0), rotated at
+    their own positions and not normalised (unless norm_window is set).
+  * One softmax over the union of selected entries and window keys.
+  * Top-k ties break to the smaller entry index.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_angles", "rope", "gated_pool", "rms_norm", "compress", "visible_entries",
+    "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
+    "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
+]
+
+
+def rope_angles(pos, rope_dim: int, theta: float) -> np.ndarray:
+    """Angles P * theta**(-2i/R) for i = 0..R/2-1 ([PR930] item 2: the compressed base
+    theta = 40000 for Flash).  `pos` is an integer array; result has shape
+    pos.shape + (R/2,)."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    inv_freq = np.power(np.float64(theta), -2.0 * i / rope_dim)
+    return np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+
+
+def rope(x: np.ndarray, pos, rope_dim: int, theta: float) -> np.ndarray:
+    """Interleaved partial RoPE on the last `rope_dim` dims of x ([BLOG] "Kernel
+    fusions": interleaved partial RoPE).  Pair i is (x[D-R+2i], x[D-R+2i+1]) and is
+    rotated by +angle: (x0 cos - x1 sin, x0 sin + x1 cos).  `pos` broadcasts against
+    x.shape[:-1]; a negative position is the inverse rotation."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    if rope_dim == 0:
+        return x
+    D = x.shape[-1]
+    ang = rope_angles(pos, rope_dim, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    lo = D - rope_dim
+    x0 = x[..., lo::2].copy()
+    x1 = x[..., lo + 1::2].copy()
+    x[..., lo::2] = x0 * c - x1 * s
+    x[..., lo + 1::2] = x0 * s + x1 * c
+    return x
+
+
+def gated_pool(va, ga, vb, gb, bias, ratio: int, overlap: bool) -> np.ndarray:
+    """Softmax-gated pooling ([BLOG] "Three attention types, interleaved": a softmax
+    over the group of gate plus a learnable per-position bias weights the sum of the
+    values; CSA entries pool their own `ratio` tokens plus the previous `ratio`).
+
+    va, ga, vb, gb: [S, D] (vb, gb unused when overlap is False); bias [span, D].
+    Returns p [S/ratio, D].
+
+    Entry s, slot j:
+      overlap: token tau_j = s*r - r + j; j < r reads (vb, gb), j >= r reads (va, ga);
+               a slot whose token is before 0 gets logit -inf.
+      disjoint: token tau_j = s*r + j, read from (va, ga).
+    """
+    S, D = va.shape
+    r = ratio
+    n = S // r
+    own_v = va[: n * r].reshape(n, r, D)
+    own_g = ga[: n * r].reshape(n, r, D)
+    if overlap:
+        prev_v = np.zeros((n, r, D))
+        prev_g = np.full((n, r, D), -np.inf)
+        if n > 1:
+            prev_v[1:] = vb[: (n - 1) * r].reshape(n - 1, r, D)
+            prev_g[1:] = gb[: (n - 1) * r].reshape(n - 1, r, D)
+        v = np.concatenate([prev_v, own_v], axis=1)  # [n, 2r, D]
+        logit = np.concatenate([prev_g, own_g], axis=1) + bias[None, :, :]
+    else:
+        v = own_v
+        logit = own_g + bias[None, :, :]
+    m = np.max(logit, axis=1, keepdims=True)
+    e = np.exp(logit - m)
+    alpha = e / np.sum(e, axis=1, keepdims=True)
+    return np.sum(alpha * v, axis=1)
+
+
+def rms_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis, weight 1 ([PR930] item 1: V4
+    RMS-normalises the KV entries directly)."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def compress(va, ga, vb, gb, bias, ratio, overlap, rope_dim, theta, eps, pos0=0):
+    """Pool, RMS-normalise, then rotate entry s at its original-sequence position
+    pos0 + s*ratio ([PR930] item 2: entry s covers the window starting at s*ratio).
+    Returns kv_c [S/ratio, D]."""
+    p = gated_pool(va, ga, vb, gb, bias, ratio, overlap)
+    nrm = rms_norm(p, eps)
+    pos = pos0 + np.arange(p.shape[0], dtype=np.int64) * ratio
+    return rope(nrm, pos, rope_dim, theta)
+
+
+def visible_entries(t: int, ratio: int) -> int:
+    """n_t: entries whose last token (s+1)*ratio - 1 is at or before t."""
+    return (t + 1) // ratio
+
+
+def window_bounds(t: int, window: int):
+    """Window tokens lo..t inclusive, lo = max(0, t - W + 1)."""
+    return max(0, t - window + 1), t
+
+
+def indexer_scores_row(q_i_t, w_t, k_i, n_vis: int) -> np.ndarray:
+    """Lightning-indexer scores of query t over its visible entries ([PR930] item 6a
+    and [BLOG] "Three attention types": I[t,s] = sum_h w[t,h] * ReLU(q_I[t,h].k_I[s])),
+    in fp64 ([PR930] item 4 keeps the indexer product in high precision).
+    q_i_t [H_I, D_I], w_t [H_I], k_i [n, D_I].  Returns [n_vis]."""
+    if n_vis == 0:
+        return np.zeros(0)
+    dots = q_i_t @ k_i[:n_vis].T  # [H_I, n_vis]
+    return w_t @ np.maximum(dots, 0.0)
+
+
+def indexer_scores(q_i, w, k_i, ratio: int) -> list:
+    """Scores for every query, as a list of rows of length n_t."""
+    S = q_i.shape[0]
+    return [indexer_scores_row(q_i[t], w[t], k_i, visible_entries(t, ratio)) for t in range(S)]
+
+
+def topk_row(scores_row: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the min(k, n) largest scores, ordered by (-score, index): ties go to
+    the smaller index.  Returned sorted ascending."""
+    n = scores_row.shape[0]
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(n), -scores_row))
+    return np.sort(order[: min(k, n)])
+
+
+def topk(scores_rows: list, k: int) -> list:
+    return [topk_row(r, k) for r in scores_rows]
+
+
+def rotate_queries(q, rope_dim, theta, pos0=0):
+    """q [S, H, D] rotated at pos0 + t."""
+    S = q.shape[0]
+    pos = (pos0 + np.arange(S, dtype=np.int64))[:, None]
+    return rope(q, pos, rope_dim, theta)
+
+
+def rotate_window(kv_raw, rope_dim, theta, eps, pos0=0, norm_window=False):
+    """Raw per-token latents rotated at their own positions (optionally normalised)."""
+    x = rms_norm(kv_raw, eps) if norm_window else kv_raw
+    pos = pos0 + np.arange(kv_raw.shape[0], dtype=np.int64)
+    return rope(x, pos, rope_dim, theta)
+
+
+def attend_row(qr_t, keys, scale: float):
+    """One query's multi-query attention: z = (q.key) * scale for every head and key,
+    one softmax over all keys, u = sum P key (K = V, [BLOG] "The DeepSeek-V4-Flash
+    architecture").  qr_t [H, D] (already rotated), keys [nk, D].  Returns (u [H, D],
+    P [H, nk])."""
+    z = (qr_t @ keys.T) * scale
+    m = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - m)
+    P = e / np.sum(e, axis=1, keepdims=True)
+    return P @ keys, P
+
+
+def _as64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_p=False):
+    """Oracle outputs for the query rows `rows` of batch 0..B-1 (rows is a list of
+    (b, t) pairs).  `inp` holds numpy arrays (any float dtype) with the shapes of
+    workloads.make_inputs.  `sel_override` maps (b, t) to a selection to use instead
+    of the oracle's own top-k (for re-evaluating on another admissible selection).
+
+    Returns a dict: o {(b,t): [H,D]}, sel {(b,t): indices}, scores {(b,t): row},
+    n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, and P when
+    want_p.  Steps, per [PR930] Part 1 and [BLOG] "Three attention types":
+      1 pool + norm + rotate entries at pos0 + s*r   (CSA, HCA)
+      2 rotate queries at pos0 + t and window tokens at pos0 + t'
+      3 indexer scores over visible entries          (CSA)
+      4 top-k (CSA) / all visible (HCA) / none (window-only)
+      5 one softmax over selected entries plus window, scale D**-0.5 ([PR930] item 1)
+      6 de-rotate the output at -(pos0 + t)          ([PR930] item 3)
+    """
+    kind = cfg.kind
+    R, theta, eps, pos0 = cfg.rope_dim, cfg.rope_theta, cfg.rms_eps, cfg.pos0
+    scale = cfg.D ** -0.5 if getattr(cfg, "softmax_scale", None) is None else cfg.softmax_scale
+    norm_window = bool(getattr(cfg, "norm_window", False))
+    out = {"o": {}, "sel": {}, "scores": {}, "n_visible": {}, "win": {}, "kv_c": {}, "P": {}}
+    batches = sorted({b for b, _ in rows})
+    for b in batches:
+        if kind in ("csa", "hca"):
+            if kv_c is not None:
+                kvb = np.asarray(kv_c[b], dtype=np.float64)
+            else:
+                kvb = compress(_as64(inp["va"][b]), _as64(inp["ga"][b]),
+                               _as64(inp["vb"][b]) if kind == "csa" else None,
+                               _as64(inp["gb"][b]) if kind == "csa" else None,
+                               _as64(inp["bias"]), cfg.ratio, kind == "csa", R, theta, eps, pos0)
+            out["kv_c"][b] = kvb
+        kv_raw_b = inp["kv_raw"][b]
+        ts = [t for bb, t in rows if bb == b]
+        for t in ts:
+            lo, hi = window_bounds(t, cfg.window)
+            win_keys = rotate_window(_as64(kv_raw_b[lo:hi + 1]), R, theta, eps, pos0 + lo, norm_window)
+            if kind == "swa":
+                n_vis, sel = 0, np.zeros(0, dtype=np.int64)
+                ent_keys = np.zeros((0, cfg.D))
+            else:
+                n_vis = visible_entries(t, cfg.ratio)
+                if sel_override is not None and (b, t) in sel_override:
+                    sel = np.sort(np.asarray(sel_override[(b, t)], dtype=np.int64))
+                    if kind == "csa":
+                        out["scores"][(b, t)] = indexer_scores_row(
+                            _as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t]),
+                            _as64(inp["k_idx"][b]), n_vis)
+                elif kind == "csa":
+                    sc = indexer_scores_row(_as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t]),
+                                            _as64(inp["k_idx"][b]), n_vis)
+                    out["scores"][(b, t)] = sc
+                    sel = topk_row(sc, cfg.topk)
+                else:
+                    sel = np.arange(n_vis, dtype=np.int64)
+                ent_keys = kvb[sel]
+            keys = np.concatenate([ent_keys, win_keys], axis=0)
+            qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
+            u, P = attend_row(qr, keys, scale)
+            out["o"][(b, t)] = rope(u, -(pos0 + t), R, theta)
+            out["sel"][(b, t)] = sel
+            out["n_visible"][(b, t)] = n_vis
+            out["win"][(b, t)] = (lo, hi)
+            if want_p:
+                out["P"][(b, t)] = P
+    return out
+
+
+def layer_forward(cfg, inp: dict, want_p=False) -> dict:
+    """Whole-layer oracle: o [B, S, H, D] plus kv_c, selections, scores and layout."""
+    rows = [(b, t) for b in range(cfg.B) for t in range(cfg.S)]
+    r = layer_rows(cfg, inp, rows, want_p=want_p)
+    o = np.zeros((cfg.B, cfg.S, cfg.H, cfg.D))
+    for (b, t), v in r["o"].items():
+        o[b, t] = v
+    r["o_full"] = o
+    return r

@@ -1,0 +1,334 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+None of these re-types the oracle's formula: each checks a closed form, an
+invariant, a library special case, a printed constant, or the independent
+pure-Python brute force.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import to_np
+from compressed_sparse_attention_hca_amd import workloads as wl
+from oracle import csa_oracle as O
+from oracle import brute
+
+
+def tiny(kind="csa", **kw):
+    base = dict(name="t", kind=kind, B=1, S=32, H=2, D=16, rope_dim=8, ratio=4, window=6,
+                topk=3, idx_heads=3, idx_dim=4, dtype=wl.F32, seed=7)
+    if kind == "hca":
+        base.update(ratio=8, topk=0)
+    if kind == "swa":
+        base.update(topk=0)
+    base.update(kw)
+    return wl.LayerConfig(**base)
+
+
+# ---------------------------------------------------------------- pooling ----------
+
+def test_pool_uniform_gates_zero_bias_is_plain_mean(rng):
+    """Uniform gate logits and zero bias make pooling a plain mean of the tokens the
+    entry covers; CSA entry 0 (no previous group) averages only its own 4 tokens."""
+    S, D, r = 24, 5, 4
+    va, vb = rng.normal(size=(S, D)), rng.normal(size=(S, D))
+    g = np.full((S, D), 0.37)
+    p = O.gated_pool(va, g, vb, g, np.zeros((2 * r, D)), r, True)
+    assert np.allclose(p[0], va[0:4].mean(0), atol=1e-14)
+    for s in range(1, S // r):
+        want = (vb[s * r - r:s * r].sum(0) + va[s * r:s * r + r].sum(0)) / 8
+        assert np.allclose(p[s], want, atol=1e-14)
+    ph = O.gated_pool(va, g, None, None, np.zeros((8, D)), 8, False)
+    for s in range(S // 8):
+        assert np.allclose(ph[s], va[s * 8:s * 8 + 8].mean(0), atol=1e-14)
+
+
+@pytest.mark.parametrize("j", range(8))
+def test_pool_dominant_gate_selects_slot_token(rng, j):
+    """A +60 gate on slot j makes the entry equal to that slot's token: slots 0-3 are
+    the previous group from the b projections, slots 4-7 the own group from a."""
+    S, D, r = 20, 3, 4
+    va, vb = rng.normal(size=(S, D)), rng.normal(size=(S, D))
+    ga, gb = np.zeros((S, D)), np.zeros((S, D))
+    s = 3
+    tok = s * r - r + j
+    if j < r:
+        gb[tok] = 60.0
+        want = vb[tok]
+    else:
+        ga[tok] = 60.0
+        want = va[tok]
+    p = O.gated_pool(va, ga, vb, gb, np.zeros((8, D)), r, True)
+    assert np.allclose(p[s], want, atol=1e-20 + 1e-12)
+
+
+@pytest.mark.parametrize("j", [0, 3, 5, 7])
+def test_pool_bias_row_is_slot(rng, j):
+    """Bias row j weights slot j (token order), not a transposed or reversed row."""
+    S, D, r = 16, 4, 4
+    va, vb = rng.normal(size=(S, D)), rng.normal(size=(S, D))
+    z = np.zeros((S, D))
+    bias = np.zeros((8, D))
+    bias[j] = 80.0
+    p = O.gated_pool(va, z, vb, z, bias, r, True)
+    s = 2
+    want = vb[s * r - r + j] if j < r else va[s * r - r + j]
+    assert np.allclose(p[s], want, atol=1e-12)
+
+
+def test_pool_hca_ratio1_is_identity(rng):
+    va = rng.normal(size=(9, 6))
+    p = O.gated_pool(va, rng.normal(size=(9, 6)), None, None, rng.normal(size=(1, 6)), 1, False)
+    assert np.array_equal(p, va)
+
+
+def test_pool_convex_combination(rng):
+    """Per channel the weights sum to 1: pooling constant values returns the constant."""
+    S, D = 16, 7
+    c = rng.normal(size=(1, D))
+    v = np.repeat(c, S, axis=0)
+    p = O.gated_pool(v, rng.normal(size=(S, D)), v, rng.normal(size=(S, D)),
+                     rng.normal(size=(8, D)), 4, True)
+    assert np.allclose(p, np.repeat(c, S // 4, axis=0), atol=1e-14)
+
+
+# ------------------------------------------------------------ norm & RoPE ----------
+
+def test_rms_norm_unit_rms(rng):
+    x = rng.normal(size=(10, 64)) * 3
+    n = O.rms_norm(x, 0.0)
+    assert np.allclose(np.sqrt((n * n).mean(-1)), 1.0, atol=1e-14)
+    n2 = O.rms_norm(x, 1e-6)
+    ms = (x * x).mean(-1)
+    assert np.allclose(np.sqrt((n2 * n2).mean(-1)), np.sqrt(ms / (ms + 1e-6)), atol=1e-14)
+
+
+def test_rope_closed_form_interleaved_last_dims():
+    """A unit pair (1, 0) at pair i comes out as (cos a, sin a), a = P*40000**(-2i/R);
+    the first D-R dims are untouched (partial RoPE on the last dims, interleaved)."""
+    D, R, P = 12, 8, 17
+    for i in range(R // 2):
+        x = np.zeros(D)
+        x[:D - R] = np.arange(1, D - R + 1)
+        x[D - R + 2 * i] = 1.0
+        y = O.rope(x, P, R, 40000.0)
+        a = P * 40000.0 ** (-(2 * i) / R)
+        assert np.array_equal(y[:D - R], x[:D - R])
+        assert abs(y[D - R + 2 * i] - math.cos(a)) < 1e-15
+        assert abs(y[D - R + 2 * i + 1] - math.sin(a)) < 1e-15
+        others = [k for k in range(D - R, D) if k not in (D - R + 2 * i, D - R + 2 * i + 1)]
+        assert np.all(y[others] == 0)
+
+
+def test_rope_inverse_zero_and_relative(rng):
+    D, R = 32, 16
+    x = rng.normal(size=(5, D))
+    assert np.allclose(O.rope(O.rope(x, 12345, R, 4e4), -12345, R, 4e4), x, atol=1e-12)
+    assert np.array_equal(O.rope(x, 0, R, 4e4), x)
+    a, b = rng.normal(size=D), rng.normal(size=D)
+    d1 = O.rope(a, 100, R, 4e4) @ O.rope(b, 37, R, 4e4)
+    d2 = O.rope(a, 1063, R, 4e4) @ O.rope(b, 1000, R, 4e4)
+    assert abs(d1 - d2) < 1e-11
+
+
+def test_compressed_position_is_s_times_ratio():
+    """Position probe (uses ratio > 1 and entry index > 0, where the two conventions
+    differ): after pooling to a known vector, entry s carries rotation pos0 + s*r."""
+    D, R, r, pos0 = 8, 4, 4, 5
+    S = 16
+    # every token's value is the same vector, so every pooled entry equals it
+    base = np.array([1.0, -1.0, 1.0, -1.0, 1.0, 0.0, 1.0, 0.0])
+    v = np.repeat(base[None], S, axis=0)
+    z = np.zeros((S, D))
+    kv = O.compress(v, z, v, z, np.zeros((8, D)), r, True, R, 40000.0, 0.0, pos0)
+    rms = math.sqrt((base ** 2).mean())
+    for s in range(S // r):
+        P = pos0 + s * r
+        for i in range(R // 2):
+            a = P * 40000.0 ** (-(2 * i) / R)
+            assert abs(kv[s, D - R + 2 * i] - math.cos(a) / rms) < 1e-14
+            assert abs(kv[s, D - R + 2 * i + 1] - math.sin(a) / rms) < 1e-14
+        wrong = pos0 + s
+        if s > 0:
+            assert abs(kv[s, D - R] - math.cos(wrong) / rms) > 1e-3
+
+
+# ------------------------------------------------------------- indexer -------------
+
+def test_indexer_hand_example():
+    """I[t,s] = sum_h w_h ReLU(q_h . k_s) on a hand-computed case."""
+    q = np.array([[1.0, 2.0], [-1.0, 0.5]])  # 2 heads x 2 dims
+    w = np.array([0.5, 2.0])
+    k = np.array([[1.0, 1.0], [2.0, -1.0], [-3.0, 1.0]])
+    # head0 dots: 3, 0, -1 -> relu 3, 0, 0 ; head1 dots: -0.5, -2.5, 3.5 -> 0, 0, 3.5
+    want = np.array([0.5 * 3, 0.0, 2.0 * 3.5])
+    assert np.allclose(O.indexer_scores_row(q, w, k, 3), want, atol=0)
+    assert np.allclose(O.indexer_scores_row(q, w, k, 2), want[:2], atol=0)
+
+
+def test_visibility_and_window_layout():
+    assert [O.visible_entries(t, 4) for t in range(10)] == [0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
+    assert O.visible_entries(127, 128) == 1 and O.visible_entries(126, 128) == 0
+    assert O.window_bounds(0, 128) == (0, 0)
+    assert O.window_bounds(200, 128) == (73, 200)
+
+
+def test_topk_ties_and_small_rows():
+    sc = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
+    assert list(O.topk_row(sc, 2)) == [1, 2]
+    assert list(O.topk_row(sc, 4)) == [1, 2, 3, 4]
+    assert list(O.topk_row(sc, 9)) == [0, 1, 2, 3, 4]
+    assert list(O.topk_row(np.zeros(0), 3)) == []
+
+
+def test_topk_matches_python_sorted(rng):
+    for n in [1, 5, 50, 300]:
+        sc = np.round(rng.normal(size=n), 1)  # many exact ties
+        k = 17
+        want = sorted(sorted(range(n), key=lambda j: (-sc[j], j))[:k])
+        assert list(O.topk_row(sc, k)) == want
+
+
+def test_topk_invariant_to_positive_weight_scale(rng):
+    """Scaling every head weight by c > 0 (e.g. the 1/90.5 temperature) leaves the
+    selection unchanged."""
+    q, k = rng.normal(size=(4, 8)), rng.normal(size=(40, 8))
+    w = rng.uniform(size=4)
+    a = O.topk_row(O.indexer_scores_row(q, w, k, 40), 7)
+    b = O.topk_row(O.indexer_scores_row(q, w / 90.5, k, 40), 7)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------- attention -------------
+
+def _sdpa_causal(q, k, v, scale):
+    """torch fp64 SDPA, q [S,H,D], k,v [S,D] shared across heads (MQA)."""
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]  # [1,H,S,D]
+    H = q.shape[1]
+    kt = torch.from_numpy(k)[None, None].expand(1, H, -1, -1).contiguous()
+    vt = torch.from_numpy(v)[None, None].expand(1, H, -1, -1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def test_hca_ratio1_no_rope_is_causal_sdpa(rng):
+    """Library special case: ratio 1 disjoint pooling of unit-RMS rows (eps 0) with no
+    window and no RoPE is plain causal multi-query attention over the entries."""
+    S, H, D = 24, 3, 8
+    va = rng.choice([-1.0, 1.0], size=(S, D))
+    cfg = tiny("hca", S=S, H=H, D=D, rope_dim=0, ratio=1, window=0, rms_eps=0.0)
+    # window 0 means no window keys; the oracle's window_bounds(t, 0) is (t+1, t): empty
+    inp = {"va": va[None], "ga": rng.normal(size=(1, S, D)), "bias": rng.normal(size=(1, D)),
+           "q": rng.normal(size=(1, S, H, D)), "kv_raw": rng.normal(size=(1, S, D))}
+    out = O.layer_forward(cfg, inp)["o_full"][0]
+    want = _sdpa_causal(inp["q"][0], va, va, D ** -0.5)
+    assert np.allclose(out, want, atol=1e-12)
+
+
+def test_swa_full_window_no_rope_is_causal_sdpa(rng):
+    S, H, D = 20, 2, 8
+    cfg = tiny("swa", S=S, H=H, D=D, rope_dim=0, window=S)
+    inp = {"q": rng.normal(size=(1, S, H, D)), "kv_raw": rng.normal(size=(1, S, D))}
+    out = O.layer_forward(cfg, inp)["o_full"][0]
+    want = _sdpa_causal(inp["q"][0], inp["kv_raw"][0], inp["kv_raw"][0], D ** -0.5)
+    assert np.allclose(out, want, atol=1e-12)
+
+
+def test_swa_with_rope_matches_sdpa_on_rotated_then_derotated(rng):
+    """With RoPE: SDPA on queries rotated at t and keys rotated at t', then the output
+    rotated back at -t, equals the layer (the de-rotation step of the output)."""
+    S, H, D, R = 16, 2, 8, 4
+    cfg = tiny("swa", S=S, H=H, D=D, rope_dim=R, window=S, pos0=3)
+    inp = {"q": rng.normal(size=(1, S, H, D)), "kv_raw": rng.normal(size=(1, S, D))}
+    out = O.layer_forward(cfg, inp)["o_full"][0]
+    t = np.arange(S) + 3
+    qr = O.rope(inp["q"][0], t[:, None], R, 4e4)
+    kr = O.rope(inp["kv_raw"][0], t, R, 4e4)
+    u = _sdpa_causal(qr, kr, kr, D ** -0.5)
+    want = O.rope(u, -t[:, None], R, 4e4)
+    assert np.allclose(out, want, atol=1e-12)
+
+
+def test_t0_output_is_raw_latent():
+    """Closed form: at t = 0 no entry is visible (ratio > 1) and the window holds only
+    token 0, so o[0,h] = RoPE(RoPE(x0, pos0), -pos0) = x0 for every head."""
+    cfg = tiny("csa", pos0=977)
+    inp = to_np(wl.make_inputs(cfg))
+    r = O.layer_rows(cfg, inp, [(0, 0)])
+    for h in range(cfg.H):
+        assert np.allclose(r["o"][(0, 0)][h], inp["kv_raw"][0, 0], atol=1e-13)
+
+
+def test_uniform_logits_average_union_of_keys():
+    """Zero queries make every logit 0: the output is the plain mean over the union of
+    selected entries and window keys (one softmax), de-rotated."""
+    cfg = tiny("hca", S=40, window=5)
+    inp = to_np(wl.make_inputs(cfg))
+    inp["q"][:] = 0.0
+    rows = [(0, t) for t in (4, 15, 16, 39)]
+    r = O.layer_rows(cfg, inp, rows)
+    kv_c = r["kv_c"][0]
+    for (b, t) in rows:
+        n = O.visible_entries(t, cfg.ratio)
+        lo = max(0, t - cfg.window + 1)
+        wk = O.rope(inp["kv_raw"][0, lo:t + 1], np.arange(lo, t + 1), cfg.rope_dim, 4e4)
+        keys = np.concatenate([kv_c[:n], wk])
+        want = O.rope(keys.mean(0), -t, cfg.rope_dim, 4e4)
+        assert np.allclose(r["o"][(b, t)], want[None].repeat(cfg.H, 0), atol=1e-13)
+        assert len(keys) == n + min(cfg.window, t + 1)
+
+
+def test_position_shift_invariance():
+    """Shifting pos0 by a multiple of the ratio leaves attention probabilities and the
+    de-rotated output unchanged."""
+    cfg = tiny("csa", S=48)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(0, 48, 5)]
+    a = O.layer_rows(cfg, inp, rows, want_p=True)
+    b = O.layer_rows(cfg.replace(pos0=4 * 1013), inp, rows, want_p=True)
+    for k in rows:
+        assert np.allclose(a["P"][k], b["P"][k], atol=1e-10)
+        assert np.allclose(a["o"][k], b["o"][k], atol=1e-10)
+
+
+def test_csa_with_topk_covering_all_equals_dense():
+    """With top-k >= visible entries for every query, CSA equals dense attention over
+    all visible entries."""
+    cfg = tiny("csa", S=48, topk=64)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(48)]
+    a = O.layer_rows(cfg, inp, rows)
+    dense_sel = {(0, t): np.arange(O.visible_entries(t, 4)) for t in range(48)}
+    b = O.layer_rows(cfg, inp, rows, sel_override=dense_sel)
+    for k in rows:
+        assert np.array_equal(a["sel"][k], dense_sel[k])
+        assert np.allclose(a["o"][k], b["o"][k], atol=0)
+
+
+# ------------------------------------------------------------ brute force ----------
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
+def test_oracle_matches_brute_force(kind):
+    cfg = tiny(kind, S=32, pos0=9 if kind != "swa" else 2, norm_window=(kind == "hca"))
+    inp = to_np(wl.make_inputs(cfg))
+    ora = O.layer_forward(cfg, inp)
+    bf = brute.brute_layer(cfg, inp)
+    assert np.allclose(ora["o_full"][0], np.array(bf["o"]), atol=1e-12)
+    for t in range(cfg.S):
+        assert list(ora["sel"][(0, t)]) == bf["sel"][t]
+        if kind == "csa":
+            assert np.allclose(ora["scores"][(0, t)], bf["scores"][t], atol=1e-12)
+    if kind != "swa":
+        assert np.allclose(ora["kv_c"][0], np.array(bf["kv_c"]), atol=1e-13)
+
+
+def test_keys_per_query_matches_pages():
+    """Keys per query: min(K, n_t) + min(W, t+1).  At long context CSA reads 512 + 128
+    = 640 keys and HCA at 1M tokens reads 10^6/128 + 128, about 7,900 ("Three
+    attention types, interleaved")."""
+    c1 = wl.C1
+    assert wl.keys_per_query(c1, 4095) == 640
+    hca_1m = wl.C2.replace(S=1_000_448)
+    assert abs(wl.keys_per_query(hca_1m, hca_1m.S - 1) - 7900) < 100
