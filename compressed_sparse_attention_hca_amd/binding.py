@@ -1,0 +1,253 @@
+"""Thin ctypes binding of libcsa.so (include/csa.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind
+the C ABI.  PyTorch supplies device memory and the current stream.  There is no CPU
+fallback; if the library is missing or fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from . import workloads as wl
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED, CSA_ERR_HIP = range(5)
+CSA_F32, CSA_BF16 = 0, 1
+OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_CSA_FWD, OP_HCA_FWD = range(5)
+FLAG_NORM_WINDOW = 1
+
+
+class Params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "S", "H", "D", "rope_dim", "ratio", "overlap", "window", "topk",
+                 "idx_heads", "idx_dim", "dtype")] + [
+        ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float), ("pos0", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+
+
+class Inputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "kv_raw", "va", "ga", "vb", "gb", "bias", "q_idx", "w_idx", "k_idx",
+                 "kv_c_out", "idx_out", "n_visible_out")]
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_status_names.get(status, status)}: {msg}")
+        self.status = status
+
+
+_status_names = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_WORKSPACE",
+                 3: "CSA_ERR_UNSUPPORTED", 4: "CSA_ERR_HIP"}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m compressed_sparse_attention_hca_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, V, I32, I64, SZ = ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "csa_compress": [P, V, V, V, V, V, V, V],
+        "csa_index_scores": [P, V, V, V, V, I64, I32, I32, V],
+        "csa_index_topk": [P, V, V, V, V, V, V, SZ, V],
+        "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
+        "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
+        "hca_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
+        "csa_debug_layout": [P, V, V, V, V],
+        "csa_fwd_traced": [P, ctypes.POINTER(Inputs), V, V, SZ, V, ctypes.POINTER(V),
+                           ctypes.POINTER(I32), I32],
+        "hca_fwd_traced": [P, ctypes.POINTER(Inputs), V, V, SZ, V, ctypes.POINTER(V),
+                           ctypes.POINTER(I32), I32],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.csa_trace_events.argtypes = [P, I32]
+    lib.csa_trace_events.restype = I32
+    lib.csa_workspace_bytes.argtypes = [P, I32]
+    lib.csa_workspace_bytes.restype = SZ
+    lib.csa_status_str.argtypes = [ctypes.c_int]
+    lib.csa_status_str.restype = ctypes.c_char_p
+    lib.csa_last_error.argtypes = []
+    lib.csa_last_error.restype = ctypes.c_char_p
+    lib.csa_abi_version.argtypes = []
+    lib.csa_abi_version.restype = ctypes.c_int32
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_sparse_mqa_fwd", "csa_fwd",
+           "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
+           "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
+           "csa_abi_version")
+
+KERNEL_NAMES = {0: "compress", 1: "window_rope", 2: "indexer", 3: "topk", 4: "attention"}
+
+
+def last_error() -> str:
+    return lib.csa_last_error().decode()
+
+
+def check(status: int):
+    if status != CSA_OK:
+        raise CsaError(status, last_error())
+
+
+def params(cfg: wl.LayerConfig, **over) -> Params:
+    """csa_params_t for a workload config (fields may be overridden by keyword)."""
+    p = Params(B=cfg.B, S=cfg.S, H=cfg.H, D=cfg.D, rope_dim=cfg.rope_dim, ratio=cfg.ratio,
+               overlap=cfg.overlap, window=cfg.window, topk=max(cfg.topk, 1),
+               idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
+               dtype=CSA_BF16 if cfg.dtype == wl.BF16 else CSA_F32,
+               rope_theta=cfg.rope_theta, rms_eps=cfg.rms_eps, softmax_scale=cfg.softmax_scale,
+               pos0=cfg.pos0, flags=FLAG_NORM_WINDOW if cfg.norm_window else 0)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(p: Params, op: int) -> int:
+    return int(lib.csa_workspace_bytes(ctypes.byref(p), op))
+
+
+def workspace(p: Params, op: int, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(p, op)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def compress(p: Params, va, ga, vb, gb, bias, kv_c=None, stream=None) -> torch.Tensor:
+    n = p.S // p.ratio
+    if kv_c is None:
+        kv_c = torch.empty((p.B, n, p.D), dtype=va.dtype, device=va.device)
+    check(lib.csa_compress(ctypes.byref(p), _ptr(va), _ptr(ga), _ptr(vb), _ptr(gb), _ptr(bias),
+                           _ptr(kv_c), _stream(stream)))
+    return kv_c
+
+
+def index_scores(p: Params, q_idx, w_idx, k_idx, t0=0, nrows=None, scores=None, stream=None):
+    nrows = p.S - t0 if nrows is None else nrows
+    ld = max(p.S // p.ratio, 1)
+    if scores is None:
+        scores = torch.full((p.B, nrows, ld), float("nan"), dtype=torch.float32, device=q_idx.device)
+    check(lib.csa_index_scores(ctypes.byref(p), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(scores),
+                               scores.shape[-1], t0, nrows, _stream(stream)))
+    return scores
+
+
+def index_topk(p: Params, q_idx, w_idx, k_idx, idx=None, n_visible=None, ws=None, stream=None):
+    dev = q_idx.device
+    if idx is None:
+        idx = torch.empty((p.B, p.S, p.topk), dtype=torch.int32, device=dev)
+    if n_visible is None:
+        n_visible = torch.empty((p.B, p.S), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(p, OP_INDEX_TOPK, dev)
+    check(lib.csa_index_topk(ctypes.byref(p), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(idx),
+                             _ptr(n_visible), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, n_visible
+
+
+def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream=None):
+    if o is None:
+        o = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(p, OP_SPARSE_MQA, q.device)
+    check(lib.csa_sparse_mqa_fwd(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx), _ptr(o),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return o
+
+
+def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=None) -> Inputs:
+    g = inp.get
+    return Inputs(q=_ptr(g("q")), kv_raw=_ptr(g("kv_raw")), va=_ptr(g("va")), ga=_ptr(g("ga")),
+                  vb=_ptr(g("vb")), gb=_ptr(g("gb")), bias=_ptr(g("bias")), q_idx=_ptr(g("q_idx")),
+                  w_idx=_ptr(g("w_idx")), k_idx=_ptr(g("k_idx")), kv_c_out=_ptr(kv_c_out),
+                  idx_out=_ptr(idx_out), n_visible_out=_ptr(n_visible_out))
+
+
+def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None, idx_out=None,
+              n_visible_out=None):
+    """csa_fwd when p.overlap == 1, else hca_fwd."""
+    q = inp["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
+    if ws is None:
+        ws = workspace(p, op, q.device)
+    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
+    f = lib.csa_fwd if p.overlap else lib.hca_fwd
+    check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
+    return o
+
+
+class LayerTrace:
+    """Caller-owned HIP events for the traced fused call; per-kernel times in ms."""
+
+    def __init__(self, p: Params):
+        op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
+        self.n = int(lib.csa_trace_events(ctypes.byref(p), op))
+        if self.n <= 0:
+            raise CsaError(CSA_ERR_INVALID_ARG, last_error())
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(self.n)]
+        for e in self.events:  # materialise the underlying hipEvent_t
+            e.record()
+        torch.cuda.synchronize()
+        self.handles = (ctypes.c_void_p * self.n)(*[e.cuda_event for e in self.events])
+        self.kinds = (ctypes.c_int32 * self.n)()
+
+    def kernel_ms(self) -> dict:
+        """Per-kernel sums of launch durations (ms) from the last traced call, plus the
+        number of launches of each kernel."""
+        ms, launches = {}, {}
+        for i in range(self.n - 1):
+            name = KERNEL_NAMES[self.kinds[i]]
+            ms[name] = ms.get(name, 0.0) + self.events[i].elapsed_time(self.events[i + 1])
+            launches[name] = launches.get(name, 0) + 1
+        return ms, launches
+
+
+def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, stream=None):
+    q = inp["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
+    if ws is None:
+        ws = workspace(p, op, q.device)
+    s = make_inputs_struct(inp)
+    f = lib.csa_fwd_traced if p.overlap else lib.hca_fwd_traced
+    check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream),
+            trace.handles, trace.kinds, trace.n))
+    return o
+
+
+def debug_layout(p: Params, device="cuda", stream=None):
+    n = max(p.S // p.ratio, 1)
+    comp = torch.full((n,), -7, dtype=torch.int32, device=device)
+    nv = torch.full((max(p.S, 1),), -7, dtype=torch.int32, device=device)
+    wl_ = torch.full((max(p.S, 1),), -7, dtype=torch.int32, device=device)
+    check(lib.csa_debug_layout(ctypes.byref(p), _ptr(comp), _ptr(nv), _ptr(wl_), _stream(stream)))
+    return comp, nv, wl_

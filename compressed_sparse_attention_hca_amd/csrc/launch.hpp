@@ -1,0 +1,31 @@
+// Internal launcher interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+enum MqaMode : int32_t { MQA_SELECTED = 0, MQA_DENSE = 1, MQA_WINDOW_ONLY = 2 };
+
+hipError_t launch_compress(const csa_params_t& p, const void* va, const void* ga, const void* vb,
+                           const void* gb, const float* bias, void* kv_c, hipStream_t st);
+
+hipError_t launch_window_rope(const csa_params_t& p, const void* kv_raw, void* kv_w, hipStream_t st);
+
+hipError_t launch_index_scores(const csa_params_t& p, const void* q_idx, const float* w_idx,
+                               const void* k_idx, float* scores, int64_t ld, int32_t t0,
+                               int32_t nrows, hipStream_t st);
+
+hipError_t launch_topk(const csa_params_t& p, const float* scores, int64_t ld, int32_t t0,
+                       int32_t nrows, int32_t* idx, int32_t* n_visible, hipStream_t st);
+
+hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
+                             const void* kv_w, const int32_t* idx, void* o, hipStream_t st);
+
+hipError_t launch_debug_layout(const csa_params_t& p, int32_t* comp_pos, int32_t* n_visible,
+                               int32_t* win_lo, hipStream_t st);
+
+}  // namespace csa

@@ -1,0 +1,207 @@
+/*
+ * csa.h -- C-ABI of the MI355X (gfx950) forward kernels for the DeepSeek-V4-Flash
+ * compressed attention layer: compressed sparse attention (CSA), heavily compressed
+ * attention (HCA) and the window-only layer.
+ *
+ * The layer, in four stages, as the pages define it:
+ *   1. softmax-gated pooling of per-token KV latents into compressed entries
+ *      ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+ *      Primus", subsection "Three attention types, interleaved": a softmax over the
+ *      group of gate plus a learnable per-position bias weights the sum; CSA groups
+ *      of 4 overlap the previous 4 tokens, HCA groups of 128 are disjoint);
+ *   2. RMSNorm of each entry, then RoPE on its last rope_dim dims at the entry's
+ *      original-sequence position pos0 + s*ratio ("fix(deepseek-v4): correct
+ *      V4-Flash attention math", Part 1 item 2; RMSNorm of entries: item 1);
+ *   3. CSA only: lightning-indexer scores I[t,s] = sum_h w[t,h] ReLU(q_I[t,h].k_I[s])
+ *      over every causally visible entry, then the top-k entries per query (same
+ *      PR, items 4 and 6a; blog, "Three attention types, interleaved");
+ *   4. multi-query attention of H heads over one shared D-wide latent that is both
+ *      key and value, across the selected entries plus a sliding window of raw
+ *      tokens, scale head_dim**-0.5 with no YaRN factor (PR item 1), then the
+ *      output's RoPE dims rotated back at -(pos0 + t) (PR item 3).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, contiguous row-major, batch-major, and
+ *     16-byte aligned.  Activations use params->dtype; bias, indexer head weights and
+ *     scores are always fp32; idx and n_visible are int32.  Accumulation is fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every call
+ *     only enqueues work on that stream and returns; nothing synchronises.
+ *   - The library never allocates or frees memory.  The caller owns every buffer,
+ *     including the workspace, whose size comes from csa_workspace_bytes(); its
+ *     contents are undefined on return.
+ *   - Arguments are validated on the host before any launch.  A bad argument
+ *     returns a status and enqueues nothing; csa_last_error() then holds a
+ *     thread-local message.  No exception crosses the ABI and nothing aborts.
+ *     CSA_ERR_HIP reports a launch failure; errors raised while kernels run surface
+ *     at the caller's next synchronisation.
+ *   - Calls are re-entrant: the library keeps no global mutable state apart from the
+ *     thread-local error string.
+ *
+ * Integer layout shared by every kernel (bit-exact, see csa_debug_layout):
+ *   n_visible(t) = floor((t + 1) / ratio)   entries whose whole group is seen by t
+ *   comp_pos(s)  = pos0 + s * ratio         rotation position of entry s
+ *   win_lo(t)    = max(0, t - window + 1)   window tokens win_lo(t) .. t
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* null required pointer, inconsistent shape, misalignment */
+  CSA_ERR_WORKSPACE = 2,   /* ws_bytes below csa_workspace_bytes() */
+  CSA_ERR_UNSUPPORTED = 3, /* valid but outside the compiled shape set, or no gfx950 */
+  CSA_ERR_HIP = 4          /* a HIP launch failed */
+} csa_status_t;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype_t;
+
+typedef enum {
+  CSA_OP_COMPRESS = 0,
+  CSA_OP_INDEX_TOPK = 1,
+  CSA_OP_SPARSE_MQA = 2,
+  CSA_OP_CSA_FWD = 3,
+  CSA_OP_HCA_FWD = 4
+} csa_op_t;
+
+/* flags */
+#define CSA_FLAG_NORM_WINDOW 1u /* RMS-normalise window latents before their RoPE */
+
+typedef struct {
+  int32_t B;          /* batch */
+  int32_t S;          /* tokens per sequence; a multiple of ratio */
+  int32_t H;          /* query heads, 1..64 */
+  int32_t D;          /* latent width = head dim: 64, 128, 256 or 512 */
+  int32_t rope_dim;   /* RoPE on the last rope_dim dims: even, <= D, <= 128 */
+  int32_t ratio;      /* compress ratio (4 for CSA, 128 for HCA in V4-Flash) */
+  int32_t overlap;    /* 1: CSA groups of 2*ratio (own + previous); 0: disjoint */
+  int32_t window;     /* sliding-window length, >= 0 */
+  int32_t topk;       /* entries kept per query (CSA), 1..2048 */
+  int32_t idx_heads;  /* indexer heads, 1..64 */
+  int32_t idx_dim;    /* indexer dim: 16, 32, 64 or 128 */
+  int32_t dtype;      /* csa_dtype_t of activations */
+  double rope_theta;  /* RoPE base, 40000 for V4-Flash */
+  float rms_eps;      /* RMSNorm epsilon (1e-6) */
+  float softmax_scale;/* D**-0.5 */
+  int64_t pos0;       /* absolute position of token 0 */
+  uint32_t flags;     /* CSA_FLAG_* */
+} csa_params_t;
+
+/* Device pointers for the fused calls.  Shapes: q [B,S,H,D], kv_raw [B,S,D],
+ * va ga vb gb [B,S,D], bias [span,D] fp32 (span = 2*ratio with overlap, else ratio),
+ * q_idx [B,S,idx_heads,idx_dim], w_idx [B,S,idx_heads] fp32, k_idx [B,S/ratio,idx_dim].
+ * The *_out pointers are optional (NULL = keep in workspace only): kv_c_out
+ * [B,S/ratio,D], idx_out [B,S,topk], n_visible_out [B,S]. */
+typedef struct {
+  const void* q;
+  const void* kv_raw;
+  const void* va;
+  const void* ga;
+  const void* vb;
+  const void* gb;
+  const float* bias;
+  const void* q_idx;
+  const float* w_idx;
+  const void* k_idx;
+  void* kv_c_out;
+  int32_t* idx_out;
+  int32_t* n_visible_out;
+} csa_inputs_t;
+
+/* Stages 1-2: gated pooling, RMSNorm and RoPE at pos0 + s*ratio.
+ *   va, ga [B,S,D]: value and gate of each entry's own group ("a" projections);
+ *   vb, gb [B,S,D]: value and gate read for the previous group ("b" projections);
+ *     must be non-NULL iff overlap == 1;
+ *   bias [span,D] fp32: row j weights pooling slot j in token order (with overlap,
+ *     rows 0..ratio-1 are the previous group, rows ratio..2*ratio-1 the own group);
+ *   kv_c [B,S/ratio,D] output.  CSA entry 0 has no previous group: those slots are
+ *   left out of its softmax. */
+csa_status_t csa_compress(const csa_params_t* p, const void* va, const void* ga,
+                          const void* vb, const void* gb, const float* bias, void* kv_c,
+                          void* stream);
+
+/* Stage 3, scores only (for checking): rows t0 .. t0+nrows-1 of every batch;
+ * scores[b][t - t0][s] for s < n_visible(t), row stride ld floats (ld >= S/ratio);
+ * entries s >= n_visible(t) are not written. */
+csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const float* w_idx,
+                              const void* k_idx, float* scores, int64_t ld, int32_t t0,
+                              int32_t nrows, void* stream);
+
+/* Stage 3: indexer scores over visible entries and the top-k per query.
+ *   idx [B,S,topk] int32: the min(topk, n_visible(t)) selected entries in ascending
+ *   order, then -1 padding; ties at the k-th score go to the smaller entry index.
+ *   n_visible [B,S] int32.  ws: csa_workspace_bytes(p, CSA_OP_INDEX_TOPK) bytes. */
+csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const float* w_idx,
+                            const void* k_idx, int32_t* idx, int32_t* n_visible, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Stage 4: attention over selected entries plus the window, then de-rotation.
+ *   q [B,S,H,D] (RMS-normalised upstream; rotated here at pos0 + t);
+ *   kv_c [B,S/ratio,D] rotated entries, or NULL for the window-only layer;
+ *   kv_raw [B,S,D] raw latents of the window (rotated here at their positions);
+ *   idx [B,S,topk] selection, or NULL to attend to every visible entry (HCA);
+ *     an index outside 0..n_visible(t)-1 is ignored;
+ *   o [B,S,H,D] output.  ws: csa_workspace_bytes(p, CSA_OP_SPARSE_MQA) bytes. */
+csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
+                                const void* kv_raw, const int32_t* idx, void* o, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Fused CSA layer (stages 1-4, overlap must be 1). */
+csa_status_t csa_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Fused HCA layer (stages 1, 2 and 4 with every visible entry; overlap must be 0;
+ * the indexer fields of `in` are ignored). */
+csa_status_t hca_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Kernels of the fused calls, as reported by the traced variants below. */
+typedef enum {
+  CSA_KERNEL_COMPRESS = 0,    /* pooling + RMSNorm + RoPE of entries */
+  CSA_KERNEL_WINDOW_ROPE = 1, /* rotation of the raw window latents */
+  CSA_KERNEL_INDEXER = 2,     /* indexer scores (one launch per query chunk) */
+  CSA_KERNEL_TOPK = 3,        /* top-k selection (one launch per query chunk) */
+  CSA_KERNEL_ATTENTION = 4    /* sparse MQA + de-rotation */
+} csa_kernel_t;
+
+/* Number of events the traced variant of `op` (CSA_OP_CSA_FWD or CSA_OP_HCA_FWD)
+ * records for these params: one more than its kernel launches; 0 on invalid params. */
+int32_t csa_trace_events(const csa_params_t* p, int32_t op);
+
+/* csa_fwd / hca_fwd that also time each kernel.  `events` are caller-created
+ * hipEvent_t handles (as void*); events[0] is recorded on `stream` before the first
+ * launch and events[i+1] right after launch i, whose csa_kernel_t is written to
+ * kinds[i] (host memory).  n_events must be >= csa_trace_events(p, op).  Recording
+ * events allocates nothing.  Work and results are those of the untraced call. */
+csa_status_t csa_fwd_traced(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
+                            size_t ws_bytes, void* stream, void* const* events, int32_t* kinds,
+                            int32_t n_events);
+csa_status_t hca_fwd_traced(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
+                            size_t ws_bytes, void* stream, void* const* events, int32_t* kinds,
+                            int32_t n_events);
+
+/* Workspace bytes an operation needs for these params (0 on invalid params). */
+size_t csa_workspace_bytes(const csa_params_t* p, int32_t op);
+
+/* The integer layout the kernels use, written by a kernel from the same helpers:
+ * comp_pos [S/ratio] (positions, truncated to int32), n_visible [S], win_lo [S].
+ * Any output may be NULL. */
+csa_status_t csa_debug_layout(const csa_params_t* p, int32_t* comp_pos, int32_t* n_visible,
+                              int32_t* win_lo, void* stream);
+
+const char* csa_status_str(csa_status_t s);
+const char* csa_last_error(void);
+int32_t csa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,182 @@
+"""C-ABI checks that need no GPU: the library loads and exports every entry point the
+header declares, the binding's struct layout matches the C compiler's, and every
+argument error is reported by host-side validation before anything is launched.
+
+Only failing-validation calls are made here (plus pure host queries), so no kernel is
+ever enqueued: these tests are safe with or without a GPU present.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from compressed_sparse_attention_hca_amd import binding as bd
+from compressed_sparse_attention_hca_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_\w+|hca_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(bd.lib, n)
+    assert set(bd.EXPORTS) == set(names)
+
+
+def test_abi_version_and_status_strings():
+    assert bd.lib.csa_abi_version() == 1
+    for code, name in bd._status_names.items():
+        assert bd.lib.csa_status_str(code).decode() == name
+
+
+def test_struct_layout_matches_c_compiler(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in bd.Params._fields_]
+    ifields = [f for f, _ in bd.Inputs._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa.h"', "int main(void){",
+             'printf("%zu %zu\\n", sizeof(csa_params_t), sizeof(csa_inputs_t));']
+    lines += [f'printf("%zu\\n", offsetof(csa_params_t, {f}));' for f in fields]
+    lines += [f'printf("%zu\\n", offsetof(csa_inputs_t, {f}));' for f in ifields]
+    lines += ["return 0;}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(bd.Params) and vals[1] == ctypes.sizeof(bd.Inputs)
+    offs = vals[2:]
+    assert offs[:len(fields)] == [getattr(bd.Params, f).offset for f in fields]
+    assert offs[len(fields):] == [getattr(bd.Inputs, f).offset for f in ifields]
+
+
+# Fake, 16-byte aligned device addresses.  Every call below fails validation, so they
+# are never dereferenced or passed to a kernel.
+A = 0x10000
+
+
+def p_c1(**kw):
+    return bd.params(wl.C1, **kw)
+
+
+def call_compress(p, va=A, ga=A, vb=A, gb=A, bias=A, out=A):
+    return bd.lib.csa_compress(ctypes.byref(p) if p is not None else None, va, ga, vb, gb, bias, out, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), bd.CSA_ERR_INVALID_ARG),
+    (dict(D=1024), bd.CSA_ERR_INVALID_ARG),
+    (dict(D=192), bd.CSA_ERR_UNSUPPORTED),
+    (dict(rope_dim=7), bd.CSA_ERR_INVALID_ARG),
+    (dict(rope_dim=576), bd.CSA_ERR_INVALID_ARG),
+    (dict(rope_dim=256), bd.CSA_ERR_UNSUPPORTED),
+    (dict(S=4097), bd.CSA_ERR_INVALID_ARG),
+    (dict(ratio=0), bd.CSA_ERR_INVALID_ARG),
+    (dict(overlap=2), bd.CSA_ERR_INVALID_ARG),
+    (dict(dtype=5), bd.CSA_ERR_INVALID_ARG),
+    (dict(flags=6), bd.CSA_ERR_INVALID_ARG),
+    (dict(B=-1), bd.CSA_ERR_INVALID_ARG),
+    (dict(rope_theta=0.0), bd.CSA_ERR_INVALID_ARG),
+    (dict(rms_eps=float("nan")), bd.CSA_ERR_INVALID_ARG),
+])
+def test_compress_rejects_bad_params(over, code):
+    assert call_compress(p_c1(**over)) == code
+    assert bd.last_error()
+
+
+def test_compress_rejects_null_and_misaligned_pointers():
+    p = p_c1()
+    assert call_compress(None) == bd.CSA_ERR_INVALID_ARG
+    assert call_compress(p, va=None) == bd.CSA_ERR_INVALID_ARG and "va" in bd.last_error()
+    assert call_compress(p, bias=A + 4) == bd.CSA_ERR_INVALID_ARG and "aligned" in bd.last_error()
+    assert call_compress(p, out=None) == bd.CSA_ERR_INVALID_ARG and "kv_c" in bd.last_error()
+    assert call_compress(p, gb=None) == bd.CSA_ERR_INVALID_ARG and "gb" in bd.last_error()
+    ph = bd.params(wl.C2)
+    assert call_compress(ph) == bd.CSA_ERR_INVALID_ARG and "NULL when overlap" in bd.last_error()
+
+
+def test_index_topk_rejects():
+    def call(p, ws_bytes=1 << 40, idx=A, ws=A):
+        return bd.lib.csa_index_topk(ctypes.byref(p), A, A, A, idx, A, ws, ws_bytes, None)
+    assert call(p_c1(topk=0)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(topk=4096)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(idx_heads=65)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(idx_dim=24)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(idx_dim=256)) == bd.CSA_ERR_UNSUPPORTED
+    assert call(p_c1(S=4 * 40000)) == bd.CSA_ERR_UNSUPPORTED
+    assert call(p_c1(), idx=None) == bd.CSA_ERR_INVALID_ARG
+    need = bd.workspace_bytes(p_c1(), bd.OP_INDEX_TOPK)
+    assert need > 0
+    assert call(p_c1(), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
+    assert call(p_c1(), ws=None) == bd.CSA_ERR_INVALID_ARG
+
+
+def test_index_scores_rejects_rows_and_ld():
+    def call(p, ld=1024, t0=0, n=16):
+        return bd.lib.csa_index_scores(ctypes.byref(p), A, A, A, A, ld, t0, n, None)
+    assert call(p_c1(), t0=-1) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), t0=4090, n=10) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), ld=1000) == bd.CSA_ERR_INVALID_ARG
+
+
+def test_sparse_mqa_rejects():
+    def call(p, q=A, kv_c=A, kv_raw=A, idx=A, o=A, ws=A, ws_bytes=1 << 40):
+        return bd.lib.csa_sparse_mqa_fwd(ctypes.byref(p), q, kv_c, kv_raw, idx, o, ws, ws_bytes, None)
+    assert call(p_c1(H=0)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(H=65)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(window=-1)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(window=0), kv_c=None, idx=None) == bd.CSA_ERR_INVALID_ARG  # nothing to attend
+    assert call(p_c1(), kv_c=None) == bd.CSA_ERR_INVALID_ARG  # idx without entries
+    assert call(p_c1(softmax_scale=0.0)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), q=None) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), kv_raw=A + 8) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), ws_bytes=100) == bd.CSA_ERR_WORKSPACE
+
+
+def test_fused_rejects():
+    ins = bd.Inputs(q=A, kv_raw=A, va=A, ga=A, vb=A, gb=A, bias=A, q_idx=A, w_idx=A, k_idx=A)
+    def call(f, p, inputs=ins, o=A, ws_bytes=1 << 40):
+        return f(ctypes.byref(p), ctypes.byref(inputs) if inputs is not None else None, o, A, ws_bytes, None)
+    assert call(bd.lib.csa_fwd, bd.params(wl.C2)) == bd.CSA_ERR_INVALID_ARG      # overlap 0
+    assert call(bd.lib.hca_fwd, p_c1()) == bd.CSA_ERR_INVALID_ARG                 # overlap 1
+    assert call(bd.lib.csa_fwd, p_c1(), inputs=None) == bd.CSA_ERR_INVALID_ARG
+    assert call(bd.lib.csa_fwd, p_c1(), o=None) == bd.CSA_ERR_INVALID_ARG
+    assert call(bd.lib.csa_fwd, p_c1(), ws_bytes=0) == bd.CSA_ERR_WORKSPACE
+    bad = bd.Inputs(q=A, kv_raw=A, va=A, ga=A, vb=A, gb=A, bias=A, q_idx=None, w_idx=A, k_idx=A)
+    assert call(bd.lib.csa_fwd, p_c1(), inputs=bad) == bd.CSA_ERR_INVALID_ARG and "q_idx" in bd.last_error()
+    hca_in = bd.Inputs(q=A, kv_raw=A, va=A, ga=A, vb=A, gb=None, bias=A)
+    assert call(bd.lib.hca_fwd, bd.params(wl.C2), inputs=hca_in) == bd.CSA_ERR_INVALID_ARG  # vb given
+
+
+def test_workspace_bytes():
+    p = p_c1()
+    csa = bd.workspace_bytes(p, bd.OP_CSA_FWD)
+    hca = bd.workspace_bytes(bd.params(wl.C2), bd.OP_HCA_FWD)
+    assert bd.workspace_bytes(p, bd.OP_COMPRESS) == 0
+    mqa = bd.workspace_bytes(p, bd.OP_SPARSE_MQA)
+    assert mqa >= 4096 * 512 * 2                     # rotated window latents
+    assert csa >= mqa + 1024 * 512 * 2 + 4096 * 512 * 4  # + entries + selection
+    assert hca >= 65536 * 512 * 2 + 512 * 512 * 2
+    assert bd.workspace_bytes(p_c1(D=96), bd.OP_CSA_FWD) == 0
+    assert bd.workspace_bytes(p, 99) == 0
+    # C3 stays well inside one GPU's memory
+    assert bd.workspace_bytes(bd.params(wl.C3), bd.OP_CSA_FWD) < 2 << 30
+
+
+def test_empty_problem_is_a_noop():
+    p = p_c1(S=0)
+    assert call_compress(p, va=None, ga=None, vb=None, gb=None, bias=None, out=None) == bd.CSA_OK
+    p = p_c1(B=0)
+    assert bd.lib.csa_sparse_mqa_fwd(ctypes.byref(p), None, None, None, None, None, None, 0, None) == bd.CSA_OK

@@ -1,0 +1,274 @@
+"""GPU-versus-oracle parity of every stage, through the C ABI.
+
+Acceptance: integer layout, masks and window bounds bit-exact; top-k sets exact except
+entries whose oracle score is within 1e-3 relative of the k-th score; outputs within
+max|gpu - oracle| <= 1e-2 * max|oracle| for bf16 inputs and 1e-5 for the fp32 config.
+Where an admissible near-tie swap occurs the oracle is re-evaluated on the GPU's
+selection for the output comparison.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_hca_amd import workloads as wl
+from oracle import csa_oracle as O
+from gpu_util import (Lazy, assert_close_rel, check_selection, full_np, lazy_inputs,
+                      sample_rows, tol)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def bd():
+    from compressed_sparse_attention_hca_amd import binding
+    return binding
+
+
+def gen(cfg):
+    """Small configs draw on the CPU generator (then copy), large ones on the device."""
+    if cfg.B * cfg.S * cfg.H * cfg.D <= (1 << 26):
+        return {k: v.to(DEV) for k, v in wl.make_inputs(cfg, "cpu").items()}
+    return wl.make_inputs(cfg, DEV)
+
+
+def run_layer(bd, cfg, inp):
+    p = bd.params(cfg)
+    B, S, n = cfg.B, cfg.S, cfg.S // cfg.ratio
+    kv_c = torch.empty((B, n, cfg.D), dtype=inp["q"].dtype, device=DEV)
+    idx = torch.empty((B, S, max(cfg.topk, 1)), dtype=torch.int32, device=DEV) if cfg.kind == "csa" else None
+    nv = torch.empty((B, S), dtype=torch.int32, device=DEV) if cfg.kind == "csa" else None
+    o = bd.layer_fwd(p, inp, kv_c_out=kv_c, idx_out=idx, n_visible_out=nv)
+    torch.cuda.synchronize()
+    return o, kv_c, idx, nv
+
+
+# ------------------------------------------------------------------ layout ---------
+
+@pytest.mark.parametrize("cfg", [wl.C0, wl.C1, wl.C2, wl.C1.replace(pos0=77777, window=5)])
+def test_layout_bit_exact(bd, cfg):
+    comp, nv, wlo = bd.debug_layout(bd.params(cfg))
+    torch.cuda.synchronize()
+    n = cfg.S // cfg.ratio
+    assert comp.cpu().tolist() == [cfg.pos0 + s * cfg.ratio for s in range(n)]
+    assert nv.cpu().tolist() == [O.visible_entries(t, cfg.ratio) for t in range(cfg.S)]
+    assert wlo.cpu().tolist() == [O.window_bounds(t, cfg.window)[0] for t in range(cfg.S)]
+
+
+# ---------------------------------------------------------------- compress ---------
+
+@pytest.mark.parametrize("name", ["C0", "C1", "C2", "C3"])
+def test_compress_parity(bd, name):
+    cfg = wl.CONFIGS[name]
+    inp = gen(cfg)
+    p = bd.params(cfg)
+    kv = bd.compress(p, inp["va"], inp["ga"], inp.get("vb"), inp.get("gb"), inp["bias"])
+    torch.cuda.synchronize()
+    got = kv.float().cpu().double().numpy()
+    for b in range(cfg.B):
+        want = O.compress(Lazy(inp["va"])[b], Lazy(inp["ga"])[b],
+                          Lazy(inp["vb"])[b] if "vb" in inp else None,
+                          Lazy(inp["gb"])[b] if "gb" in inp else None,
+                          Lazy(inp["bias"])[:], cfg.ratio, cfg.kind == "csa", cfg.rope_dim,
+                          cfg.rope_theta, cfg.rms_eps, cfg.pos0)
+        assert_close_rel(got[b], want, tol(cfg), f"kv_c {name}")
+
+
+# ----------------------------------------------------------------- indexer ---------
+
+@pytest.mark.parametrize("name", ["C0", "C1"])
+def test_index_scores_parity_full(bd, name):
+    cfg = wl.CONFIGS[name]
+    inp = gen(cfg)
+    sc = bd.index_scores(bd.params(cfg), inp["q_idx"], inp["w_idx"], inp["k_idx"])
+    torch.cuda.synchronize()
+    got = sc.cpu().double().numpy()
+    ki = Lazy(inp["k_idx"])[0]
+    qi, wi = Lazy(inp["q_idx"])[0], Lazy(inp["w_idx"])[0]
+    worst = 0.0
+    for t in range(cfg.S):
+        n = O.visible_entries(t, cfg.ratio)
+        want = O.indexer_scores_row(qi[t], wi[t], ki, n)
+        if n:
+            worst = max(worst, float(np.max(np.abs(got[0, t, :n] - want)) / np.max(np.abs(want))))
+        assert np.all(np.isnan(got[0, t, n:])), "entries past n_t must not be written"
+    assert worst <= 1e-5, worst
+
+
+def test_index_scores_parity_rows_C3(bd):
+    cfg = wl.C3
+    inp = gen(cfg)
+    t0, nrows = 40000, 37  # ragged row chunk away from the start
+    sc = bd.index_scores(bd.params(cfg), inp["q_idx"], inp["w_idx"], inp["k_idx"], t0=t0, nrows=nrows)
+    torch.cuda.synchronize()
+    ki = Lazy(inp["k_idx"])[0]
+    for j in (0, 1, 17, 36):
+        t = t0 + j
+        n = O.visible_entries(t, cfg.ratio)
+        want = O.indexer_scores_row(Lazy(inp["q_idx"])[0, t], Lazy(inp["w_idx"])[0, t], ki, n)
+        assert_close_rel(sc[0, j, :n].cpu().double().numpy(), want, 1e-5, f"scores row {t}")
+
+
+# ------------------------------------------------------------------- top-k ---------
+
+@pytest.mark.parametrize("name", ["C0", "C1"])
+def test_topk_parity_full(bd, name):
+    cfg = wl.CONFIGS[name]
+    inp = gen(cfg)
+    idx, nv = bd.index_topk(bd.params(cfg), inp["q_idx"], inp["w_idx"], inp["k_idx"])
+    torch.cuda.synchronize()
+    idx, nv = idx.cpu().numpy(), nv.cpu().numpy()
+    ki = Lazy(inp["k_idx"])[0]
+    qi, wi = Lazy(inp["q_idx"])[0], Lazy(inp["w_idx"])[0]
+    swaps = 0
+    for t in range(cfg.S):
+        n = O.visible_entries(t, cfg.ratio)
+        assert nv[0, t] == n
+        sc = O.indexer_scores_row(qi[t], wi[t], ki, n)
+        swaps += check_selection(idx[0, t], n, cfg.topk, sc, O.topk_row(sc, cfg.topk))
+    assert swaps <= cfg.S // 100, swaps
+
+
+# ------------------------------------------------------------- whole layer ---------
+
+def layer_check(bd, cfg, rows=None):
+    inp = gen(cfg)
+    o, kv_c, idx, nv = run_layer(bd, cfg, inp)
+    rows = rows if rows is not None else [(b, t) for b in range(cfg.B) for t in range(cfg.S)]
+    lz = lazy_inputs(inp)
+    sel_override = None
+    swaps = 0
+    if cfg.kind == "csa":
+        idx_np, nv_np = idx.cpu().numpy(), nv.cpu().numpy()
+        ora = O.layer_rows(cfg, lz, rows)
+        sel_override = {}
+        for (b, t) in rows:
+            n = O.visible_entries(t, cfg.ratio)
+            assert nv_np[b, t] == n
+            swaps += check_selection(idx_np[b, t], n, cfg.topk, ora["scores"][(b, t)], ora["sel"][(b, t)])
+            sel_override[(b, t)] = idx_np[b, t][:min(cfg.topk, n)]
+    ora = O.layer_rows(cfg, lz, rows, sel_override=sel_override)
+    got = np.stack([o[b, t].float().cpu().double().numpy() for (b, t) in rows])
+    want = np.stack([ora["o"][k] for k in rows])
+    err, scale = assert_close_rel(got, want, tol(cfg), f"o {cfg.name}")
+    if cfg.kind != "swa":
+        for b in range(cfg.B):
+            assert_close_rel(kv_c[b].float().cpu().double().numpy(), ora["kv_c"][b], tol(cfg), "kv_c")
+    return err, scale, swaps
+
+
+def test_layer_parity_C0_full(bd):
+    layer_check(bd, wl.C0)
+
+
+def test_layer_parity_C1_sampled(bd):
+    layer_check(bd, wl.C1, sample_rows(wl.C1, 48))
+
+
+def test_layer_parity_C2_sampled(bd):
+    layer_check(bd, wl.C2, sample_rows(wl.C2, 24))
+
+
+def test_layer_parity_C3_sampled(bd):
+    layer_check(bd, wl.C3, sample_rows(wl.C3, 24))
+
+
+def test_window_only_parity(bd):
+    cfg = wl.C1.replace(kind="swa", topk=0, S=1024, name="swa_1024")
+    inp = gen(cfg)
+    p = bd.params(cfg)
+    o = bd.sparse_mqa_fwd(p, inp["q"], None, inp["kv_raw"])
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, 32)
+    ora = O.layer_rows(cfg, lazy_inputs(inp), rows)
+    got = np.stack([o[b, t].float().cpu().double().numpy() for (b, t) in rows])
+    assert_close_rel(got, np.stack([ora["o"][k] for k in rows]), 1e-2, "swa o")
+
+
+# ------------------------------------------------------------- edge cases ----------
+
+EDGE = [
+    # ragged S (not a multiple of the 32-key tile), two batches, offset positions
+    dict(kind="csa", B=2, S=44, H=5, D=64, rope_dim=16, ratio=4, window=7, topk=3, idx_heads=3,
+         idx_dim=16, dtype=wl.F32, pos0=1_000_003),
+    # heads padded to 64, wider latent and indexer, window longer than the sequence
+    dict(kind="csa", B=1, S=96, H=20, D=128, rope_dim=32, ratio=4, window=200, topk=5, idx_heads=40,
+         idx_dim=32, dtype=wl.BF16, pos0=5),
+    # top-k covering every entry; window of 1
+    dict(kind="csa", B=1, S=64, H=16, D=256, rope_dim=64, ratio=2, window=1, topk=64, idx_heads=64,
+         idx_dim=64, dtype=wl.BF16),
+    # HCA with a 16-token disjoint group (single-wave pooling path), normalised window
+    dict(kind="hca", B=2, S=160, H=64, D=512, rope_dim=64, ratio=16, window=9, topk=0, dtype=wl.BF16,
+         norm_window=True),
+    # HCA fp32 with a 128-token group (split pooling path) and no RoPE
+    dict(kind="hca", B=1, S=256, H=3, D=64, rope_dim=0, ratio=128, window=4, topk=0, dtype=wl.F32),
+    # window-only layer, fp32
+    dict(kind="swa", B=1, S=70, H=17, D=64, rope_dim=16, window=11, topk=0, dtype=wl.F32),
+]
+
+
+@pytest.mark.parametrize("i", range(len(EDGE)))
+def test_edge_cases_full(bd, i):
+    cfg = wl.LayerConfig(name=f"edge{i}", seed=900 + i, **EDGE[i])
+    if cfg.kind == "swa":
+        inp = gen(cfg)
+        o = bd.sparse_mqa_fwd(bd.params(cfg), inp["q"], None, inp["kv_raw"])
+        torch.cuda.synchronize()
+        ora = O.layer_forward(cfg, full_np(inp))
+        assert_close_rel(o.float().cpu().double().numpy(), ora["o_full"], tol(cfg), "swa edge")
+    else:
+        layer_check(bd, cfg)
+
+
+def test_no_keys_gives_zero_output(bd):
+    """window 0 and t < ratio - 1: no key at all; the output is defined as zero."""
+    cfg = wl.LayerConfig(name="nokeys", kind="hca", B=1, S=32, H=4, D=64, rope_dim=16, ratio=8,
+                         window=0, topk=0, dtype=wl.F32, seed=5)
+    inp = gen(cfg)
+    o, *_ = run_layer(bd, cfg, inp)
+    assert torch.all(o[0, :7] == 0)
+    ora = O.layer_rows(cfg, full_np(inp), [(0, t) for t in range(7, 32)])
+    got = np.stack([o[0, t].cpu().double().numpy() for t in range(7, 32)])
+    assert_close_rel(got, np.stack([ora["o"][(0, t)] for t in range(7, 32)]), 1e-5, "o")
+
+
+def test_empty_batch_is_noop(bd):
+    import ctypes
+    p = bd.params(wl.C0.replace(B=0))
+    ins = bd.Inputs()
+    assert bd.lib.csa_fwd(ctypes.byref(p), ctypes.byref(ins), None, None, 0, None) == bd.CSA_OK
+    p = bd.params(wl.C1.replace(S=0))
+    assert bd.lib.csa_sparse_mqa_fwd(ctypes.byref(p), None, None, None, None, None, None, 0, None) == bd.CSA_OK
+
+
+# -------------------------------------------------------------- invariants ---------
+
+def test_topk_covering_all_equals_dense_bitwise(bd):
+    """With top-k >= visible entries CSA selects every entry in ascending order, so the
+    fused CSA output equals the dense (HCA-style) attention over the same entries."""
+    cfg = wl.C1.replace(S=1024, topk=1024, name="c1_dense")
+    inp = gen(cfg)
+    o, kv_c, idx, nv = run_layer(bd, cfg, inp)
+    p = bd.params(cfg)
+    o_dense = bd.sparse_mqa_fwd(p, inp["q"], kv_c, inp["kv_raw"], None)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_dense)
+
+
+def test_position_shift_invariance(bd):
+    cfg = wl.C1.replace(S=1024, name="c1_shift")
+    inp = gen(cfg)
+    o1, *_ = run_layer(bd, cfg, inp)
+    o2, *_ = run_layer(bd, cfg.replace(pos0=4 * 1013), inp)
+    ref = float(o1.float().abs().max())
+    assert float((o1.float() - o2.float()).abs().max()) <= 1e-2 * ref
+
+
+def test_deterministic(bd):
+    cfg = wl.C1
+    inp = gen(cfg)
+    o1, kv1, idx1, _ = run_layer(bd, cfg, inp)
+    o2, kv2, idx2, _ = run_layer(bd, cfg, inp)
+    assert torch.equal(idx1, idx2) and torch.equal(kv1, kv2) and torch.equal(o1, o2)
