@@ -16,16 +16,18 @@
 // output leaves; item 6g: done in-kernel).
 //
 // Mapping: one workgroup per query; wave w owns heads 16w .. 16w+15 and all D output
-// dims.  Keys stream through LDS in tiles of 32, shared by every head.  Per tile:
-//   S^T[key, head] = K_tile . Q^T     v_mfma_f32_16x16x32_bf16, keys on M (A from LDS,
-//                                     row-major), heads on N (B = rotated q in regs)
+// dims.  Keys stream through LDS in tiles of 32 rows, shared by every head, staged by
+// direct-to-LDS loads (one 1 KB wave load per line) into two stages while the other
+// stage is being used.  Per tile:
+//   S^T[key, head] = K_tile . Q^T     v_mfma_f32_16x16x32_bf16, keys on M (A from the
+//                                     row-major tile), heads on N (B = rotated q in regs)
 //   online softmax in registers, base-2, max rescale only when the tile max grows by
 //   more than 2^8 (exact: the final normalisation uses the same reference)
-//   O^T[dim, head] += V^T . P^T       dims on M (A from a transposed LDS copy of the
-//                                     tile), heads on N (B = P straight from S^T)
+//   O^T[dim, head] += V^T . P^T       dims on M (A read from the same row-major tile with
+//                                     ds_read_b64_tr_b16), heads on N (B = P from S^T)
 // The S^T accumulator gives lane (head, g) keys 4g..4g+3 and 16+4g..16+4g+3; those 8
-// are exactly that lane's B-operand k-slots for PV if the transposed copy stores key
-// sigma(g,i) at slot 8g+i, so P never leaves registers.
+// are that lane's B-operand k-slots for PV, and the two transposing reads fetch V for
+// exactly those keys, so P never leaves registers.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -46,23 +48,34 @@ struct MqaArgs {
 // Key slot (within a tile of 32) held at k-slot i of lane group g.
 __device__ __host__ constexpr int slot_key(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
+#define CSA_LDS __attribute__((address_space(3)))
+
+constexpr int MQA_MAX_TOPK = 2048;
+
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_mqa_kernel(MqaArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int HP = NW * 16;                 // heads handled (padded)
-  constexpr int VEC = 16 / sizeof(T);         // elements per 16-byte piece
-  constexpr int KT = 32;                      // keys per tile
-  constexpr int QROW = D + VEC;               // padded row of the q / o staging
-  constexpr int KROW = D + VEC;               // padded row of the key tile
-  constexpr int VROW = KT + VEC;              // padded row of the transposed tile
-  constexpr int NCH = D / VEC;                // 16-byte pieces per latent row
-  constexpr int NBLK = 4 * NCH;               // staging blocks (8 keys x VEC dims) per tile
-  constexpr int BPT = (NBLK + NT - 1) / NT;   // blocks per thread
-  constexpr int SZ_Q = HP * QROW * (int)sizeof(T);
-  constexpr int SZ_KV = (KT * KROW + D * VROW) * (int)sizeof(T);
-  constexpr int SZ = SZ_Q > SZ_KV ? SZ_Q : SZ_KV;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SZ];
-  __shared__ int kvalid[KT];
+  constexpr int HP = NW * 16;                       // heads handled (padded)
+  constexpr int ES = (int)sizeof(T);
+  constexpr int VEC = 16 / ES;                      // elements per 16-byte piece
+  constexpr int KT = 32;                            // keys per tile
+  constexpr int ROWB = D * ES;                      // bytes per latent row
+  constexpr int NCH = ROWB / 16;                    // 16-byte pieces per row
+  // A key tile is a sequence of 1 KB lines (one direct-to-LDS wave load each) padded
+  // to 1072 B so that row-wise and transposed reads of 16 rows hit distinct banks.
+  constexpr int RPL = ROWB < 1024 ? 1024 / ROWB : 1;  // rows per line
+  constexpr int LPR = ROWB > 1024 ? ROWB / 1024 : 1;  // lines per row
+  constexpr int NL = KT * LPR / RPL;                  // lines per tile
+  constexpr int LSTRIDE = 1024 + 48;
+  constexpr int QROWB = ROWB + 16;                    // q / o staging row
+  constexpr int TILEB = NL * LSTRIDE;
+  constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
+  // Two stages in two distinct arrays: the compiler then sees that the loads in
+  // flight into one stage do not alias the reads of the other.
+  __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
+  __shared__ int kv0[KT], kv1[KT];
+  __shared__ int sidx[MQA_MAX_TOPK];
   __shared__ float2 cs[64];
 
   // workgroup -> query: 32 consecutive queries per XCD visit (window keys stay in that
@@ -95,103 +108,91 @@ __global__ __launch_bounds__(NW * 64) void sparse_mqa_kernel(MqaArgs a) {
     rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
     cs[threadIdx.x] = make_float2(c, s);
   }
+  if (a.mode == MQA_SELECTED) {
+    const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+    for (int i = threadIdx.x; i < nsel; i += NT) sidx[i] = irow[i];
+  }
 
-  // ---- q[b,t] (H x D, contiguous) -> LDS, coalesced; rows >= H are zero
-  T* qs = reinterpret_cast<T*>(smem);
-  const T* qg = static_cast<const T*>(a.q) + ((int64_t)b * a.S + t) * a.H * D;
+  // ---- q[b,t] (H x D, contiguous) -> LDS (heads 0..HP/2-1 in st0, the rest in st1)
+  const unsigned char* qg =
+      reinterpret_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
   for (int c = threadIdx.x; c < HP * NCH; c += NT) {
-    const int row = c / NCH, col = (c % NCH) * VEC;
-    Vec16<T> v;
-    if (row < a.H) v = load16(qg + (int64_t)row * D + col);
-    else *reinterpret_cast<uint4*>(v.v) = make_uint4(0, 0, 0, 0);
-    store16(qs + row * QROW + col, v);
+    const int row = c / NCH, col = (c % NCH) * 16;
+    const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(qg + (int64_t)row * ROWB + col)
+                              : make_uint4(0, 0, 0, 0);
+    unsigned char* dst = (row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col;
+    *reinterpret_cast<uint4*>(dst) = v;
   }
   __syncthreads();
 
   // ---- Q^T fragments (B operand): lane (head 16w+hl, group g), k-step k holds dims
   // 32k + 8g .. +7, rotated at +P where they fall in the last R dims.
   Frag<T> qf[D / 32];
+  {
+    const int h = 16 * wave + hl;
+    const unsigned char* qrow = (h < HP / 2 ? st0 : st1) + (h % (HP / 2)) * QROWB;
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d0 = 32 * k + 8 * g;
-    qf[k] = load_frag(qs + (16 * wave + hl) * QROW + d0);
-    if (d0 + 8 > rlo) {
+    for (int k = 0; k < D / 32; ++k) {
+      const int d0 = 32 * k + 8 * g;
+      qf[k] = load_frag(reinterpret_cast<const T*>(qrow) + d0);
+      if (d0 + 8 > rlo) {
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const int d = d0 + i;
-        if (d >= rlo) {
-          const float2 r = cs[(d - rlo) >> 1];
-          const float x0 = to_f32(qf[k].v[i]), x1 = to_f32(qf[k].v[i + 1]);
-          qf[k].v[i] = from_f32<T>(x0 * r.x - x1 * r.y);
-          qf[k].v[i + 1] = from_f32<T>(x0 * r.y + x1 * r.x);
+        for (int i = 0; i < 8; i += 2) {
+          const int d = d0 + i;
+          if (d >= rlo) {
+            const float2 r = cs[(d - rlo) >> 1];
+            const float x0 = to_f32(qf[k].v[i]), x1 = to_f32(qf[k].v[i + 1]);
+            qf[k].v[i] = from_f32<T>(x0 * r.x - x1 * r.y);
+            qf[k].v[i + 1] = from_f32<T>(x0 * r.y + x1 * r.x);
+          }
         }
       }
     }
   }
-  __syncthreads();  // the q staging area becomes the key tile
+  __syncthreads();  // the staging area becomes the key tiles
 
-  T* krm = reinterpret_cast<T*>(smem);  // [KT][KROW]  key-major
-  T* vt = krm + KT * KROW;              // [D][VROW]   dim-major, slot-permuted
-  const T* kv_c = static_cast<const T*>(a.kv_c);
-  const T* kv_w = static_cast<const T*>(a.kv_w);
-  const int32_t* irow = a.mode == MQA_SELECTED ? a.idx + ((int64_t)b * a.S + t) * a.topk : nullptr;
+  const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
+  const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
 
-  // Address of key kk of this query's list, or null if it is masked.
-  auto key_ptr = [&](int kk) -> const T* {
+  // Byte offset of (key row r, dim d) inside a tile.
+  auto eoff = [](int r, int d) -> int {
+    const int byte = d * ES;
+    return ((r / RPL) * LPR + byte / 1024) * LSTRIDE + (r % RPL) * ROWB + (byte % 1024);
+  };
+  // Source row of key kk of this query's list; masked keys read this query's own q
+  // row instead (finite data, never used: their probability is 0).
+  auto key_src = [&](int kk, int* ok) -> const unsigned char* {
     if (kk < nsel) {
-      const int s = irow ? irow[kk] : kk;
-      if (s < 0 || s >= n_t) return nullptr;  // malformed selection: ignored
-      return kv_c + ((int64_t)b * a.n_entries + s) * D;
-    }
-    if (kk < nk) return kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * D;
-    return nullptr;
-  };
-
-  // Staging block bi: key group gq = bi & 3 (keys sigma(gq, 0..7)), dims (bi >> 2)*VEC.
-  uint4 pf[BPT][8];
-  int pbits[BPT];
-  auto fetch = [&](int tile) {
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int bi = threadIdx.x + k * NT;
-      int bits = 0;
-      if (bi < NBLK) {
-        const int gq = bi & 3, col = (bi >> 2) * VEC;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const T* p = key_ptr(tile * KT + slot_key(gq, i));
-          pf[k][i] = p ? *reinterpret_cast<const uint4*>(p + col) : make_uint4(0, 0, 0, 0);
-          bits |= (p != nullptr) << i;
-        }
+      const int s = a.mode == MQA_SELECTED ? sidx[kk] : kk;
+      if (s >= 0 && s < n_t) {
+        *ok = 1;
+        return kv_c + ((int64_t)b * a.n_entries + s) * ROWB;
       }
-      pbits[k] = bits;
+    } else if (kk < nk) {
+      *ok = 1;
+      return kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
     }
+    *ok = 0;
+    return qg;
   };
-  auto commit = [&]() {
+  // Direct-to-LDS loads of tile `tile`: wave w loads lines w, w+NW, ...; one 16-byte
+  // piece per lane lands at line base + 16 * lane.
+  auto issue = [&](int tile, unsigned char* sb, int* kv) {
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int bi = threadIdx.x + k * NT;
-      if (bi < NBLK) {
-        const int gq = bi & 3, col = (bi >> 2) * VEC;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint4*>(krm + slot_key(gq, i) * KROW + col) = pf[k][i];
-        // transpose: for each dim of the piece, the 8 keys in slot order
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          T col8[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) col8[i] = reinterpret_cast<const T*>(&pf[k][i])[j];
-          T* dst = vt + (col + j) * VROW + 8 * gq;
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(col8);
-          if constexpr (sizeof(T) == 4)
-            *reinterpret_cast<uint4*>(dst + 4) = *reinterpret_cast<const uint4*>(col8 + 4);
-        }
-        if (col == 0) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kvalid[slot_key(gq, i)] = (pbits[k] >> i) & 1;
-        }
+    for (int L = wave; L < NL; L += NW) {
+      int r, byte;
+      if constexpr (RPL > 1) {
+        r = L * RPL + lane / NCH;
+        byte = (lane % NCH) * 16;
+      } else {
+        r = L / LPR;
+        byte = (L % LPR) * 1024 + lane * 16;
       }
+      int ok;
+      const unsigned char* src = key_src(tile * KT + r, &ok);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
+                                       (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
+      if (byte == 0) kv[r] = ok;
     }
   };
 
@@ -200,29 +201,21 @@ __global__ __launch_bounds__(NW * 64) void sparse_mqa_kernel(MqaArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = (nk + KT - 1) / KT;
-  if (ntiles > 0) {
-    fetch(0);
-    commit();
-  }
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 1 < ntiles) fetch(tile + 1);
-
+  auto compute = [&](const unsigned char* sb, const int* kv) {
     // S^T = K . Q^T : keys 0..15 and 16..31 of the tile
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) {
-      const Frag<T> a0 = load_frag(krm + hl * KROW + 32 * k + 8 * g);
-      const Frag<T> a1 = load_frag(krm + (16 + hl) * KROW + 32 * k + 8 * g);
+      const Frag<T> a0 = load_frag(reinterpret_cast<const T*>(sb + eoff(hl, 32 * k + 8 * g)));
+      const Frag<T> a1 = load_frag(reinterpret_cast<const T*>(sb + eoff(16 + hl, 32 * k + 8 * g)));
       s0 = mfma16x16x32(a0, qf[k], s0);
       s1 = mfma16x16x32(a1, qf[k], s1);
     }
     float z[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = kvalid[4 * g + i] ? s0[i] * a.scale_log2 : -INFINITY;
-      z[4 + i] = kvalid[16 + 4 * g + i] ? s1[i] * a.scale_log2 : -INFINITY;
+      z[i] = kv[4 * g + i] ? s0[i] * a.scale_log2 : -INFINITY;
+      z[4 + i] = kv[16 + 4 * g + i] ? s1[i] * a.scale_log2 : -INFINITY;
     }
     float mt = z[0];
 #pragma unroll
@@ -248,15 +241,40 @@ __global__ __launch_bounds__(NW * 64) void sparse_mqa_kernel(MqaArgs a) {
     }
     l_run += ls;
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T.  The V^T fragment of lane (dim 16db+hl, group g) is keys
+    // sigma(g, 0..7) of that dim: two transposing 8-byte LDS reads (keys 4g..4g+3 and
+    // 16+4g..16+4g+3), each lane addressing key 4g+hl/4 (+16), dims 16db+4(hl%4)..+3.
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const Frag<T> av = load_frag(vt + (16 * db + hl) * VROW + 8 * g);
+      Frag<T> av;
+      if constexpr (ES == 2) {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        const int kr = 4 * g + (hl >> 2), dc = 16 * db + 4 * (hl & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (CSA_LDS i16x4*)(sb + eoff(kr, dc)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (CSA_LDS i16x4*)(sb + eoff(16 + kr, dc)));
+        *reinterpret_cast<i16x4*>(av.v) = lo;
+        *reinterpret_cast<i16x4*>(av.v + 4) = hi;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          av.v[i] = *reinterpret_cast<const T*>(sb + eoff(slot_key(g, i), 16 * db + hl));
+      }
       O[db] = mfma16x16x32(av, pfr, O[db]);
     }
-    __syncthreads();
+  };
+
+  const int ntiles = (nk + KT - 1) / KT;
+  if (ntiles > 0) issue(0, st0, kv0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    if (tile + 1 < ntiles) issue(tile + 1, st1, kv1);
+    compute(st0, kv0);
+    __syncthreads();  // tile+1 landed in st1; every wave is done with st0
     if (tile + 1 < ntiles) {
-      commit();
+      if (tile + 2 < ntiles) issue(tile + 2, st0, kv0);
+      compute(st1, kv1);
       __syncthreads();
     }
   }
@@ -265,31 +283,35 @@ __global__ __launch_bounds__(NW * 64) void sparse_mqa_kernel(MqaArgs a) {
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  T* os = reinterpret_cast<T*>(smem);
+  {
+    const int h = 16 * wave + hl;
+    unsigned char* orow = (h < HP / 2 ? st0 : st1) + (h % (HP / 2)) * QROWB;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    const int d0 = 16 * db + 4 * g;
-    float x[4];
+    for (int db = 0; db < D / 16; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = O[db][i] * inv;
-    if (d0 >= rlo) {
+      for (int i = 0; i < 4; ++i) x[i] = O[db][i] * inv;
+      if (d0 >= rlo) {
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const float2 r = cs[(d0 + i - rlo) >> 1];
-        const float x0 = x[i], x1 = x[i + 1];
-        x[i] = x0 * r.x + x1 * r.y;
-        x[i + 1] = -x0 * r.y + x1 * r.x;
+        for (int i = 0; i < 4; i += 2) {
+          const float2 r = cs[(d0 + i - rlo) >> 1];
+          const float x0 = x[i], x1 = x[i + 1];
+          x[i] = x0 * r.x + x1 * r.y;
+          x[i + 1] = -x0 * r.y + x1 * r.x;
+        }
       }
-    }
-    T* dst = os + (16 * wave + hl) * QROW + d0;
+      T* dst = reinterpret_cast<T*>(orow) + d0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(x[i]);
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(x[i]);
+    }
   }
   __syncthreads();
-  T* og = static_cast<T*>(a.o) + ((int64_t)b * a.S + t) * a.H * D;
+  unsigned char* og = reinterpret_cast<unsigned char*>(a.o) + ((int64_t)b * a.S + t) * a.H * ROWB;
   for (int c = threadIdx.x; c < a.H * NCH; c += NT) {
-    const int row = c / NCH, col = (c % NCH) * VEC;
-    store16(og + (int64_t)row * D + col, load16(os + row * QROW + col));
+    const int row = c / NCH, col = (c % NCH) * 16;
+    const unsigned char* src = (row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col;
+    *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) = *reinterpret_cast<const uint4*>(src);
   }
 }
 
