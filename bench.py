@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="JSON file with per-kernel HBM bytes from rocprofv3 counters")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB twice (a plain copy "
+                         "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -168,6 +171,13 @@ def main():
     ws = bd.workspace(p, op, dev)
     o = torch.empty_like(inp["q"])
     traces = [bd.LayerTrace(p) for _ in range(args.steps)]
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     log(f"[bench] warmup {args.warmup}")

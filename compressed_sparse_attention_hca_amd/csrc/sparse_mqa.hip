@@ -21,8 +21,8 @@
 // stage is being used.  Per tile:
 //   S^T[key, head] = K_tile . Q^T     v_mfma_f32_16x16x32_bf16, keys on M (A from the
 //                                     row-major tile), heads on N (B = rotated q in regs)
-//   online softmax in registers, base-2, max rescale only when the tile max grows by
-//   more than 2^8 (exact: the final normalisation uses the same reference)
+//   softmax in registers, base-2, against a fixed reference (the first tile's max;
+//   exact by shift invariance, with a second pass if later logits could overflow)
 //   O^T[dim, head] += V^T . P^T       dims on M (A read from the same row-major tile with
 //                                     ds_read_b64_tr_b16), heads on N (B = P from S^T)
 // The S^T accumulator gives lane (head, g) keys 4g..4g+3 and 16+4g..16+4g+3; those 8
@@ -57,16 +57,20 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int HP = NW * 16;                       // heads handled (padded)
   constexpr int ES = (int)sizeof(T);
-  constexpr int VEC = 16 / ES;                      // elements per 16-byte piece
   constexpr int KT = 32;                            // keys per tile
   constexpr int ROWB = D * ES;                      // bytes per latent row
   constexpr int NCH = ROWB / 16;                    // 16-byte pieces per row
-  // A key tile is a sequence of 1 KB lines (one direct-to-LDS wave load each) padded
-  // to 1072 B so that row-wise and transposed reads of 16 rows hit distinct banks.
+  // A key tile is a sequence of 1 KB lines, one direct-to-LDS wave load each.  When a
+  // latent row is exactly one line (D = 512 bf16) the 16-byte chunks of row r are
+  // stored XOR-swizzled, chunk c at position c ^ swz(r) with swz(r) = 2(r&3) | (r>>2 &1):
+  // then the 8 rows read together by ds_read_b128 and the 4-row x 32-byte blocks read
+  // by ds_read_b64_tr_b16 both cover the 32 LDS banks without conflicts.  Other row
+  // sizes use lines padded to 1072 B.
   constexpr int RPL = ROWB < 1024 ? 1024 / ROWB : 1;  // rows per line
   constexpr int LPR = ROWB > 1024 ? ROWB / 1024 : 1;  // lines per row
   constexpr int NL = KT * LPR / RPL;                  // lines per tile
-  constexpr int LSTRIDE = 1024 + 48;
+  constexpr bool SWZ = ROWB == 1024 && ES == 2;
+  constexpr int LSTRIDE = SWZ ? 1024 : 1024 + 48;
   constexpr int QROWB = ROWB + 16;                    // q / o staging row
   constexpr int TILEB = NL * LSTRIDE;
   constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
@@ -155,8 +159,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
 
   // Byte offset of (key row r, dim d) inside a tile.
-  auto eoff = [](int r, int d) -> int {
+  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
+  auto eoff = [&](int r, int d) -> int {
     const int byte = d * ES;
+    if constexpr (SWZ) return r * 1024 + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15));
     return ((r / RPL) * LPR + byte / 1024) * LSTRIDE + (r % RPL) * ROWB + (byte % 1024);
   };
   // Source row of key kk of this query's list; masked keys read this query's own q
@@ -184,6 +190,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
       if constexpr (RPL > 1) {
         r = L * RPL + lane / NCH;
         byte = (lane % NCH) * 16;
+      } else if constexpr (SWZ) {
+        r = L;
+        byte = (lane ^ swz(r)) * 16;  // LDS position `lane` holds chunk lane ^ swz(r)
       } else {
         r = L / LPR;
         byte = (L % LPR) * 1024 + lane * 16;
@@ -196,18 +205,61 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // Softmax with a fixed reference (shift invariance): the first tile's max per head,
+  // so the accumulator is never rescaled inside the loop.  If a later tile's max
+  // exceeds the reference by more than 2^64 (not reachable with RMS-normalised inputs,
+  // possible in general), the workgroup runs the tiles again with the largest max
+  // seen as the reference, so every exp2 argument is <= 0 and nothing can overflow.
+  __shared__ int overflow;
+  float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
   f32x4 O[D / 16];
+
+  // Per-lane LDS byte offsets of the fragments this lane reads (constant across tiles).
+  // QK: rows hl and 16+hl, dims 32k+8g..+7 (chunk 4k+g).  With the swizzle the chunk
+  // position is (4k+g) ^ swz = 4(k ^ s2) + ((g ^ s) & 3), s = swz(hl), s2 = s >> 2, so
+  // even and odd k use two bases and 64k stays an immediate.
+  // PV: rows 4g+hl/4 (+16), bytes 32db + 8(hl&3): chunk 2db + hb, hb = (hl>>1)&1;
+  // position (2db+hb) ^ swz = 2(db ^ a) + (hb ^ c), a = hl>>2, c = g&1, so four bases
+  // (by db mod 4) and 128 (db>>2) stays an immediate.
+  int qk_base[2], pv_base[4];
+  if constexpr (SWZ) {
+    const int s = swz(hl), s2 = s >> 2;
+    const int lo = hl * 1024 + (((g ^ s) & 3) << 4);
+    qk_base[0] = lo + (s2 ? 64 : 0);   // k even: 4(k ^ s2) = 4k + 4 s2
+    qk_base[1] = lo - (s2 ? 64 : 0);   // k odd:  4(k ^ s2) = 4k - 4 s2
+    const int a4 = hl >> 2, c = g & 1, hb = (hl >> 1) & 1;
+    const int row = 4 * g + a4;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m)
+      pv_base[m] = row * 1024 + ((m ^ a4) - m) * 32 + ((hb ^ c) << 4) + ((hl & 1) << 3);
+  } else {
+    qk_base[0] = qk_base[1] = eoff(hl, 8 * g);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pv_base[m] = eoff(4 * g + (hl >> 2), 4 * (hl & 3));
+  }
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
 
   auto compute = [&](const unsigned char* sb, const int* kv) {
-    // S^T = K . Q^T : keys 0..15 and 16..31 of the tile
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
+    auto ld_k = [&](int row16, int k) {  // QK A fragment: rows row16+hl, dims 32k+8g..
+      Frag<T> f;
+      const CSA_LDS unsigned char* p =
+          lb + qk_base[k & 1] + (SWZ ? row16 * 1024 + 64 * k : eoff(row16, 32 * k) - eoff(0, 0));
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
+      if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
+      return f;
+    };
+    // S^T = K . Q^T : keys 0..15 and 16..31, one fragment pair ahead
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    Frag<T> n0 = ld_k(0, 0), n1 = ld_k(16, 0);
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) {
-      const Frag<T> a0 = load_frag(reinterpret_cast<const T*>(sb + eoff(hl, 32 * k + 8 * g)));
-      const Frag<T> a1 = load_frag(reinterpret_cast<const T*>(sb + eoff(16 + hl, 32 * k + 8 * g)));
+      const Frag<T> a0 = n0, a1 = n1;
+      if (k + 1 < D / 32) {
+        n0 = ld_k(0, k + 1);
+        n1 = ld_k(16, k + 1);
+      }
       s0 = mfma16x16x32(a0, qf[k], s0);
       s1 = mfma16x16x32(a1, qf[k], s1);
     }
@@ -222,20 +274,14 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (__any(mt > m_run + 8.0f)) {
-      const float mn = fmaxf(m_run, mt);
-      const float al = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mn);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) O[db] *= al;
-      l_run *= al;
-      m_run = mn;
-    }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    m_seen = fmaxf(m_seen, mt);
+    if (m_ref == -INFINITY) m_ref = mt;  // O and l are still zero
+    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
     Frag<T> pfr;
     float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = exp2f(z[i] - mref);
+      const float p = __builtin_amdgcn_exp2f(z[i] - mref);
       ls += p;
       pfr.v[i] = from_f32<T>(p);
     }
@@ -244,39 +290,55 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
     // O^T += V^T . P^T.  The V^T fragment of lane (dim 16db+hl, group g) is keys
     // sigma(g, 0..7) of that dim: two transposing 8-byte LDS reads (keys 4g..4g+3 and
     // 16+4g..16+4g+3), each lane addressing key 4g+hl/4 (+16), dims 16db+4(hl%4)..+3.
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      Frag<T> av;
+    auto ld_v = [&](int db) {
+      Frag<T> f;
       if constexpr (ES == 2) {
-        typedef short i16x4 __attribute__((ext_vector_type(4)));
-        const int kr = 4 * g + (hl >> 2), dc = 16 * db + 4 * (hl & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (CSA_LDS i16x4*)(sb + eoff(kr, dc)));
+        const CSA_LDS unsigned char* p =
+            lb + pv_base[db & 3] + (SWZ ? 32 * db : eoff(0, 16 * db) - eoff(0, 0));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (CSA_LDS i16x4*)(sb + eoff(16 + kr, dc)));
-        *reinterpret_cast<i16x4*>(av.v) = lo;
-        *reinterpret_cast<i16x4*>(av.v + 4) = hi;
+            (CSA_LDS i16x4*)(p + (SWZ ? 16 * 1024 : eoff(16, 0) - eoff(0, 0))));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<i16x8*>(f.v) = v;
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          av.v[i] = *reinterpret_cast<const T*>(sb + eoff(slot_key(g, i), 16 * db + hl));
+          f.v[i] = *(const CSA_LDS T*)(lb + eoff(slot_key(g, i), 16 * db + hl));
       }
+      return f;
+    };
+    Frag<T> nv = ld_v(0);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const Frag<T> av = nv;
+      if (db + 1 < D / 16) nv = ld_v(db + 1);
       O[db] = mfma16x16x32(av, pfr, O[db]);
     }
   };
 
   const int ntiles = (nk + KT - 1) / KT;
-  if (ntiles > 0) issue(0, st0, kv0);
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    if (tile + 1 < ntiles) issue(tile + 1, st1, kv1);
-    compute(st0, kv0);
-    __syncthreads();  // tile+1 landed in st1; every wave is done with st0
-    if (tile + 1 < ntiles) {
-      if (tile + 2 < ntiles) issue(tile + 2, st0, kv0);
-      compute(st1, kv1);
-      __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    if (threadIdx.x == 0) overflow = 0;
+    if (ntiles > 0) issue(0, st0, kv0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      if (tile + 1 < ntiles) issue(tile + 1, st1, kv1);
+      compute(st0, kv0);
+      __syncthreads();  // tile+1 landed in st1; every wave is done with st0
+      if (tile + 1 < ntiles) {
+        if (tile + 2 < ntiles) issue(tile + 2, st0, kv0);
+        compute(st1, kv1);
+        __syncthreads();
+      }
     }
+    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(&overflow, 1);
+    __syncthreads();
+    if (!overflow) break;
+    m_ref = m_seen;  // exact reference for the second pass
   }
 
   // ---- normalise, de-rotate at -P, stage through LDS, write o[b,t] coalesced
@@ -311,6 +373,302 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   for (int c = threadIdx.x; c < a.H * NCH; c += NT) {
     const int row = c / NCH, col = (c % NCH) * 16;
     const unsigned char* src = (row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col;
+    *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 fast path for up to 64 heads: two waves per query, 32 heads per wave on
+// v_mfma_f32_32x32x16_bf16, so every LDS fragment feeds 32 heads and every MFMA does
+// twice the work of the 16x16 shape.  Per wave and 32-key tile:
+//   S^T[32 keys, 32 heads] = sum_k K[:, 16k..16k+15] . Q^T[16k.., heads]   (D/16 MFMAs)
+//     lane (head l%32, g = l/32) receives keys 8j + 4g + i, j, i = 0..3
+//   O^T[32 dims, 32 heads] += V^T[dims, 16 slots] . P^T[16 slots, heads]  (2 per block)
+//     k-step ks takes accumulator rows j = 2ks, 2ks+1: keys 16ks + {4g..4g+3, 8+4g..8+4g+3}
+//     for lane group g; V^T for those keys comes from two transposing LDS reads.
+// The D x 32 fp32 output accumulator (256 registers for D = 512) sits in AGPRs; the
+// wave runs alone on its SIMD and two queries share a CU.
+// ---------------------------------------------------------------------------------
+__device__ inline f32x16 mfma32(const Frag<bf16>& a, const Frag<bf16>& b, f32x16 c) {
+  bf16x8 av, bv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { av[i] = a.v[i]; bv[i] = b.v[i]; }
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void sparse_mqa32_kernel(MqaArgs a) {
+  typedef bf16 T;
+  constexpr int NW = 2, NT = 128, HP = 64, ES = 2, KT = 32;
+  constexpr int ROWB = D * ES;
+  constexpr int NCH = ROWB / 16;
+  constexpr int RPL = ROWB < 1024 ? 1024 / ROWB : 1;
+  constexpr int NL = KT / RPL;
+  constexpr int LSTRIDE = 1024 + 48;
+  constexpr int QROWB = ROWB + 16;
+  constexpr int TILEB = NL * LSTRIDE;
+  constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
+  static_assert(ROWB <= 1024, "rows of at most 1 KB");
+  __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
+  __shared__ uint32_t km0, km1;  // per-tile key validity bits
+  __shared__ int sidx[MQA_MAX_TOPK];
+  __shared__ float2 cs[64];
+
+  const int total = a.B * a.S;
+  int gi = blockIdx.x;
+  const int nfull = total & ~255;
+  if (gi < nfull) {
+    const int xcd = gi & 7, j = gi >> 3;
+    gi = (((j >> 5) << 3) + xcd) * 32 + (j & 31);
+  }
+  gi = total - 1 - gi;
+  const int b = gi / a.S;
+  const int t = gi % a.S;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int n_t = a.mode == MQA_WINDOW_ONLY ? 0 : visible_entries(t, a.ratio);
+  const int nsel = a.mode == MQA_SELECTED ? min(a.topk, n_t) : n_t;
+  const int nwin = window_count(t, a.window);
+  const int wlo = window_lo(t, a.window);
+  const int nk = nsel + nwin;
+  const int64_t P = a.pos0 + t;
+  const int rlo = D - a.R;
+
+  if (threadIdx.x < a.R / 2) {
+    float c, s;
+    rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
+    cs[threadIdx.x] = make_float2(c, s);
+  }
+  if (a.mode == MQA_SELECTED) {
+    const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+    for (int i = threadIdx.x; i < nsel; i += NT) sidx[i] = irow[i];
+  }
+
+  // q[b,t] -> LDS (heads 0..31 in st0, 32..63 in st1), coalesced
+  const unsigned char* qg =
+      reinterpret_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
+  for (int c = threadIdx.x; c < HP * NCH; c += NT) {
+    const int row = c / NCH, col = (c % NCH) * 16;
+    const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(qg + (int64_t)row * ROWB + col)
+                              : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>((row < 32 ? st0 : st1) + (row % 32) * QROWB + col) = v;
+  }
+  __syncthreads();
+
+  // Q^T fragments: lane (head 32w + l32, g), k-step k: dims 16k + 8g .. +7, rotated
+  Frag<T> qf[D / 16];
+  {
+    const unsigned char* qrow = (wave == 0 ? st0 : st1) + l32 * QROWB;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const int d0 = 16 * k + 8 * g;
+      qf[k] = load_frag(reinterpret_cast<const T*>(qrow) + d0);
+      if (d0 + 8 > rlo) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const int d = d0 + i;
+          if (d >= rlo) {
+            const float2 r = cs[(d - rlo) >> 1];
+            const float x0 = to_f32(qf[k].v[i]), x1 = to_f32(qf[k].v[i + 1]);
+            qf[k].v[i] = from_f32<T>(x0 * r.x - x1 * r.y);
+            qf[k].v[i + 1] = from_f32<T>(x0 * r.y + x1 * r.x);
+          }
+        }
+      }
+    }
+  }
+  // Register classes: the D x 32 accumulator in AGPRs, the q fragments in VGPRs (empty
+  // asm statements that only constrain allocation).
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = qf[k].v[i];
+    asm volatile("" : "+v"(v));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[k].v[i] = v[i];
+  }
+  __syncthreads();
+
+  const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
+  const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
+  auto eoff = [](int r, int d) -> int {
+    return (r / RPL) * LSTRIDE + (r % RPL) * ROWB + d * ES;
+  };
+  auto key_src = [&](int kk, int* ok) -> const unsigned char* {
+    if (kk < nsel) {
+      const int s = a.mode == MQA_SELECTED ? sidx[kk] : kk;
+      if (s >= 0 && s < n_t) {
+        *ok = 1;
+        return kv_c + ((int64_t)b * a.n_entries + s) * ROWB;
+      }
+    } else if (kk < nk) {
+      *ok = 1;
+      return kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
+    }
+    *ok = 0;
+    return qg;
+  };
+  // wave w loads lines w, w+2, ...; the validity of the tile's 32 keys is gathered
+  // into one mask word (the lane loading byte 0 of a row sets its bit)
+  auto issue = [&](int tile, unsigned char* sb, uint32_t* km) {
+    uint32_t bits = 0;
+#pragma unroll 1
+    for (int L = wave; L < NL; L += NW) {
+      int r, byte;
+      if constexpr (RPL > 1) {
+        r = L * RPL + lane / NCH;
+        byte = (lane % NCH) * 16;
+      } else {
+        r = L;
+        byte = lane * 16;
+      }
+      int ok;
+      const unsigned char* src = key_src(tile * KT + r, &ok);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
+                                       (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
+      if (byte == 0 && ok) bits |= 1u << r;
+    }
+    // OR the bits of both waves: wave 0 stores, wave 1 adds after the barrier-free
+    // atomic (LDS atomics order within the workgroup)
+    for (int m = 32; m >= 1; m >>= 1) bits |= (uint32_t)__shfl_xor((int)bits, m, 64);
+    if (lane == 0) atomicOr(km, bits);
+  };
+
+  // Softmax with a fixed reference (shift invariance): the first tile's max per head.
+  // No accumulator rescale inside the loop.  If a later tile's max exceeds the
+  // reference by more than 2^64 (not reachable with RMS-normalised inputs, possible
+  // in general), the workgroup runs the tiles again with the largest max seen as the
+  // reference, so every exp2 argument is <= 0 and nothing can overflow.
+  __shared__ int overflow;
+  float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
+  f32x16 O[D / 32];
+
+  auto compute = [&](const unsigned char* sb, uint32_t kmask) {
+    f32x16 s = {};
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const Frag<T> ka = load_frag(reinterpret_cast<const T*>(sb + eoff(l32, 16 * k + 8 * g)));
+      s = mfma32(ka, qf[k], s);
+    }
+    // lane (head l32, g): element 4j+i is key 8j + 4g + i
+    float z[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 8 * j + 4 * g + i;
+        const float v = ((kmask >> key) & 1u) ? s[4 * j + i] * a.scale_log2 : -INFINITY;
+        z[4 * j + i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    m_seen = fmaxf(m_seen, mt);
+    if (m_ref == -INFINITY) m_ref = mt;  // O and l are still zero
+    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+    Frag<T> pf[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(z[e] - mref);
+      ls += p;
+      pf[e >> 3].v[e & 7] = from_f32<T>(p);
+    }
+    l_run += ls;
+    // V^T fragments: 16-lane group h = lane/16 covers dims 32db + 16(h&1) + 0..15;
+    // lane j of the group addresses key row base + j/4, dims + 4(j%4)
+    const int hj = lane & 15, hh = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        const int kr = 16 * ks + 4 * g + (hj >> 2);
+        const int dc = 32 * db + 16 * hh + 4 * (hj & 3);
+        Frag<T> av;
+        *reinterpret_cast<i16x4*>(av.v) =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(sb + eoff(kr, dc)));
+        *reinterpret_cast<i16x4*>(av.v + 4) =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(sb + eoff(kr + 8, dc)));
+        O[db] = mfma32(av, pf[ks], O[db]);
+      }
+      asm volatile("" : "+a"(O[db]));
+    }
+  };
+
+  const int ntiles = (nk + KT - 1) / KT;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+    {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+      asm volatile("" : "+a"(O[db]));
+    }
+    l_run = 0.f;
+    if (threadIdx.x == 0) { km0 = 0u; km1 = 0u; overflow = 0; }
+    __syncthreads();
+    if (ntiles > 0) issue(0, st0, &km0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      if (tile + 1 < ntiles) issue(tile + 1, st1, &km1);
+      compute(st0, km0);
+      __syncthreads();
+      if (threadIdx.x == 0) km0 = 0u;
+      if (tile + 1 < ntiles) {
+        if (tile + 2 < ntiles) {
+          __syncthreads();  // km0 cleared before it is OR-ed again
+          issue(tile + 2, st0, &km0);
+        }
+        compute(st1, km1);
+        __syncthreads();
+        if (threadIdx.x == 0) km1 = 0u;
+      }
+    }
+    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(&overflow, 1);
+    __syncthreads();
+    if (!overflow) break;
+    m_ref = m_seen;  // exact reference for the second pass
+  }
+
+  // normalise, de-rotate, stage by head rows, write o[b,t] coalesced
+  l_run += __shfl_xor(l_run, 32, 64);
+  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  __syncthreads();
+  {
+    unsigned char* orow = (wave == 0 ? st0 : st1) + l32 * QROWB;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * g;
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = O[db][4 * j + i] * inv;
+        if (d0 >= rlo) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float2 r = cs[(d0 + i - rlo) >> 1];
+            const float x0 = x[i], x1 = x[i + 1];
+            x[i] = x0 * r.x + x1 * r.y;
+            x[i + 1] = -x0 * r.y + x1 * r.x;
+          }
+        }
+        T* dst = reinterpret_cast<T*>(orow) + d0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(x[i]);
+      }
+  }
+  __syncthreads();
+  unsigned char* og = reinterpret_cast<unsigned char*>(a.o) + ((int64_t)b * a.S + t) * a.H * ROWB;
+  for (int c = threadIdx.x; c < a.H * NCH; c += NT) {
+    const int row = c / NCH, col = (c % NCH) * 16;
+    const unsigned char* src = (row < 32 ? st0 : st1) + (row % 32) * QROWB + col;
     *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) = *reinterpret_cast<const uint4*>(src);
   }
 }
