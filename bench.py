@@ -52,6 +52,8 @@ def kernel_work(cfg, wl):
     }
     if cfg.kind == "csa":
         work["indexer"] = (f["indexer"], "flops", "mfma")
+        # fused indexer + selection: the indexer's FLOPs (the selection reads no scores)
+        work["index_topk"] = (f["indexer"], "flops", "mfma")
         # read every visible score once, write K indices + n_visible per row
         work["topk"] = (4 * f["visible_pairs"] + B * S * (4 * cfg.topk + 4), "bytes", "hbm")
     return work

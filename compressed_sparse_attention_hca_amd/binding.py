@@ -90,7 +90,8 @@ EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_sparse_mqa
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
 
-KERNEL_NAMES = {0: "compress", 1: "window_rope", 2: "indexer", 3: "topk", 4: "attention"}
+KERNEL_NAMES = {0: "compress", 1: "window_rope", 2: "indexer", 3: "topk", 4: "attention",
+                5: "index_topk"}
 
 
 def last_error() -> str:

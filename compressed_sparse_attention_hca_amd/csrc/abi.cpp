@@ -49,6 +49,11 @@ int32_t n_chunks(const WsPlan& plan, int32_t S) {
   return plan.chunk_rows > 0 ? (S + plan.chunk_rows - 1) / plan.chunk_rows : 0;
 }
 
+// Kernel launches of the indexer/top-k stage: one fused launch, or two per chunk.
+int32_t index_launches(const csa_params_t& p, const WsPlan& plan) {
+  return p.topk <= kFusedTopkMax ? 1 : 2 * n_chunks(plan, p.S);
+}
+
 csa_status_t check_ws(const csa_params_t* p, int32_t op, void* ws, size_t ws_bytes, WsPlan* plan) {
   *plan = plan_workspace(*p, op);
   if (plan->total == 0) return CSA_OK;
@@ -63,9 +68,14 @@ csa_status_t check_ws(const csa_params_t* p, int32_t op, void* ws, size_t ws_byt
 csa_status_t run_index_topk(const csa_params_t* p, const void* q_idx, const float* w_idx,
                             const void* k_idx, int32_t* idx, int32_t* nvis, unsigned char* ws,
                             const WsPlan& plan, hipStream_t st, Tracer* tr = nullptr) {
-  float* scores = reinterpret_cast<float*>(ws + plan.scores);
   Tracer none;
   if (!tr) tr = &none;
+  if (p->topk <= kFusedTopkMax) {
+    CSA_HIP(launch_index_topk(*p, q_idx, w_idx, k_idx, idx, nvis, st), "indexer/top-k launch");
+    CSA_HIP(tr->mark(CSA_KERNEL_INDEX_TOPK, st), "event record");
+    return CSA_OK;
+  }
+  float* scores = reinterpret_cast<float*>(ws + plan.scores);
   for (int32_t t0 = 0; t0 < p->S; t0 += plan.chunk_rows) {
     const int32_t rows = p->S - t0 < plan.chunk_rows ? p->S - t0 : plan.chunk_rows;
     CSA_HIP(launch_index_scores(*p, q_idx, w_idx, k_idx, scores, plan.ld, t0, rows, st), "indexer launch");
@@ -235,7 +245,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
   void* kv_c = in->kv_c_out ? in->kv_c_out : static_cast<void*>(w + plan.kv_c);
   void* kv_w = w + plan.kv_w;
   if (tr->events) {
-    const int32_t need = 4 + (csa_layer ? 2 * n_chunks(plan, p->S) : 0);
+    const int32_t need = 4 + (csa_layer ? index_launches(*p, plan) : 0);
     if (tr->n < need || !tr->kinds) {
       set_error("traced call needs %d events and a kinds array, got %d", need, tr->n);
       return CSA_ERR_INVALID_ARG;
@@ -278,7 +288,7 @@ int32_t csa_trace_events(const csa_params_t* p, int32_t op) {
   const bool csa_layer = op == CSA_OP_CSA_FWD;
   const uint32_t need = csa_layer ? (Need::COMPRESS | Need::INDEX | Need::MQA) : (Need::COMPRESS | Need::MQA);
   if (validate_params(p, need, false) != CSA_OK) return 0;
-  return 4 + (csa_layer ? 2 * n_chunks(plan_workspace(*p, op), p->S) : 0);
+  return 4 + (csa_layer ? index_launches(*p, plan_workspace(*p, op)) : 0);
 }
 
 static csa_status_t traced(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,

@@ -103,7 +103,7 @@ WsPlan plan_workspace(const csa_params_t& p, int32_t op) {
     w.idx = take(B * S * (size_t)p.topk * 4);
     w.nvis = take(B * S * 4);
   }
-  if (idx) {
+  if (idx && p.topk > kFusedTopkMax) {  // separate scores + top-k kernels over chunks
     w.ld = (int64_t)align_up(n > 0 ? n : 1, 32);
     const size_t row_bytes = B * (size_t)w.ld * 4;
     size_t rows = row_bytes ? kScoresTarget / row_bytes : S;

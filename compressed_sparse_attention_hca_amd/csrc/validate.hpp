@@ -15,6 +15,7 @@ const char* last_error();
 constexpr int32_t kMaxTopk = 2048;
 constexpr int32_t kMaxEntries = 32768;  // entries per row the top-k kernel holds
 constexpr size_t kScoresTarget = size_t(128) << 20;  // bytes of scores per chunk
+constexpr int32_t kFusedTopkMax = 512;  // top-k selected inside the indexer kernel
 
 enum class Need : uint32_t {
   COMPRESS = 1u << 0,
@@ -40,7 +41,7 @@ struct WsPlan {
   size_t kv_c = 0, kv_w = 0, idx = 0, nvis = 0, scores = 0;  // offsets
   size_t total = 0;
   int64_t ld = 0;         // scores row stride (floats)
-  int32_t chunk_rows = 0; // query rows per indexer/top-k chunk
+  int32_t chunk_rows = 0; // query rows per indexer/top-k chunk (0: fused, no scores)
 };
 WsPlan plan_workspace(const csa_params_t& p, int32_t op);
 

@@ -138,7 +138,9 @@ csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const fl
 /* Stage 3: indexer scores over visible entries and the top-k per query.
  *   idx [B,S,topk] int32: the min(topk, n_visible(t)) selected entries in ascending
  *   order, then -1 padding; ties at the k-th score go to the smaller entry index.
- *   n_visible [B,S] int32.  ws: csa_workspace_bytes(p, CSA_OP_INDEX_TOPK) bytes. */
+ *   n_visible [B,S] int32.  ws: csa_workspace_bytes(p, CSA_OP_INDEX_TOPK) bytes (none
+ *   when topk <= 512: the selection is made inside the indexer kernel and no score
+ *   leaves the chip; larger topk scores query chunks into the workspace, then selects). */
 csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const float* w_idx,
                             const void* k_idx, int32_t* idx, int32_t* n_visible, void* ws,
                             size_t ws_bytes, void* stream);
@@ -167,9 +169,10 @@ csa_status_t hca_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, voi
 typedef enum {
   CSA_KERNEL_COMPRESS = 0,    /* pooling + RMSNorm + RoPE of entries */
   CSA_KERNEL_WINDOW_ROPE = 1, /* rotation of the raw window latents */
-  CSA_KERNEL_INDEXER = 2,     /* indexer scores (one launch per query chunk) */
-  CSA_KERNEL_TOPK = 3,        /* top-k selection (one launch per query chunk) */
-  CSA_KERNEL_ATTENTION = 4    /* sparse MQA + de-rotation */
+  CSA_KERNEL_INDEXER = 2,     /* indexer scores (one launch per query chunk, topk > 512) */
+  CSA_KERNEL_TOPK = 3,        /* top-k selection (one launch per query chunk, topk > 512) */
+  CSA_KERNEL_ATTENTION = 4,   /* sparse MQA + de-rotation */
+  CSA_KERNEL_INDEX_TOPK = 5   /* indexer scores fused with top-k (topk <= 512) */
 } csa_kernel_t;
 
 /* Number of events the traced variant of `op` (CSA_OP_CSA_FWD or CSA_OP_HCA_FWD)

@@ -117,10 +117,13 @@ def test_index_topk_rejects():
     assert call(p_c1(idx_dim=256)) == bd.CSA_ERR_UNSUPPORTED
     assert call(p_c1(S=4 * 40000)) == bd.CSA_ERR_UNSUPPORTED
     assert call(p_c1(), idx=None) == bd.CSA_ERR_INVALID_ARG
-    need = bd.workspace_bytes(p_c1(), bd.OP_INDEX_TOPK)
-    assert need > 0
-    assert call(p_c1(), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
-    assert call(p_c1(), ws=None) == bd.CSA_ERR_INVALID_ARG
+    # top-k <= 512 is selected inside the indexer kernel: no workspace
+    assert bd.workspace_bytes(p_c1(), bd.OP_INDEX_TOPK) == 0
+    # larger top-k scores query chunks into the workspace first
+    need = bd.workspace_bytes(p_c1(topk=1024), bd.OP_INDEX_TOPK)
+    assert need >= 64 * 1024 * 4  # at least 64 query rows of 1024 fp32 scores
+    assert call(p_c1(topk=1024), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
+    assert call(p_c1(topk=1024), ws=None) == bd.CSA_ERR_INVALID_ARG
 
 
 def test_index_scores_rejects_rows_and_ld():

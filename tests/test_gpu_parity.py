@@ -131,6 +131,23 @@ def test_topk_parity_full(bd, name):
     assert swaps <= cfg.S // 100, swaps
 
 
+def test_topk_parity_chunked_path(bd):
+    """top-k above 512 takes the separate scores + selection kernels over query chunks."""
+    cfg = wl.C1.replace(S=8192, topk=1024, name="c1_topk1024")
+    inp = gen(cfg)
+    idx, nv = bd.index_topk(bd.params(cfg), inp["q_idx"], inp["w_idx"], inp["k_idx"])
+    torch.cuda.synchronize()
+    idx, nv = idx.cpu().numpy(), nv.cpu().numpy()
+    ki = Lazy(inp["k_idx"])[0]
+    swaps = 0
+    for t in list(range(0, 8192, 97)) + [4095, 4096, 4099, 8191]:
+        n = O.visible_entries(t, cfg.ratio)
+        assert nv[0, t] == n
+        sc = O.indexer_scores_row(Lazy(inp["q_idx"])[0, t], Lazy(inp["w_idx"])[0, t], ki, n)
+        swaps += check_selection(idx[0, t], n, cfg.topk, sc, O.topk_row(sc, cfg.topk))
+    assert swaps <= 2, swaps
+
+
 # ------------------------------------------------------------- whole layer ---------
 
 def layer_check(bd, cfg, rows=None):
