@@ -31,6 +31,10 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Pointer qualifier for LDS (address space 3): reads through it compile to ds_* ops.
+#define CSA_LDS __attribute__((address_space(3)))
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(bf16 x) { return (float)x; }

@@ -34,6 +34,11 @@ struct IndexArgs {
   int32_t chunk_qb_min[IDX_MAX_CHUNKS];      // first query block that needs the chunk
 };
 
+// ReLU as one integer max on the bit pattern: every negative float (and -0) is a
+// negative int32, every positive float a positive one.  fmaxf(x, 0) would cost two
+// instructions on MFMA results, which the compiler cannot prove NaN-canonical.
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // 32x32 fragment: lane l holds row/col (l % 32) and k-slots 8*(l/32) .. +7.  bf16 is
 // one v_mfma_f32_32x32x16_bf16; fp32 issues eight v_mfma_f32_32x32x2_f32 (instruction
 // i consumes element i), summing the same 16 k-slots.
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaf(w[hb][i], fmaxf(acc[hb][i], 0.f), v);
+        for (int i = 0; i < 16; ++i) v = fmaf(w[hb][i], relu(acc[hb][i]), v);
       v += __shfl_xor(v, 32, 64);
       const int e = eb + l32;
       if (g == 0 && e < n_t) srow[e] = v;
@@ -184,15 +189,37 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
 // the same MFMA tiles and epilogue as index_scores_kernel and keeps a streaming
 // selection in LDS: a score whose order-preserving key exceeds the wave's threshold is
 // appended (entries arrive in ascending order, so the buffer stays sorted by index).
-// When the buffer is nearly full the wave compacts it to exactly the top-k by (key
-// desc, index asc) with a wave-local radix select, and the k-th key becomes the new
-// threshold.  An entry at or below the threshold has at least k entries that beat it
-// (a higher key, or an equal key with a smaller index), so the final set is exact.
+// When the buffer is nearly full the wave prunes it with one radix pass to the keys
+// at or above a bound that at least k buffered keys reach, and the bound becomes the
+// new threshold; at the end an exact radix select keeps the top-k by (key desc, index
+// asc).  A dropped or refused entry always has at least k buffered entries that beat
+// it (a higher key, or an equal key and a smaller index), so the final set is exact.
+//
+// Entry tiles of k_I (64 rows) go straight from global memory into a three-stage LDS
+// ring (global_load_lds), two tiles ahead of the one being multiplied.  Rows are
+// padded by 16 bytes, so the fragment reads are free of bank conflicts and their
+// addresses are one base plus immediate offsets; the DMA simply also fills the pads.
+// Each wave issues the MFMAs of its next 32-entry block next to the epilogue of the
+// previous one (branch-free), so the scoring VALU work overlaps the matrix core.
 // ---------------------------------------------------------------------------------
 constexpr int FT_WAVES = 8;
-constexpr int FT_TILE = 64;
-constexpr int FT_CAP = 1024;   // candidates per query
+constexpr int FT_TILE = 64;    // entries per LDS stage (two 32-entry MFMA blocks)
 constexpr int FT_MAXK = 512;   // largest top-k of the fused path
+constexpr int FT_LDS = 160 * 1024;
+
+template <typename T, int DI> struct FtShape {
+  static constexpr int ROWB = DI * (int)sizeof(T);       // bytes per k_I row
+  static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  static constexpr int SPR = CPR + 1;                    // LDS slots per row (one pad)
+  static constexpr int ROWP = SPR * 16;                  // padded row pitch in LDS
+  static constexpr int STAGE = FT_TILE * ROWP;           // bytes per ring stage
+  static constexpr int NI = STAGE / 1024;                // 1 KB DMA instructions per stage
+  static constexpr int LPW = (NI + FT_WAVES - 1) / FT_WAVES;  // DMA lines per wave (max)
+  static constexpr int CAP_FIT = (FT_LDS - 3 * STAGE - FT_WAVES * 1024 - 256) / (FT_WAVES * 8) / 64 * 64;
+  static constexpr int CAP = CAP_FIT < 2048 ? CAP_FIT : 2048;  // candidates per query
+  static_assert(STAGE % 1024 == 0, "a stage is whole 1 KB DMA lines");
+  static_assert(CAP >= FT_MAXK + 2 * FT_TILE + 2, "candidate buffer too small");
+};
 
 struct IndexTopkArgs {
   const void* q_idx;
@@ -219,34 +246,53 @@ __device__ inline int wave_excl_scan(int v) {
   return x - v;
 }
 
+__device__ inline uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m, 64));
+  return x;
+}
+__device__ inline uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m, 64));
+  return x;
+}
+
 #define CSA_WAVE_FENCE() __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront")
 
-// Keep exactly the top `K` of ckey/cidx[0..c) in place (in buffer order); returns the
-// k-th key.  Wave-local: every lane of the wave calls it.
-__device__ inline uint32_t wave_compact(uint32_t* ckey, int* cidx, int* hist, int c, int K) {
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their "no wait" maxima), optionally also
+// draining this wave's LDS operations.
+template <int N, bool LGKM0>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((N >> 4) << 14));
+}
+
+struct Pruned {
+  int c;           // keys kept
+  uint32_t theta;  // admit later keys strictly above this
+  uint32_t kmin;   // lower bound of every kept key (and of later admissions)
+};
+
+// Shrink the candidates ckey/cidx[0..c) of one wave, in place and in buffer order.
+// kmin <= every key <= kmax (wave-uniform).  An 8-bit radix pass at a time narrows
+// the prefix of the k-th largest key.  EXACT keeps exactly the top K by (key desc,
+// buffer position asc); otherwise the wave may stop as soon as the keys at or above
+// the current prefix number at most `target` (>= K), and keeps all of them.
+template <bool EXACT>
+__device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K, int target,
+                              uint32_t kmin, uint32_t kmax) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  // common high bits of the buffered keys
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = lane; i < c; i += 64) {
-    const uint32_t k = ckey[i];
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, 64));
-  }
   const uint32_t diff = kmin ^ kmax;
   int shift = diff ? 32 - __clz(diff) : 0;
   uint64_t prefix = (uint64_t)kmin >> shift;
-  int rem = K;  // slots left among keys whose bits above `shift` equal `prefix`
+  int rem = K;           // slots left among keys whose bits above `shift` equal prefix
+  bool keep_eq = false;  // keep every key equal to the prefix (no tie cut needed)
   while (shift > 0) {
     const int w = shift >= 8 ? 8 : shift;
     const int lo = shift - w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+    *reinterpret_cast<int4*>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
     CSA_WAVE_FENCE();
     for (int i = lane; i < c; i += 64) {
       const uint32_t k = ckey[i];
@@ -254,13 +300,9 @@ __device__ inline uint32_t wave_compact(uint32_t* ckey, int* cidx, int* hist, in
     }
     CSA_WAVE_FENCE();
     // lane l holds digits 255-4l .. 252-4l (top digits first)
-    int cnt[4], sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 255 - 4 * lane - j;
-      cnt[j] = d < (1 << w) ? hist[d] : 0;
-      sum += cnt[j];
-    }
+    const int4 h4 = *reinterpret_cast<const int4*>(&hist[252 - 4 * lane]);
+    const int cnt[4] = {h4.w, h4.z, h4.y, h4.x};
+    const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
     int above = wave_excl_scan(sum);
     int sel = -1, sel_above = 0, sel_cnt = 0;
 #pragma unroll
@@ -281,10 +323,14 @@ __device__ inline uint32_t wave_compact(uint32_t* ckey, int* cidx, int* hist, in
     prefix = (prefix << w) | (uint64_t)sel;
     shift = lo;
     CSA_WAVE_FENCE();
-    if (sel_cnt == rem) break;  // every key with this prefix is kept
+    if (sel_cnt == rem || (!EXACT && K - rem + sel_cnt <= target)) {
+      keep_eq = true;
+      break;
+    }
   }
-  // stable in-place compaction: key above the prefix, or equal and among the first rem
+  // stable in-place compaction; track the bounds of what is kept
   int out = 0, eq_seen = 0;
+  uint32_t nmin = 0xffffffffu;
   for (int base = 0; base < c; base += 64) {
     const int i = base + lane;
     uint32_t k = 0;
@@ -297,40 +343,45 @@ __device__ inline uint32_t wave_compact(uint32_t* ckey, int* cidx, int* hist, in
     const bool gt = i < c && kp > prefix;
     const bool eq = i < c && kp == prefix;
     const uint64_t be = __ballot(eq);
-    const bool keep = gt || (eq && eq_seen + __popcll(be & lt) < rem);
+    const bool keep = gt || (eq && (keep_eq || eq_seen + __popcll(be & lt) < rem));
     const uint64_t bk = __ballot(keep);
     CSA_WAVE_FENCE();  // all reads of this chunk precede the writes below
     if (keep) {
       const int pos = out + __popcll(bk & lt);
       ckey[pos] = k;
       cidx[pos] = id;
+      nmin = min(nmin, k);
     }
     out += __popcll(bk);
     eq_seen += __popcll(be);
     CSA_WAVE_FENCE();
   }
-  // the k-th key: smallest kept key (prefix padded with zeros bounds it from below)
-  uint32_t kth = 0xffffffffu;
-  for (int i = lane; i < K; i += 64) kth = min(kth, ckey[i]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) kth = min(kth, (uint32_t)__shfl_xor((int)kth, m, 64));
-  CSA_WAVE_FENCE();
-  return kth;
+  Pruned r;
+  r.c = out;
+  const uint32_t T = (uint32_t)(prefix << shift);
+  // keep_eq: every kept key is >= T and at least K of them are kept, so a later key
+  // below T is beaten K times.  Otherwise the kept set is exactly the top K and a
+  // later key equal to the smallest kept one loses on index.
+  const uint32_t kept_min = wave_min(nmin);
+  r.theta = (keep_eq && out > K) ? (T ? T - 1u : 0u) : kept_min;
+  r.kmin = min(kept_min, r.theta + 1u);  // later admissions are above theta
+  return r;
 }
 
 template <typename T, int DI>
 __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs a) {
+  using SH = FtShape<T, DI>;
   constexpr int KS = DI / 16;
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int ROW = DI + 16 / sizeof(T);
   constexpr int HB = 2;
-  constexpr int NT = FT_WAVES * 64;
-  constexpr int CHUNKS_PER_TILE = FT_TILE * DI / VEC;
-  constexpr int PER_THREAD = (CHUNKS_PER_TILE + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) T tile[2][FT_TILE * ROW];
-  __shared__ uint32_t ckey[FT_WAVES][FT_CAP];
-  __shared__ int cidx[FT_WAVES][FT_CAP];
-  __shared__ int hist[FT_WAVES][256];
+  constexpr int CAP = SH::CAP;
+  // three distinct arrays, so the compiler can tell a stage being read from the
+  // stages that DMA writes are still in flight to
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[SH::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[SH::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[SH::STAGE];
+  __shared__ uint32_t ckey[FT_WAVES][CAP];
+  __shared__ int cidx[FT_WAVES][CAP];
+  __shared__ __attribute__((aligned(16))) int hist[FT_WAVES][256];
 
   // latest (heaviest) query blocks first
   const int id = a.B * a.qblocks - 1 - (int)blockIdx.x;
@@ -362,6 +413,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
         for (int i = 0; i < 8; ++i) qa[hb][ks].v[i] = from_f32<T>(0.f);
       }
     }
+    // accumulator element 4j+i is head hb*32 + 8j + 4g + i
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -371,92 +423,131 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       }
   }
 
-  const T* kbase = static_cast<const T*>(a.k_idx) + (int64_t)b * a.n_entries * DI;
-  uint4 pf[PER_THREAD];
-  auto fetch = [&](int e0) {
+  // Stage layout: row r at r * ROWP, chunk c of the row at slot r * SPR + c; the DMA
+  // line L of a stage covers slots 64L .. 64L+63, one per lane.  A lane's row and
+  // chunk do not depend on the tile, so they are worked out once.
+  const unsigned char* kbase =
+      static_cast<const unsigned char*>(a.k_idx) + (int64_t)b * a.n_entries * SH::ROWB;
+  int dma_row[SH::LPW], dma_off[SH::LPW];
 #pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) {
-      const int cI = threadIdx.x + k * NT;
-      const int row = cI / (DI / VEC);
-      const int col = (cI % (DI / VEC)) * VEC;
-      pf[k] = (cI < CHUNKS_PER_TILE && e0 + row < n_blk)
-                  ? *reinterpret_cast<const uint4*>(kbase + (int64_t)(e0 + row) * DI + col)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto commit = [&](int buf) {
+  for (int j = 0; j < SH::LPW; ++j) {
+    const int slot = (wave + j * FT_WAVES) * 64 + lane;
+    const int ch = slot % SH::SPR;
+    dma_row[j] = slot / SH::SPR;
+    dma_off[j] = ch < SH::CPR ? ch * 16 : 0;  // a pad slot reloads chunk 0
+  }
+  auto issue = [&](int tile, unsigned char* st) {
 #pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) {
-      const int cI = threadIdx.x + k * NT;
-      if (cI < CHUNKS_PER_TILE) {
-        const int row = cI / (DI / VEC);
-        const int col = (cI % (DI / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(&tile[buf][row * ROW + col]) = pf[k];
+    for (int j = 0; j < SH::LPW; ++j) {
+      const int L = wave + j * FT_WAVES;
+      if (L < SH::NI) {  // wave-uniform
+        const int row = min(tile * FT_TILE + dma_row[j], n_blk - 1);  // past the end: a valid row
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(kbase + (int64_t)row * SH::ROWB + dma_off[j]),
+            (CSA_LDS void*)(st + L * 1024), 16, 0, 0);
       }
     }
   };
+  // B fragment of block nb, k-step ks: row nb*32 + l32, elements ks*16 + 8g .. +7
+  auto frag = [&](const unsigned char* st, int nb, int ks) -> Frag<T> {
+    const CSA_LDS unsigned char* p = (const CSA_LDS unsigned char*)st + (nb * 32 + l32) * SH::ROWP +
+                                     (ks * 16 + g * 8) * (int)sizeof(T);
+    Frag<T> f;
+    *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
+    if constexpr (sizeof(T) == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
+    return f;
+  };
+  auto mfma_block = [&](const unsigned char* st, int nb, f32x16* acc) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const Frag<T> kb = frag(st, nb, ks);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb, acc[hb]);
+    }
+  };
 
-  uint32_t theta = 0u;  // admit keys strictly above (every real score's key is > 0)
-  int c = 0;
   uint32_t* my_key = ckey[wave];
   int* my_idx = cidx[wave];
   int* my_hist = hist[wave];
+  uint32_t theta = 0u;                      // admit keys strictly above
+  uint32_t kmin = 1u, kmax_l = 0u;          // bounds of buffered keys (kmax per lane)
+  int c = 0;
+
+  // ReLU(.) * w summed over the lane's 16 heads of each block (four independent
+  // partial sums), then across the two lane halves; admit into the buffer.
+  auto epilogue = [&](const f32x16* acc, int eb) {
+    float v4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v4[i & 3] = fmaf(w[hb][i], relu(acc[hb][i]), v4[i & 3]);
+    const float v = (v4[0] + v4[1]) + (v4[2] + v4[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int e = eb + l32;
+    const uint32_t key = score_key(s);
+    const bool admit = g == 0 && e >= 0 && e < n_t && key > theta;
+    const uint64_t bm = __ballot(admit);
+    // branch-free append: refused lanes all write the first free slot (c + 32 < CAP
+    // holds here, see make_room)
+    const int pos = c + __popcll(admit ? bm & lt : bm);
+    my_key[pos] = key;
+    my_idx[pos] = e;
+    kmax_l = admit ? max(kmax_l, key) : kmax_l;
+    c += __popcll(bm);
+  };
 
   const int ntiles = (n_blk + FT_TILE - 1) / FT_TILE;
-  if (ntiles > 0) {
-    fetch(0);
-    commit(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int e0 = it * FT_TILE;
-    if (it + 1 < ntiles) fetch(e0 + FT_TILE);
-    const T* tb = tile[it & 1];
-    if (!select_all) {
-#pragma unroll
-      for (int nb = 0; nb < FT_TILE / 32; ++nb) {
-        const int eb = e0 + nb * 32;
-        if (eb < n_t) {  // wave-uniform
-          f32x16 acc[HB];
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const Frag<T> kb = load_frag(tb + (nb * 32 + l32) * ROW + ks * 16 + g * 8);
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb, acc[hb]);
-          }
-          // ReLU(.) * w summed over the lane's 16 heads of each block, as four
-          // independent partial sums, then across the two lane halves
-          float v4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v4[i & 3] = fmaf(w[hb][i], fmaxf(acc[hb][i], 0.f), v4[i & 3]);
-          float v = (v4[0] + v4[1]) + (v4[2] + v4[3]);
-          v += __shfl_xor(v, 32, 64);
-          const int e = eb + l32;
-          const uint32_t key = score_key(v);
-          const bool admit = g == 0 && e < n_t && key > theta;
-          const uint64_t bm = __ballot(admit);
-          if (admit) {
-            const int pos = c + __popcll(bm & lt);
-            my_key[pos] = key;
-            my_idx[pos] = e;
-          }
-          c += __popcll(bm);
-          if (c > FT_CAP - 32) {
-            CSA_WAVE_FENCE();
-            theta = wave_compact(my_key, my_idx, my_hist, c, K);
-            c = K;
-          }
-        }
-      }
+  if (ntiles > 0) issue(0, st0);
+  if (ntiles > 1) issue(1, st1);
+
+  // Prune when fewer than `need` + 1 slots are free (each epilogue admits up to 32
+  // keys and may write one spare slot past them).
+  auto make_room = [&](int need) {
+    if (c > CAP - need - 1) {
+      CSA_WAVE_FENCE();
+      const Pruned pr = wave_select<false>(my_key, my_idx, my_hist, c, K, (K + CAP) / 2, kmin,
+                                           wave_max(kmax_l));
+      c = pr.c;
+      theta = pr.theta;
+      kmin = pr.kmin;
     }
-    if (it + 1 < ntiles) commit((it + 1) & 1);
-    __syncthreads();
+  };
+
+  f32x16 accA[HB], accB[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accB[hb][i] = 0.f;
+  // One tile: wait for its stage, refill the stage read two tiles ago, then
+  // MFMA(block 0) | epilogue(block 1 of the previous tile) | MFMA(block 1) |
+  // epilogue(block 0).  Blocks past n_t are multiplied too (their rows are valid
+  // data) and refused by the epilogue's mask; at it == 0 there is no previous block.
+  auto step = [&](int it, const unsigned char* cur, unsigned char* refill) {
+    if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, true>();
+    else wait_vmcnt<0, true>();
+    __builtin_amdgcn_s_barrier();
+    if (it + 2 < ntiles) issue(it + 2, refill);
+    if (select_all) return;
+    make_room(2 * 32);
+    const int e0 = it * FT_TILE;
+    mfma_block(cur, 0, accA);
+    epilogue(accB, e0 - 32);
+    mfma_block(cur, 1, accB);
+    epilogue(accA, e0);
+  };
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, st0, st2);
+    if (it + 1 < ntiles) step(it + 1, st1, st0);
+    if (it + 2 < ntiles) step(it + 2, st2, st1);
+  }
+  if (!select_all && ntiles > 0) {
+    make_room(32);
+    epilogue(accB, ntiles * FT_TILE - 32);
   }
 
   if (!q_ok) return;
@@ -467,7 +558,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     return;
   }
   CSA_WAVE_FENCE();
-  if (c > K) wave_compact(my_key, my_idx, my_hist, c, K);
+  if (c > K) wave_select<true>(my_key, my_idx, my_hist, c, K, K, kmin, wave_max(kmax_l));
   for (int j = lane; j < K; j += 64) out[j] = my_idx[j];
 }
 

@@ -48,8 +48,6 @@ struct MqaArgs {
 // Key slot (within a tile of 32) held at k-slot i of lane group g.
 __device__ __host__ constexpr int slot_key(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
-#define CSA_LDS __attribute__((address_space(3)))
-
 constexpr int MQA_MAX_TOPK = 2048;
 
 template <typename T, int D, int NW>
@@ -245,7 +243,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
       Frag<T> f;
       const CSA_LDS unsigned char* p =
           lb + qk_base[k & 1] + (SWZ ? row16 * 1024 + 64 * k : eoff(row16, 32 * k) - eoff(0, 0));
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
       *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
       if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
       return f;
