@@ -375,43 +375,60 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// bf16 fast path for up to 64 heads: two waves per query, 32 heads per wave on
-// v_mfma_f32_32x32x16_bf16, so every LDS fragment feeds 32 heads and every MFMA does
-// twice the work of the 16x16 shape.  Per wave and 32-key tile:
-//   S^T[32 keys, 32 heads] = sum_k K[:, 16k..16k+15] . Q^T[16k.., heads]   (D/16 MFMAs)
-//     lane (head l%32, g = l/32) receives keys 8j + 4g + i, j, i = 0..3
-//   O^T[32 dims, 32 heads] += V^T[dims, 16 slots] . P^T[16 slots, heads]  (2 per block)
-//     k-step ks takes accumulator rows j = 2ks, 2ks+1: keys 16ks + {4g..4g+3, 8+4g..8+4g+3}
-//     for lane group g; V^T for those keys comes from two transposing LDS reads.
-// The D x 32 fp32 output accumulator (256 registers for D = 512) sits in AGPRs; the
-// wave runs alone on its SIMD and two queries share a CU.
+// bf16 fast path for D = 512 and up to 64 heads: four waves per query, wave w owning
+// head group hg = w/2 (32 heads) and latent half dh = w%2 (dims 256dh .. 256dh+255).
+// Every LDS fragment then feeds 32 heads on v_mfma_f32_32x32x16_bf16, and each wave
+// reads only its half of every key row, so a 32-key tile costs 160 KB of LDS reads and
+// writes per workgroup instead of the 256 KB of the 16-head mapping.  Per tile:
+//   partial S^T[32 keys, 32 heads] over the wave's 256 dims      (16 MFMAs)
+//     lane (head l%32, g = l/32) holds keys 8j + 4g + i, j, i = 0..3
+//   exchange partials with the partner wave (same heads, other half) through LDS;
+//   both add own + partner's (fp32 addition commutes, so both get identical logits)
+//   softmax against a fixed reference, P^T to bf16 in registers
+//   O^T[256 dims, 32 heads] += V^T . P^T                          (16 MFMAs)
+//     k-step ks takes accumulator rows j = 2ks, 2ks+1: keys 16ks + {4g..4g+3,
+//     8+4g..8+4g+3}; V^T for those keys comes from two transposing LDS reads.
+// LDS is exactly two 32 KB key stages plus the 16 KB exchange buffer (two workgroups
+// per CU); the RoPE table and the overflow flag borrow the exchange buffer outside the
+// key loop, and the key indices are read from global memory one tile ahead.
 // ---------------------------------------------------------------------------------
-__device__ inline f32x16 mfma32(const Frag<bf16>& a, const Frag<bf16>& b, f32x16 c) {
-  bf16x8 av, bv;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { av[i] = a.v[i]; bv[i] = b.v[i]; }
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+// Combine lane l with lane l ^ 32 (v_permlane32_swap: no LDS traffic, no address
+// register).  The swap yields both halves' values in every lane, in the same order in
+// both halves, so the two halves get bit-identical results.
+__device__ inline uint2 swap_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_uint2(r[0], r[1]);
+}
+__device__ inline float halves_max(float x) {
+  const uint2 r = swap_halves(x);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ inline float halves_sum(float x) {
+  const uint2 r = swap_halves(x);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void sparse_mqa32_kernel(MqaArgs a) {
-  typedef bf16 T;
-  constexpr int NW = 2, NT = 128, HP = 64, ES = 2, KT = 32;
-  constexpr int ROWB = D * ES;
-  constexpr int NCH = ROWB / 16;
-  constexpr int RPL = ROWB < 1024 ? 1024 / ROWB : 1;
-  constexpr int NL = KT / RPL;
-  constexpr int LSTRIDE = 1024 + 48;
-  constexpr int QROWB = ROWB + 16;
-  constexpr int TILEB = NL * LSTRIDE;
-  constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
-  static_assert(ROWB <= 1024, "rows of at most 1 KB");
-  __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
-  __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
-  __shared__ uint32_t km0, km1;  // per-tile key validity bits
-  __shared__ int sidx[MQA_MAX_TOPK];
-  __shared__ float2 cs[64];
+// Workgroup barrier ordering LDS only: outstanding global loads (the next tile's
+// direct-to-LDS copies) stay in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
+__global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
+  typedef bf16 T;
+  constexpr int D = 512, ROWB = 1024, KT = 32, NT = 256;
+  // 16-byte chunk c of row r sits at chunk position c ^ swz(r) (see sparse_mqa_kernel)
+  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
+  auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
+  __shared__ __attribute__((aligned(16))) f32x4 xb[4][4][64];
+  float2* cs = reinterpret_cast<float2*>(&xb[0][0][0]);  // RoPE table outside the loop
+  int* ovf = reinterpret_cast<int*>(&xb[0][0][0]);       // overflow flag outside the loop
+
+  // workgroup -> query: as sparse_mqa_kernel (32 consecutive queries per XCD visit)
   const int total = a.B * a.S;
   int gi = blockIdx.x;
   const int nfull = total & ~255;
@@ -424,7 +441,8 @@ __global__ __launch_bounds__(128) void sparse_mqa32_kernel(MqaArgs a) {
   const int t = gi % a.S;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave >> 1, dh = wave & 1;
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int n_t = a.mode == MQA_WINDOW_ONLY ? 0 : visible_entries(t, a.ratio);
@@ -435,215 +453,220 @@ __global__ __launch_bounds__(128) void sparse_mqa32_kernel(MqaArgs a) {
   const int64_t P = a.pos0 + t;
   const int rlo = D - a.R;
 
-  if (threadIdx.x < a.R / 2) {
-    float c, s;
-    rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
-    cs[threadIdx.x] = make_float2(c, s);
-  }
-  if (a.mode == MQA_SELECTED) {
-    const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
-    for (int i = threadIdx.x; i < nsel; i += NT) sidx[i] = irow[i];
-  }
+  auto rope_table = [&]() {
+    if (threadIdx.x < a.R / 2) {
+      float c, s;
+      rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
+      cs[threadIdx.x] = make_float2(c, s);
+    }
+  };
+  rope_table();
 
-  // q[b,t] -> LDS (heads 0..31 in st0, 32..63 in st1), coalesced
+  // q[b,t] -> LDS rows (heads 0..31 in st0, 32..63 in st1), swizzled, coalesced
   const unsigned char* qg =
       reinterpret_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
-  for (int c = threadIdx.x; c < HP * NCH; c += NT) {
-    const int row = c / NCH, col = (c % NCH) * 16;
+  for (int c = threadIdx.x; c < 64 * (ROWB / 16); c += NT) {
+    const int row = c >> 6, col = (c & 63) * 16;
     const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(qg + (int64_t)row * ROWB + col)
                               : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>((row < 32 ? st0 : st1) + (row % 32) * QROWB + col) = v;
+    *reinterpret_cast<uint4*>((row < 32 ? st0 : st1) + off(row & 31, col)) = v;
   }
   __syncthreads();
 
-  // Q^T fragments: lane (head 32w + l32, g), k-step k: dims 16k + 8g .. +7, rotated
-  Frag<T> qf[D / 16];
+  // Q^T fragments: lane (head 32hg + l32, g), k-step k: dims 256dh + 16k + 8g .. +7,
+  // rotated at +P where they fall in the last R dims
+  // (bf16x8 vectors: packed two per register; an array of scalar bf16 would take one
+  // register per element)
+  bf16x8 qf[16];
   {
-    const unsigned char* qrow = (wave == 0 ? st0 : st1) + l32 * QROWB;
+    const unsigned char* qs = hg == 0 ? st0 : st1;
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const int d0 = 16 * k + 8 * g;
-      qf[k] = load_frag(reinterpret_cast<const T*>(qrow) + d0);
+    for (int k = 0; k < 16; ++k) {
+      const int d0 = 256 * dh + 16 * k + 8 * g;
+      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + off(l32, 2 * d0)));
       if (d0 + 8 > rlo) {
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           const int d = d0 + i;
           if (d >= rlo) {
             const float2 r = cs[(d - rlo) >> 1];
-            const float x0 = to_f32(qf[k].v[i]), x1 = to_f32(qf[k].v[i + 1]);
-            qf[k].v[i] = from_f32<T>(x0 * r.x - x1 * r.y);
-            qf[k].v[i + 1] = from_f32<T>(x0 * r.y + x1 * r.x);
+            const float x0 = (float)qf[k][i], x1 = (float)qf[k][i + 1];
+            qf[k][i] = (bf16)(x0 * r.x - x1 * r.y);
+            qf[k][i + 1] = (bf16)(x0 * r.y + x1 * r.x);
           }
         }
       }
     }
   }
-  // Register classes: the D x 32 accumulator in AGPRs, the q fragments in VGPRs (empty
-  // asm statements that only constrain allocation).
-#pragma unroll
-  for (int k = 0; k < D / 16; ++k) {
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = qf[k].v[i];
-    asm volatile("" : "+v"(v));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qf[k].v[i] = v[i];
-  }
-  __syncthreads();
+  __syncthreads();  // q staging and the RoPE table are no longer read
 
+  // Key sources, one tile ahead: lane l < 32 resolves key tile*32 + l.
   const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
   const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
-  auto eoff = [](int r, int d) -> int {
-    return (r / RPL) * LSTRIDE + (r % RPL) * ROWB + d * ES;
+  const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+  // Every lane loads (from a clamped position, so the load is not predicated) and the
+  // value is only inspected at the next tile's issue: using it earlier would make the
+  // wave wait for the direct-to-LDS copies issued before it.
+  const bool gather = a.mode == MQA_SELECTED && nsel > 0;
+  auto load_idx = [&](int tile) -> int {
+    return gather ? irow[min(tile * KT + l32, nsel - 1)] : 0;
   };
-  auto key_src = [&](int kk, int* ok) -> const unsigned char* {
+  const int dma_off0 = (lane ^ (2 * (wave & 3))) << 4, dma_off1 = (lane ^ (2 * (wave & 3) + 1)) << 4;
+  // Direct-to-LDS copy of tile `tile` (index values `sv` from load_idx): wave w loads
+  // rows w, w+4, ..., one 1 KB wave load per row; returns the tile's key-validity bits.
+  auto issue = [&](int tile, int sv, unsigned char* sb) -> uint32_t {
+    const int kk = tile * KT + l32;
+    const unsigned char* src = qg;  // masked keys read finite data that is never used
+    bool ok = false;
     if (kk < nsel) {
-      const int s = a.mode == MQA_SELECTED ? sidx[kk] : kk;
-      if (s >= 0 && s < n_t) {
-        *ok = 1;
-        return kv_c + ((int64_t)b * a.n_entries + s) * ROWB;
+      if (!gather) sv = kk;
+      if (sv >= 0 && sv < n_t) {
+        ok = true;
+        src = kv_c + ((int64_t)b * a.n_entries + sv) * ROWB;
       }
     } else if (kk < nk) {
-      *ok = 1;
-      return kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
+      ok = true;
+      src = kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
     }
-    *ok = 0;
-    return qg;
-  };
-  // wave w loads lines w, w+2, ...; the validity of the tile's 32 keys is gathered
-  // into one mask word (the lane loading byte 0 of a row sets its bit)
-  auto issue = [&](int tile, unsigned char* sb, uint32_t* km) {
-    uint32_t bits = 0;
-#pragma unroll 1
-    for (int L = wave; L < NL; L += NW) {
-      int r, byte;
-      if constexpr (RPL > 1) {
-        r = L * RPL + lane / NCH;
-        byte = (lane % NCH) * 16;
-      } else {
-        r = L;
-        byte = lane * 16;
-      }
-      int ok;
-      const unsigned char* src = key_src(tile * KT + r, &ok);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
-                                       (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
-      if (byte == 0 && ok) bits |= 1u << r;
+    const uint32_t bits = (uint32_t)__ballot(ok && lane < 32);
+    const uint64_t sp = reinterpret_cast<uint64_t>(src);
+    const uint32_t sp_lo = (uint32_t)sp, sp_hi = (uint32_t)(sp >> 32);
+#pragma unroll
+    for (int m = 0; m < KT / 4; ++m) {
+      const int r = wave + 4 * m;  // swz(r) = 2 wave | (m & 1)
+      const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
+      const unsigned char* gp = reinterpret_cast<const unsigned char*>(row) + (m & 1 ? dma_off1 : dma_off0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp),
+                                       (CSA_LDS void*)(sb + r * ROWB), 16, 0, 0);
     }
-    // OR the bits of both waves: wave 0 stores, wave 1 adds after the barrier-free
-    // atomic (LDS atomics order within the workgroup)
-    for (int m = 32; m >= 1; m >>= 1) bits |= (uint32_t)__shfl_xor((int)bits, m, 64);
-    if (lane == 0) atomicOr(km, bits);
+    return bits;
   };
 
-  // Softmax with a fixed reference (shift invariance): the first tile's max per head.
-  // No accumulator rescale inside the loop.  If a later tile's max exceeds the
-  // reference by more than 2^64 (not reachable with RMS-normalised inputs, possible
-  // in general), the workgroup runs the tiles again with the largest max seen as the
-  // reference, so every exp2 argument is <= 0 and nothing can overflow.
-  __shared__ int overflow;
+  // Per-lane LDS offsets.  QK: row l32, chunk 32dh + 2k + g at position
+  // 32dh + 8(k>>2) + ((2(k&3) + g) ^ swz(l32)): four bases, 128(k>>2) an immediate.
+  int qk_base[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qk_base[m] = l32 * ROWB + ((32 * dh + ((2 * m + g) ^ swz(l32))) << 4);
+  // PV: 16-lane group h = lane/16 covers dims 256dh + 32db + 16(h&1) .. +15; lane j of
+  // the group addresses key row 16ks + 4g + j/4 (and +8), dims + 4(j%4).  With
+  // a4 = j/4 the row's swizzle is 2a4 | g for every ks and for the +8 row, and the
+  // chunk position is 32dh + 8(db>>1) + 2((2(db&1) + hh) ^ a4) + (((j>>1)&1) ^ g):
+  // two bases (db even / odd); 128(db>>1), 16 KB ks and 8 KB for the +8 row are
+  // immediates.
+  const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
+  int pv_base[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    pv_base[m] = (4 * g + a4) * ROWB +
+                 ((32 * dh + 2 * ((2 * m + hh) ^ a4) + (((hj >> 1) & 1) ^ g)) << 4) + 8 * (hj & 1);
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+  // Softmax with a fixed reference (shift invariance), as in sparse_mqa_kernel.
   float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
-  f32x16 O[D / 32];
+  f32x16 O[8];
 
   auto compute = [&](const unsigned char* sb, uint32_t kmask) {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
     f32x16 s = {};
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const Frag<T> ka = load_frag(reinterpret_cast<const T*>(sb + eoff(l32, 16 * k + 8 * g)));
-      s = mfma32(ka, qf[k], s);
+    for (int k = 0; k < 16; ++k) {
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+      if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    // lane (head l32, g): element 4j+i is key 8j + 4g + i
+    // exchange partial logits with the partner wave
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xb[wave][q][lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+    lds_barrier();
     float z[16];
     float mt = -INFINITY;
+    const uint32_t kml = kmask >> (4 * g);  // bit 8q + i: key 8q + 4g + i (constant shifts)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 o4 = xb[wave ^ 1][q][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 8 * j + 4 * g + i;
-        const float v = ((kmask >> key) & 1u) ? s[4 * j + i] * a.scale_log2 : -INFINITY;
-        z[4 * j + i] = v;
+        const int e = 4 * q + i;
+        const float v = ((kml >> (8 * q + i)) & 1u) ? (s[e] + o4[i]) * a.scale_log2 : -INFINITY;
+        z[e] = v;
         mt = fmaxf(mt, v);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    }
+    mt = halves_max(mt);
     m_seen = fmaxf(m_seen, mt);
     if (m_ref == -INFINITY) m_ref = mt;  // O and l are still zero
     const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
-    Frag<T> pf[2];
+    bf16x8 pf[2];
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(z[e] - mref);
       ls += p;
-      pf[e >> 3].v[e & 7] = from_f32<T>(p);
+      pf[e >> 3][e & 7] = (bf16)p;
     }
     l_run += ls;
-    // V^T fragments: 16-lane group h = lane/16 covers dims 32db + 16(h&1) + 0..15;
-    // lane j of the group addresses key row base + j/4, dims + 4(j%4)
-    const int hj = lane & 15, hh = (lane >> 4) & 1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        typedef short i16x4 __attribute__((ext_vector_type(4)));
-        const int kr = 16 * ks + 4 * g + (hj >> 2);
-        const int dc = 32 * db + 16 * hh + 4 * (hj & 3);
-        Frag<T> av;
-        *reinterpret_cast<i16x4*>(av.v) =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(sb + eoff(kr, dc)));
-        *reinterpret_cast<i16x4*>(av.v + 4) =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(sb + eoff(kr + 8, dc)));
-        O[db] = mfma32(av, pf[ks], O[db]);
+        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + 16 * ROWB * ks;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], O[db], 0, 0, 0);
       }
-      asm volatile("" : "+a"(O[db]));
+      // keep the transposing reads at most one block ahead of their MFMAs
+      if (db & 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int ntiles = (nk + KT - 1) / KT;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-    {
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
-      asm volatile("" : "+a"(O[db]));
-    }
     l_run = 0.f;
-    if (threadIdx.x == 0) { km0 = 0u; km1 = 0u; overflow = 0; }
-    __syncthreads();
-    if (ntiles > 0) issue(0, st0, &km0);
+    uint32_t km0 = 0u, km1 = 0u;
+    int sv = 0;
+    if (ntiles > 0) km0 = issue(0, load_idx(0), st0);
+    if (ntiles > 1) sv = load_idx(1);
     __syncthreads();
     for (int tile = 0; tile < ntiles; tile += 2) {
-      if (tile + 1 < ntiles) issue(tile + 1, st1, &km1);
+      if (tile + 1 < ntiles) km1 = issue(tile + 1, sv, st1);
+      if (tile + 2 < ntiles) sv = load_idx(tile + 2);
       compute(st0, km0);
-      __syncthreads();
-      if (threadIdx.x == 0) km0 = 0u;
+      __syncthreads();  // tile+1 landed in st1; every wave is done with st0 and xb
       if (tile + 1 < ntiles) {
-        if (tile + 2 < ntiles) {
-          __syncthreads();  // km0 cleared before it is OR-ed again
-          issue(tile + 2, st0, &km0);
-        }
+        if (tile + 2 < ntiles) km0 = issue(tile + 2, sv, st0);
+        if (tile + 3 < ntiles) sv = load_idx(tile + 3);
         compute(st1, km1);
         __syncthreads();
-        if (threadIdx.x == 0) km1 = 0u;
       }
     }
-    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(&overflow, 1);
+    if (threadIdx.x == 0) *ovf = 0;
     __syncthreads();
-    if (!overflow) break;
+    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(ovf, 1);
+    __syncthreads();
+    const int again = *ovf;
+    __syncthreads();
+    if (!again) break;
     m_ref = m_seen;  // exact reference for the second pass
   }
 
-  // normalise, de-rotate, stage by head rows, write o[b,t] coalesced
-  l_run += __shfl_xor(l_run, 32, 64);
+  // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced
+  rope_table();
+  l_run = halves_sum(l_run);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   __syncthreads();
   {
-    unsigned char* orow = (wave == 0 ? st0 : st1) + l32 * QROWB;
+    unsigned char* os = hg == 0 ? st0 : st1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * db + 8 * j + 4 * g;
+        const int d0 = 256 * dh + 32 * db + 8 * j + 4 * g;
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = O[db][4 * j + i] * inv;
@@ -656,23 +679,30 @@ __global__ __launch_bounds__(128) void sparse_mqa32_kernel(MqaArgs a) {
             x[i + 1] = -x0 * r.y + x1 * r.x;
           }
         }
-        T* dst = reinterpret_cast<T*>(orow) + d0;
+        T y[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(x[i]);
+        for (int i = 0; i < 4; ++i) y[i] = from_f32<T>(x[i]);
+        *reinterpret_cast<uint2*>(os + off(l32, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
       }
   }
   __syncthreads();
   unsigned char* og = reinterpret_cast<unsigned char*>(a.o) + ((int64_t)b * a.S + t) * a.H * ROWB;
-  for (int c = threadIdx.x; c < a.H * NCH; c += NT) {
-    const int row = c / NCH, col = (c % NCH) * 16;
-    const unsigned char* src = (row < 32 ? st0 : st1) + (row % 32) * QROWB + col;
-    *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) = *reinterpret_cast<const uint4*>(src);
+  for (int c = threadIdx.x; c < a.H * (ROWB / 16); c += NT) {
+    const int row = c >> 6, col = (c & 63) * 16;
+    *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) =
+        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + off(row & 31, col));
   }
 }
 
 template <typename T, int D>
 static void launch_d(const MqaArgs& a, int H, hipStream_t st) {
   dim3 grid(a.B * a.S);
+  if constexpr (D == 512 && sizeof(T) == 2) {
+    if (H > 16) {
+      hipLaunchKernelGGL(sparse_mqa_hd_kernel, grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
   if (H <= 16) hipLaunchKernelGGL((sparse_mqa_kernel<T, D, 1>), grid, dim3(64), 0, st, a);
   else hipLaunchKernelGGL((sparse_mqa_kernel<T, D, 4>), grid, dim3(256), 0, st, a);
 }
