@@ -219,6 +219,7 @@ template <typename T, int DI> struct FtShape {
   static constexpr int CAP = CAP_FIT < 2048 ? CAP_FIT : 2048;  // candidates per query
   static_assert(STAGE % 1024 == 0, "a stage is whole 1 KB DMA lines");
   static_assert(CAP >= FT_MAXK + 2 * FT_TILE + 2, "candidate buffer too small");
+  static_assert(CAP % 4 == 0, "16-byte candidate accesses");
 };
 
 struct IndexTopkArgs {
@@ -268,10 +269,18 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier that orders LDS accesses only: direct-to-LDS copies still in flight
+// (counted by vmcnt) are waited for separately by wait_vmcnt.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 struct Pruned {
-  int c;           // keys kept
-  uint32_t theta;  // admit later keys strictly above this
-  uint32_t kmin;   // lower bound of every kept key (and of later admissions)
+  int c;              // keys kept
+  uint32_t theta;     // admit later keys strictly above this
+  uint32_t kept_min;  // smallest kept key
 };
 
 // Shrink the candidates ckey/cidx[0..c) of one wave, in place and in buffer order.
@@ -279,24 +288,38 @@ struct Pruned {
 // the prefix of the k-th largest key.  EXACT keeps exactly the top K by (key desc,
 // buffer position asc); otherwise the wave may stop as soon as the keys at or above
 // the current prefix number at most `target` (>= K), and keeps all of them.
+// Lane l handles buffer positions 4(l + 64j) .. +3 (one 16-byte LDS access each for
+// keys and indices, made only when the first of them is below c; the buffers are
+// 16-byte aligned and their capacity is a multiple of 4, so such an access stays in
+// the buffer).  Positions >= c are ignored.
 template <bool EXACT>
 __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K, int target,
                               uint32_t kmin, uint32_t kmax) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const uint32_t diff = kmin ^ kmax;
-  int shift = diff ? 32 - __clz(diff) : 0;
-  uint64_t prefix = (uint64_t)kmin >> shift;
-  int rem = K;           // slots left among keys whose bits above `shift` equal prefix
-  bool keep_eq = false;  // keep every key equal to the prefix (no tie cut needed)
+  int shift = diff ? 32 - __clz(diff) : 0;  // bits below `shift` are still undecided
+  // the decided bits: key & hmask == pbits (hmask = 0 while shift == 32)
+  uint32_t hmask = shift >= 32 ? 0u : (~0u << shift);
+  uint32_t pbits = kmin & hmask;
+  int rem = K;           // slots left among keys matching the decided bits
+  bool keep_eq = false;  // keep every matching key (no tie cut needed)
+  const int nb = (c + 255) >> 8;  // 256-key batches
   while (shift > 0) {
     const int w = shift >= 8 ? 8 : shift;
     const int lo = shift - w;
+    const uint32_t dmask = (1u << w) - 1u;
     *reinterpret_cast<int4*>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
     CSA_WAVE_FENCE();
-    for (int i = lane; i < c; i += 64) {
-      const uint32_t k = ckey[i];
-      if (((uint64_t)k >> shift) == prefix) atomicAdd(&hist[(k >> lo) & ((1u << w) - 1u)], 1);
+    for (int jb = 0; jb < nb; ++jb) {
+      const int base = 4 * (lane + 64 * jb);
+      const uint4 k4 = base < c ? *reinterpret_cast<const uint4*>(&ckey[base]) : make_uint4(0, 0, 0, 0);
+      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool m = base + u < c && (kk[u] & hmask) == pbits;
+        atomicAdd(&hist[(kk[u] >> lo) & dmask], m ? 1 : 0);
+      }
     }
     CSA_WAVE_FENCE();
     // lane l holds digits 255-4l .. 252-4l (top digits first)
@@ -320,7 +343,9 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
     sel_above = __shfl(sel_above, src, 64);
     sel_cnt = __shfl(sel_cnt, src, 64);
     rem -= sel_above;
-    prefix = (prefix << w) | (uint64_t)sel;
+    pbits |= (uint32_t)sel << lo;
+    hmask = ~0u << lo;
+    if (lo == 0) hmask = ~0u;
     shift = lo;
     CSA_WAVE_FENCE();
     if (sel_cnt == rem || (!EXACT && K - rem + sel_cnt <= target)) {
@@ -328,43 +353,69 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
       break;
     }
   }
-  // stable in-place compaction; track the bounds of what is kept
+  if (shift == 0) hmask = ~0u;
+  // stable in-place compaction; track the smallest kept key
   int out = 0, eq_seen = 0;
   uint32_t nmin = 0xffffffffu;
-  for (int base = 0; base < c; base += 64) {
-    const int i = base + lane;
-    uint32_t k = 0;
-    int id = 0;
-    if (i < c) {
-      k = ckey[i];
-      id = cidx[i];
+  for (int jb = 0; jb < nb; ++jb) {
+    const int base = 4 * (lane + 64 * jb);
+    uint4 k4 = make_uint4(0, 0, 0, 0);
+    int4 i4 = make_int4(0, 0, 0, 0);
+    if (base < c) {
+      k4 = *reinterpret_cast<const uint4*>(&ckey[base]);
+      i4 = *reinterpret_cast<const int4*>(&cidx[base]);
     }
-    const uint64_t kp = (uint64_t)k >> shift;
-    const bool gt = i < c && kp > prefix;
-    const bool eq = i < c && kp == prefix;
-    const uint64_t be = __ballot(eq);
-    const bool keep = gt || (eq && (keep_eq || eq_seen + __popcll(be & lt) < rem));
-    const uint64_t bk = __ballot(keep);
-    CSA_WAVE_FENCE();  // all reads of this chunk precede the writes below
-    if (keep) {
-      const int pos = out + __popcll(bk & lt);
-      ckey[pos] = k;
-      cidx[pos] = id;
-      nmin = min(nmin, k);
+    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+    const int ii[4] = {i4.x, i4.y, i4.z, i4.w};
+    bool gt[4], eq[4];
+    uint64_t be[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = base + u < c;
+      const uint32_t hk = kk[u] & hmask;
+      gt[u] = valid && hk > pbits;
+      eq[u] = valid && hk == pbits;
+      be[u] = __ballot(eq[u]);
     }
-    out += __popcll(bk);
-    eq_seen += __popcll(be);
+    // rank among equal keys in buffer order: lanes below, then this lane's earlier slots
+    int eq_rank = eq_seen;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) eq_rank += __popcll(be[u] & lt);
+    bool keep[4];
+    uint64_t bk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      keep[u] = gt[u] || (eq[u] && (keep_eq || eq_rank < rem));
+      eq_rank += eq[u] ? 1 : 0;
+      bk[u] = __ballot(keep[u]);
+    }
+    int pos = out;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pos += __popcll(bk[u] & lt);
+    CSA_WAVE_FENCE();  // all reads of this batch precede the writes below
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (keep[u]) {
+        ckey[pos] = kk[u];
+        cidx[pos] = ii[u];
+        nmin = min(nmin, kk[u]);
+        ++pos;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      out += __popcll(bk[u]);
+      eq_seen += __popcll(be[u]);
+    }
     CSA_WAVE_FENCE();
   }
   Pruned r;
   r.c = out;
-  const uint32_t T = (uint32_t)(prefix << shift);
-  // keep_eq: every kept key is >= T and at least K of them are kept, so a later key
-  // below T is beaten K times.  Otherwise the kept set is exactly the top K and a
+  // keep_eq: every kept key is >= pbits and at least K of them are kept, so a later key
+  // below pbits is beaten K times.  Otherwise the kept set is exactly the top K and a
   // later key equal to the smallest kept one loses on index.
-  const uint32_t kept_min = wave_min(nmin);
-  r.theta = (keep_eq && out > K) ? (T ? T - 1u : 0u) : kept_min;
-  r.kmin = min(kept_min, r.theta + 1u);  // later admissions are above theta
+  r.kept_min = wave_min(nmin);
+  r.theta = (keep_eq && out > K) ? (pbits ? pbits - 1u : 0u) : r.kept_min;
   return r;
 }
 
@@ -379,9 +430,10 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   __shared__ __attribute__((aligned(1024))) unsigned char st0[SH::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[SH::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char st2[SH::STAGE];
-  __shared__ uint32_t ckey[FT_WAVES][CAP];
-  __shared__ int cidx[FT_WAVES][CAP];
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[FT_WAVES][CAP];
+  __shared__ __attribute__((aligned(16))) int cidx[FT_WAVES][CAP];
   __shared__ __attribute__((aligned(16))) int hist[FT_WAVES][256];
+  __shared__ __attribute__((aligned(16))) int vote[FT_WAVES];  // last tile a wave asked for a prune
 
   // latest (heaviest) query blocks first
   const int id = a.B * a.qblocks - 1 - (int)blockIdx.x;
@@ -457,16 +509,22 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     if constexpr (sizeof(T) == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
     return f;
   };
+  // The fragment reads run two k-steps ahead of the MFMAs that consume them, so the
+  // LDS latency hides behind the matrix work of the same wave.
+  constexpr int LA = KS < 3 ? KS : 3;
   auto mfma_block = [&](const unsigned char* st, int nb, f32x16* acc) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+    Frag<T> kb[LA];
+#pragma unroll
+    for (int ks = 0; ks < LA - 1; ++ks) kb[ks] = frag(st, nb, ks);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const Frag<T> kb = frag(st, nb, ks);
+      if (ks + LA - 1 < KS) kb[(ks + LA - 1) % LA] = frag(st, nb, ks + LA - 1);
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb, acc[hb]);
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb[ks % LA], acc[hb]);
     }
   };
 
@@ -474,7 +532,10 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   int* my_idx = cidx[wave];
   int* my_hist = hist[wave];
   uint32_t theta = 0u;                      // admit keys strictly above
-  uint32_t kmin = 1u, kmax_l = 0u;          // bounds of buffered keys (kmax per lane)
+  // Bounds of the buffered keys for the radix select: the smallest key kept by the
+  // last prune, and per lane the smallest and largest key admitted since (largest:
+  // ever).  Tight bounds make the first radix digit discriminate.
+  uint32_t kept_lo = 0xffffffffu, kmn_l = 0xffffffffu, kmax_l = 0u;
   int c = 0;
 
   // ReLU(.) * w summed over the lane's 16 heads of each block (four independent
@@ -498,6 +559,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     my_key[pos] = key;
     my_idx[pos] = e;
     kmax_l = admit ? max(kmax_l, key) : kmax_l;
+    kmn_l = admit ? min(kmn_l, key) : kmn_l;
     c += __popcll(bm);
   };
 
@@ -506,15 +568,20 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   if (ntiles > 1) issue(1, st1);
 
   // Prune when fewer than `need` + 1 slots are free (each epilogue admits up to 32
-  // keys and may write one spare slot past them).
-  auto make_room = [&](int need) {
-    if (c > CAP - need - 1) {
+  // keys and may write one spare slot past them), or, with `early`, once the buffer
+  // is more than half way from K to full.  A prune stalls the whole workgroup at the
+  // next barrier, so the waves announce an upcoming prune one tile ahead (vote) and
+  // then prune together: the stalls overlap instead of adding up.
+  constexpr int PRUNE_EARLY = (FT_MAXK + CAP) / 2;
+  auto make_room = [&](int need, bool early) {
+    if (c > CAP - need - 1 || (early && c > max(K, PRUNE_EARLY))) {
       CSA_WAVE_FENCE();
-      const Pruned pr = wave_select<false>(my_key, my_idx, my_hist, c, K, (K + CAP) / 2, kmin,
-                                           wave_max(kmax_l));
+      const Pruned pr = wave_select<false>(my_key, my_idx, my_hist, c, K, (K + CAP) / 2,
+                                           min(kept_lo, wave_min(kmn_l)), wave_max(kmax_l));
       c = pr.c;
       theta = pr.theta;
-      kmin = pr.kmin;
+      kept_lo = pr.kept_min;
+      kmn_l = 0xffffffffu;
     }
   };
 
@@ -527,18 +594,27 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   // MFMA(block 0) | epilogue(block 1 of the previous tile) | MFMA(block 1) |
   // epilogue(block 0).  Blocks past n_t are multiplied too (their rows are valid
   // data) and refused by the epilogue's mask; at it == 0 there is no previous block.
+  if (lane == 0) vote[wave] = -2;
   auto step = [&](int it, const unsigned char* cur, unsigned char* refill) {
-    if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, true>();
-    else wait_vmcnt<0, true>();
-    __builtin_amdgcn_s_barrier();
+    if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, false>();
+    else wait_vmcnt<0, false>();
+    lds_barrier();
+    if (!select_all) {  // prune before the refill is issued: the prune's LDS atomics wait
+                        // for every copy in flight, and the older one has likely landed
+      const int4 v0 = *reinterpret_cast<const int4*>(&vote[0]);
+      const int4 v1 = *reinterpret_cast<const int4*>(&vote[4]);
+      const int vmax = max(max(max(v0.x, v0.y), max(v0.z, v0.w)), max(max(v1.x, v1.y), max(v1.z, v1.w)));
+      make_room(2 * 32, vmax >= it - 1);
+    }
     if (it + 2 < ntiles) issue(it + 2, refill);
     if (select_all) return;
-    make_room(2 * 32);
     const int e0 = it * FT_TILE;
     mfma_block(cur, 0, accA);
     epilogue(accB, e0 - 32);
     mfma_block(cur, 1, accB);
     epilogue(accA, e0);
+    // two more tiles could fill the buffer: ask every wave to prune at the next tile
+    if (c > CAP - 3 * FT_TILE - 1 && lane == 0) vote[wave] = it;
   };
   for (int it = 0; it < ntiles; it += 3) {
     step(it, st0, st2);
@@ -546,7 +622,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     if (it + 2 < ntiles) step(it + 2, st2, st1);
   }
   if (!select_all && ntiles > 0) {
-    make_room(32);
+    make_room(32, false);
     epilogue(accB, ntiles * FT_TILE - 32);
   }
 
@@ -558,7 +634,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     return;
   }
   CSA_WAVE_FENCE();
-  if (c > K) wave_select<true>(my_key, my_idx, my_hist, c, K, K, kmin, wave_max(kmax_l));
+  if (c > K) wave_select<true>(my_key, my_idx, my_hist, c, K, K, min(kept_lo, wave_min(kmn_l)), wave_max(kmax_l));
   for (int j = lane; j < K; j += 64) out[j] = my_idx[j];
 }
 
