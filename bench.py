@@ -69,6 +69,92 @@ def roofline_entry(amount, unit, bound, ms):
             "frac": round(achieved / PEAK_HBM_GBS, 4)}
 
 
+# Library kernel -> (rocprofv3 kernel-name fragment, source files it is built from).
+KERNEL_SOURCES = {
+    "compress": ("compress_kernel", ["compress.hip"]),
+    "window_rope": ("window_rope_kernel", ["compress.hip"]),
+    "indexer": ("index_scores_kernel", ["indexer.hip"]),
+    "index_topk": ("index_topk_kernel", ["indexer.hip"]),
+    "topk": ("topk_kernel", ["topk.hip"]),
+    "attention": ("sparse_mqa", ["sparse_mqa.hip"]),
+}
+COMMON_SOURCES = ["common.hpp", "launch.hpp"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_sha(kernel: str) -> str:
+    """sha256 over the sources a library kernel is compiled from: counters taken on
+    another version of the kernel are not reported for this one."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "compressed_sparse_attention_hca_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel][1] + COMMON_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(d: str):
+    """(kernel name, counter name, value) from every rocprofv3 counter CSV under d."""
+    import csv
+    import glob
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                yield r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id", "")
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mb: int, workload: str) -> dict:
+    """Per-launch HBM bytes of each library kernel from one FETCH_SIZE run and one
+    WRITE_SIZE run of this script under rocprofv3 (counters in KiB per dispatch).  Each
+    counter is scaled by what it reads for the plain copy kernel of `copy_mb` MiB that
+    the run performs first (--calib-copy-mb): factor = copied bytes / counter bytes."""
+    out = {"workload": workload, "copy_bytes": copy_mb << 20, "kernels": {}}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = {}
+        copies = []
+        for name, cname, val, _ in _counter_rows(d):
+            if cname != counter:
+                continue
+            if COPY_KERNEL in name:
+                copies.append(val)
+                continue
+            # longest fragment first: "topk_kernel" is also part of "index_topk_kernel"
+            for k, (frag, _) in sorted(KERNEL_SOURCES.items(), key=lambda kv: -len(kv[1][0])):
+                if "csa" in name and frag in name:
+                    per.setdefault(k, []).append(val)
+                    break
+        if not copies:
+            raise SystemExit(f"no {COPY_KERNEL} dispatch under {d}: run with --calib-copy-mb")
+        # the calibration copies are the largest copy dispatches of the run
+        ref = max(copies)
+        factor = (copy_mb << 20) / (ref * 1024.0)
+        out[counter.lower() + "_factor"] = round(factor, 4)
+        for k, vals in per.items():
+            e = out["kernels"].setdefault(k, {})
+            e[counter.lower() + "_kib_per_launch"] = sum(vals) / len(vals)
+            e["launches"] = len(vals)
+    for k, e in out["kernels"].items():
+        if "fetch_size_kib_per_launch" in e and "write_size_kib_per_launch" in e:
+            e["bytes_per_launch"] = round(1024.0 * (e["fetch_size_kib_per_launch"] * out["fetch_size_factor"]
+                                                    + e["write_size_kib_per_launch"] * out["write_size_factor"]))
+        e["source_sha"] = kernel_source_sha(k)
+    return out
+
+
+def traffic_for(kernel: str, path: str):
+    """Counter-derived HBM bytes per launch of `kernel`, or None when there are none or
+    they were taken on a different version of the kernel's sources."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tj = json.load(fh)
+    e = tj.get("kernels", {}).get(kernel)
+    if not e or "bytes_per_launch" not in e or e.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    return e["bytes_per_launch"]
+
+
 class RowStore:
     """Host float64 rows of a [B,S,...] device tensor for the sampled (b, t) only."""
 
@@ -113,12 +199,13 @@ def cpu_baseline(cfg, inp, budget_s: float):
                       cfg.kind == "csa", cfg.rope_dim, cfg.rope_theta, cfg.rms_eps, cfg.pos0)
     t_comp = time.perf_counter() - t_start
 
-    # rows: a seeded random order of 512 evenly spaced rows, so every prefix is spread
-    # over the sequence; rows are added 8 at a time until the budget is used
-    order = np.random.default_rng(0).permutation(np.linspace(0, S - 1, 512).astype(int))
+    # rows: a seeded random order of up to 16384 evenly spaced rows, so every prefix is
+    # spread over the sequence; rows are added 32 at a time until the budget is used
+    n_cand = min(S, 16384)
+    order = np.random.default_rng(0).permutation(np.linspace(0, S - 1, n_cand).astype(int))
     sample, t_rows = [], 0.0
-    for i in range(0, len(order), 8):
-        rows = [(0, int(t)) for t in order[i:i + 8]]
+    for i in range(0, len(order), 32):
+        rows = [(0, int(t)) for t in order[i:i + 32]]
         store = {"q": RowStore(inp["q"], rows), "kv_raw": B0(host["kv_raw"])}
         if cfg.kind == "csa":
             store.update({"q_idx": RowStore(inp["q_idx"], rows), "w_idx": RowStore(inp["w_idx"], rows),
@@ -147,11 +234,24 @@ def main():
     ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3"])
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None, help="JSON file with per-kernel HBM bytes from rocprofv3 counters")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON of per-kernel HBM bytes from rocprofv3 counters (default: "
+                         "profiles/traffic_<workload>.json)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic JSON from a FETCH_SIZE run and a WRITE_SIZE run of "
+                         "this script under rocprofv3 --pmc, then exit (no GPU use)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB twice (a plain copy "
                          "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if args.summarize_counters:
+        s = summarize_counters(*args.summarize_counters, args.calib_copy_mb or 1024, args.workload)
+        with open(traffic_path, "w") as fh:
+            json.dump(s, fh, indent=1)
+        print(json.dumps(s))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -210,10 +310,7 @@ def main():
                   "avg_launch_ms": round(v / launches[k], 4)})
         kernels[k] = e
     dom = max(tot, key=tot.get)
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tj = json.load(open(args.traffic))
-        traffic = tj.get(dom)
+    traffic = traffic_for(dom, traffic_path)
     d = kernels[dom]
     amt, unit, bound = work[dom]
     roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],

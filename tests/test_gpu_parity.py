@@ -36,6 +36,10 @@ def gen(cfg):
 
 def run_layer(bd, cfg, inp):
     p = bd.params(cfg)
+    if cfg.kind == "swa":  # window-only layer: the attention entry point without entries
+        o = bd.sparse_mqa_fwd(p, inp["q"], None, inp["kv_raw"])
+        torch.cuda.synchronize()
+        return o, None, None, None
     B, S, n = cfg.B, cfg.S, cfg.S // cfg.ratio
     kv_c = torch.empty((B, n, cfg.D), dtype=inp["q"].dtype, device=DEV)
     idx = torch.empty((B, S, max(cfg.topk, 1)), dtype=torch.int32, device=DEV) if cfg.kind == "csa" else None
@@ -190,6 +194,32 @@ def test_layer_parity_C2_sampled(bd):
 
 def test_layer_parity_C3_sampled(bd):
     layer_check(bd, wl.C3, sample_rows(wl.C3, 24))
+
+
+STACK = wl.stack_layers()  # 43 layers, B=4, S=8192: SWA, SWA, then CSA/HCA alternating
+
+
+def stack_rows(cfg, layer, full):
+    """Rows of one stack layer: its group, window and top-k edges plus random rows,
+    spread over the 4 batches (every batch for the representative layers)."""
+    if full:
+        return sample_rows(cfg, 8, seed=layer)
+    S, r, W = cfg.S, cfg.ratio, cfg.window
+    ts = [0, r - 1, r, W - 1, W, 512 * r + 1, S // 2 + 3, S - 1]
+    ts += [int(x) for x in np.random.default_rng(layer).integers(0, S, 4)]
+    ts = sorted({t for t in ts if 0 <= t < S})
+    return [(i % cfg.B, t) for i, t in enumerate(ts)]
+
+
+@pytest.mark.parametrize("layer", range(len(STACK)))
+def test_stack_C4_layer(bd, layer):
+    """Each layer of the 43-layer training-shape stack on its own seeded inputs, through
+    its entry point (window-only attention, csa_fwd or hca_fwd), at the full B=4,
+    S=8192 shape: sampled rows against the oracle (all four batches and the edge rows
+    for layers 0, 2, 3 and 42), and the whole compressed table of every batch."""
+    cfg = STACK[layer]
+    layer_check(bd, cfg, stack_rows(cfg, layer, layer in (0, 2, 3, 42)))
+    torch.cuda.empty_cache()
 
 
 def test_window_only_parity(bd):
