@@ -462,43 +462,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   };
   rope_table();
 
-  // q[b,t] -> LDS rows (heads 0..31 in st0, 32..63 in st1), swizzled, coalesced
   const unsigned char* qg =
       reinterpret_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
-  for (int c = threadIdx.x; c < 64 * (ROWB / 16); c += NT) {
-    const int row = c >> 6, col = (c & 63) * 16;
-    const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(qg + (int64_t)row * ROWB + col)
-                              : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>((row < 32 ? st0 : st1) + off(row & 31, col)) = v;
-  }
-  __syncthreads();
-
-  // Q^T fragments: lane (head 32hg + l32, g), k-step k: dims 256dh + 16k + 8g .. +7,
-  // rotated at +P where they fall in the last R dims
-  // (bf16x8 vectors: packed two per register; an array of scalar bf16 would take one
-  // register per element)
-  bf16x8 qf[16];
-  {
-    const unsigned char* qs = hg == 0 ? st0 : st1;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int d0 = 256 * dh + 16 * k + 8 * g;
-      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qs + off(l32, 2 * d0)));
-      if (d0 + 8 > rlo) {
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const int d = d0 + i;
-          if (d >= rlo) {
-            const float2 r = cs[(d - rlo) >> 1];
-            const float x0 = (float)qf[k][i], x1 = (float)qf[k][i + 1];
-            qf[k][i] = (bf16)(x0 * r.x - x1 * r.y);
-            qf[k][i + 1] = (bf16)(x0 * r.y + x1 * r.x);
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();  // q staging and the RoPE table are no longer read
 
   // Key sources, one tile ahead: lane l < 32 resolves key tile*32 + l.
   const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
@@ -542,6 +507,44 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     }
     return bits;
   };
+
+  bf16x8 qf[16];
+  // Pass 0's first tile is requested before q, so both latencies overlap.
+  const int ntiles = (nk + KT - 1) / KT;
+  uint32_t km0 = 0u, km1 = 0u;
+  int sv = 0;
+  {
+    const int sv0 = ntiles > 0 ? load_idx(0) : 0;
+    // Q^T fragments straight from global memory: lane (head 32hg + l32, g), k-step k
+    // holds dims 256dh + 16k + 8g .. +7 (bf16x8 vectors: two values per register)
+    const int h = 32 * hg + l32;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      qf[k] = h < a.H ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                            qg + (int64_t)h * ROWB + 2 * (256 * dh + 16 * k + 8 * g)))
+                      : bf16x8{};
+    if (ntiles > 0) km0 = issue(0, sv0, st0);
+    if (ntiles > 1) sv = load_idx(1);
+  }
+  __syncthreads();  // the RoPE table is written; q and key tile 0 have landed
+  // rotate q at +P where its dims fall in the last R
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int d0 = 256 * dh + 16 * k + 8 * g;
+    if (d0 + 8 > rlo) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int d = d0 + i;
+        if (d >= rlo) {
+          const float2 r = cs[(d - rlo) >> 1];
+          const float x0 = (float)qf[k][i], x1 = (float)qf[k][i + 1];
+          qf[k][i] = (bf16)(x0 * r.x - x1 * r.y);
+          qf[k][i + 1] = (bf16)(x0 * r.y + x1 * r.x);
+        }
+      }
+    }
+  }
+  lds_barrier();  // the table is read; the exchange buffer may be reused
 
   // Per-lane LDS offsets.  QK: row l32, chunk 32dh + 2k + g at position
   // 32dh + 8(k>>2) + ((2(k&3) + g) ^ swz(l32)): four bases, 128(k>>2) an immediate.
@@ -621,18 +624,17 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     }
   };
 
-  const int ntiles = (nk + KT - 1) / KT;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
     l_run = 0.f;
-    uint32_t km0 = 0u, km1 = 0u;
-    int sv = 0;
-    if (ntiles > 0) km0 = issue(0, load_idx(0), st0);
-    if (ntiles > 1) sv = load_idx(1);
-    __syncthreads();
+    if (pass > 0) {
+      if (ntiles > 0) km0 = issue(0, load_idx(0), st0);
+      if (ntiles > 1) sv = load_idx(1);
+      __syncthreads();
+    }
     for (int tile = 0; tile < ntiles; tile += 2) {
       if (tile + 1 < ntiles) km1 = issue(tile + 1, sv, st1);
       if (tile + 2 < ntiles) sv = load_idx(tile + 2);
