@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the fused compressed-attention layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3|C2|C1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3|C2|C1|C4]
 
 One step is one fused layer call (csa_fwd for CSA, hca_fwd for HCA) over one batch of
 seeded synthetic inputs that are already resident in HBM: gated pooling + RMSNorm +
@@ -226,12 +226,78 @@ def cpu_baseline(cfg, inp, budget_s: float):
             "seconds": round(t_comp + t_rows, 2)}
 
 
+def run_stack(args, dev) -> dict:
+    """The 43-layer training-shape stack (B=4, S=8192): every layer's seeded inputs are
+    generated once and stay resident (about 110 GB); a step runs all 43 layers in order
+    through their entry points (window-only attention, csa_fwd, hca_fwd), each into the
+    same output buffer.  tokens/s = B*S per step."""
+    import torch
+    from compressed_sparse_attention_hca_amd import binding as bd
+    from compressed_sparse_attention_hca_amd import workloads as wl
+
+    layers = wl.stack_layers()
+    log(f"[bench] 43-layer stack: generating inputs on the GPU")
+    inps = [wl.make_inputs(c, dev) for c in layers]
+    params = [bd.params(c) for c in layers]
+    ops = {"csa": bd.OP_CSA_FWD, "hca": bd.OP_HCA_FWD, "swa": bd.OP_SPARSE_MQA}
+    ws_bytes = max(bd.workspace_bytes(p, ops[c.kind]) for p, c in zip(params, layers))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(inps[0]["q"])
+
+    def layer(k):
+        c, p, inp = layers[k], params[k], inps[k]
+        if c.kind == "swa":
+            bd.sparse_mqa_fwd(p, inp["q"], None, inp["kv_raw"], o=o, ws=ws)
+        else:
+            bd.layer_fwd(p, inp, o=o, ws=ws)
+
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        for k in range(len(layers)):
+            layer(k)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for k in range(len(layers)):
+            layer(k)
+            ev[s][k + 1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per_kind = {}
+    for s in range(args.steps):
+        for k, c in enumerate(layers):
+            per_kind[c.kind] = per_kind.get(c.kind, 0.0) + ev[s][k].elapsed_time(ev[s][k + 1]) / args.steps
+    flops = sum(wl.layer_flops(c)["total"] for c in layers)
+    B, S = layers[0].B, layers[0].S
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    counts = {kd: sum(1 for c in layers if c.kind == kd) for kd in per_kind}
+    return {
+        "metric": "43-layer V4-Flash attention stack fwd tokens/s (B=4, S=8192, 1 GPU)",
+        "value": round(B * S / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": "v4flash_stack43_bf16_B4_S8192", "B": B, "S": S, "layers": len(layers),
+                   "csa": counts.get("csa", 0), "hca": counts.get("hca", 0), "swa": counts.get("swa", 0)},
+        "layer_tokens_per_s": round(len(layers) * B * S / (ms_step * 1e-3), 1),
+        "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops,
+        "ms_per_kind": {kd: round(v, 3) for kd, v in per_kind.items()},
+        "ms_per_layer_of_kind": {kd: round(v / counts[kd], 3) for kd, v in per_kind.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3"])
+    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4"],
+                    help="C3 (default): the CSA layer at S=65536; C4: the 43-layer stack")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -263,9 +329,12 @@ def main():
     from compressed_sparse_attention_hca_amd import binding as bd
     from compressed_sparse_attention_hca_amd import workloads as wl
 
-    cfg = wl.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "C4":
+        print(json.dumps(run_stack(args, dev)), flush=True)
+        return
+    cfg = wl.CONFIGS[args.workload]
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = wl.make_inputs(cfg, dev)
     p = bd.params(cfg)
