@@ -582,29 +582,32 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) xb[wave][q][lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
     lds_barrier();
+    // logits in unscaled units; the base-2 scale is folded into the exponent's FMA
     float z[16];
-    float mt = -INFINITY;
-    const uint32_t kml = kmask >> (4 * g);  // bit 8q + i: key 8q + 4g + i (constant shifts)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 o4 = xb[wave ^ 1][q][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * q + i;
-        const float v = ((kml >> (8 * q + i)) & 1u) ? (s[e] + o4[i]) * a.scale_log2 : -INFINITY;
-        z[e] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int i = 0; i < 4; ++i) z[4 * q + i] = s[4 * q + i] + o4[i];
     }
+    if (kmask != 0xffffffffu) {  // wave-uniform: only partial or masked tiles pay for the mask
+      const uint32_t kml = kmask >> (4 * g);  // bit 8q + i: key 8q + 4g + i
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!((kml >> (8 * (e >> 2) + (e & 3))) & 1u)) z[e] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, z[e]);
     mt = halves_max(mt);
     m_seen = fmaxf(m_seen, mt);
     if (m_ref == -INFINITY) m_ref = mt;  // O and l are still zero
-    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+    const float nbias = (m_ref == -INFINITY) ? 0.f : -m_ref * a.scale_log2;
     bf16x8 pf[2];
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(z[e] - mref);
+      const float p = __builtin_amdgcn_exp2f(fmaf(z[e], a.scale_log2, nbias));
       ls += p;
       pf[e >> 3][e & 7] = (bf16)p;
     }
@@ -649,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     }
     if (threadIdx.x == 0) *ovf = 0;
     __syncthreads();
-    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(ovf, 1);
+    if (__any((m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0) atomicOr(ovf, 1);
     __syncthreads();
     const int again = *ovf;
     __syncthreads();
