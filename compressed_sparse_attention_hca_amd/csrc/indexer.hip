@@ -231,9 +231,13 @@ struct IndexTopkArgs {
   int32_t B, S, HI, ratio, n_entries, topk, qblocks;  // query blocks per batch
 };
 
+// Order-preserving key of a score: negative floats have every bit flipped, the others
+// only the sign bit.  The epilogue's scores are never -0 (each is a round-to-nearest sum
+// that starts from +0, and such a sum is -0 only when every term is -0), so +0 and -0
+// need no merging here.
 __device__ inline uint32_t score_key(float f) {
-  const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);  // -0 and +0 tie
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ inline int wave_excl_scan(int v) {
@@ -269,13 +273,10 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup barrier that orders LDS accesses only: direct-to-LDS copies still in flight
-// (counted by vmcnt) are waited for separately by wait_vmcnt.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// Barrier after this wave's LDS accesses have completed; the copies in flight are
+// waited for separately (wait_vmcnt), and the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ inline void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct Pruned {
   int c;              // keys kept
@@ -443,7 +444,6 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 5;
   const int l32 = lane & 31;
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int t = qb * FT_WAVES + wave;
   const bool q_ok = t < a.S;
   const int n_t = q_ok ? visible_entries(t, a.ratio) : 0;
@@ -494,9 +494,11 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       const int L = wave + j * FT_WAVES;
       if (L < SH::NI) {  // wave-uniform
         const int row = min(tile * FT_TILE + dma_row[j], n_blk - 1);  // past the end: a valid row
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(kbase + (int64_t)row * SH::ROWB + dma_off[j]),
-            (CSA_LDS void*)(st + L * 1024), 16, 0, 0);
+        // written in assembly, so the compiler adds no conservative waits for the LDS
+        // writes; the waits are the explicit vmcnt waits before each tile's barrier
+        const uint32_t voff = (uint32_t)row * SH::ROWB + dma_off[j];
+        const uint32_t lds = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(st + L * 1024);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(kbase), "{m0}"(lds) : "memory");
       }
     }
   };
@@ -553,17 +555,20 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     const uint32_t key = score_key(s);
     const bool admit = g == 0 && e >= 0 && e < n_t && key > theta;
     const uint64_t bm = __ballot(admit);
-    // branch-free append: refused lanes all write the first free slot (c + 32 < CAP
-    // holds here, see make_room)
-    const int pos = c + __popcll(admit ? bm & lt : bm);
+    const int nadm = __popcll(bm);
+    // branch-free append: an admitted lane writes after the admitted lanes below it
+    // (only lanes < 32 admit, so the low half of the mask counts them); refused lanes
+    // all write the first free slot (c + 32 < CAP holds here, see make_room)
+    const int pos = c + (admit ? (int)__builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u) : nadm);
     my_key[pos] = key;
     my_idx[pos] = e;
     kmax_l = admit ? max(kmax_l, key) : kmax_l;
     kmn_l = admit ? min(kmn_l, key) : kmn_l;
-    c += __popcll(bm);
+    c += nadm;
   };
 
   const int ntiles = (n_blk + FT_TILE - 1) / FT_TILE;
+  wait_vmcnt<0, false>();  // q and w are in registers before any copy is counted
   if (ntiles > 0) issue(0, st0);
   if (ntiles > 1) issue(1, st1);
 
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   auto step = [&](int it, const unsigned char* cur, unsigned char* refill) {
     if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, false>();
     else wait_vmcnt<0, false>();
-    lds_barrier();
+    lds_only_barrier();
     if (!select_all) {  // prune before the refill is issued: the prune's LDS atomics wait
                         // for every copy in flight, and the older one has likely landed
       const int4 v0 = *reinterpret_cast<const int4*>(&vote[0]);
