@@ -381,16 +381,20 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
 // reads only its half of every key row, so a 32-key tile costs 160 KB of LDS reads and
 // writes per workgroup instead of the 256 KB of the 16-head mapping.  Per tile:
 //   partial S^T[32 keys, 32 heads] over the wave's 256 dims      (16 MFMAs)
-//     lane (head l%32, g = l/32) holds keys 8j + 4g + i, j, i = 0..3
-//   exchange partials with the partner wave (same heads, other half) through LDS;
-//   both add own + partner's (fp32 addition commutes, so both get identical logits)
-//   softmax against a fixed reference, P^T to bf16 in registers
-//   O^T[256 dims, 32 heads] += V^T . P^T                          (16 MFMAs)
-//     k-step ks takes accumulator rows j = 2ks, 2ks+1: keys 16ks + {4g..4g+3,
-//     8+4g..8+4g+3}; V^T for those keys comes from two transposing LDS reads.
-// LDS is exactly two 32 KB key stages plus the 16 KB exchange buffer (two workgroups
-// per CU); the RoPE table and the overflow flag borrow the exchange buffer outside the
-// key loop, and the key indices are read from global memory one tile ahead.
+//     lane (head l%32, g = l/32) holds accumulator rows 8j + 4g + i, j, i = 0..3;
+//     row r is key r ^ 16dh, so rows 0..15 are the wave's own half of the keys
+//   send the partner wave (same heads, other latent half) the partials of its keys and
+//   add the partner's partials of this wave's keys (through LDS)
+//   softmax of the wave's 16 keys against a fixed reference, P^T to bf16; swap the
+//   bf16 probabilities with the partner (through LDS)
+//   O^T[256 dims, 32 heads] += V^T . P^T over all 32 keys        (16 MFMAs)
+//     k-step 0 takes the wave's own keys, k-step 1 the partner's: keys {4g..4g+3,
+//     8+4g..8+4g+3} of that half; V^T for them comes from two transposing LDS reads.
+// Splitting the softmax halves its exponentials and VALU work per wave, for one more
+// barrier per tile.  LDS is exactly two 32 KB key stages plus a 16 KB exchange area
+// (two workgroups per CU); the RoPE table and the overflow flag borrow the exchange
+// area outside the key loop, and the key indices are read from global memory one tile
+// ahead.
 // ---------------------------------------------------------------------------------
 // Combine lane l with lane l ^ 32 (v_permlane32_swap: no LDS traffic, no address
 // register).  The swap yields both halves' values in every lane, in the same order in
@@ -424,9 +428,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
   __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
-  __shared__ __attribute__((aligned(16))) f32x4 xb[4][4][64];
-  float2* cs = reinterpret_cast<float2*>(&xb[0][0][0]);  // RoPE table outside the loop
-  int* ovf = reinterpret_cast<int*>(&xb[0][0][0]);       // overflow flag outside the loop
+  // exchange area: partial logits xh (8 KB), probabilities xp (4 KB), per-head maxima
+  // and sums xm (1 KB); the RoPE table and the overflow flag borrow it outside the loop
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[16384];
+  f32x4 (*xh)[2][64] = reinterpret_cast<f32x4 (*)[2][64]>(xbuf);
+  u32x4 (*xp)[64] = reinterpret_cast<u32x4 (*)[64]>(xbuf + 8192);
+  float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
+  float2* cs = reinterpret_cast<float2*>(xbuf);  // RoPE table outside the loop
+  int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
 
   // workgroup -> query: as sparse_mqa_kernel (32 consecutive queries per XCD visit)
   const int total = a.B * a.S;
@@ -546,11 +555,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   }
   lds_barrier();  // the table is read; the exchange buffer may be reused
 
-  // Per-lane LDS offsets.  QK: row l32, chunk 32dh + 2k + g at position
-  // 32dh + 8(k>>2) + ((2(k&3) + g) ^ swz(l32)): four bases, 128(k>>2) an immediate.
+  // Per-lane LDS offsets.  QK: lane row l32 holds key kr = l32 ^ 16dh (this wave's own
+  // keys 16dh .. 16dh+15 become accumulator rows 0..15, the partner's rows 16..31);
+  // chunk 32dh + 2k + g of key row kr sits at 32dh + 8(k>>2) + ((2(k&3) + g) ^ swz(kr)):
+  // four bases, 128(k>>2) an immediate.
+  const int kr = l32 ^ (16 * dh);
   int qk_base[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) qk_base[m] = l32 * ROWB + ((32 * dh + ((2 * m + g) ^ swz(l32))) << 4);
+  for (int m = 0; m < 4; ++m) qk_base[m] = kr * ROWB + ((32 * dh + ((2 * m + g) ^ swz(kr))) << 4);
   // PV: 16-lane group h = lane/16 covers dims 256dh + 32db + 16(h&1) .. +15; lane j of
   // the group addresses key row 16ks + 4g + j/4 (and +8), dims + 4(j%4).  With
   // a4 = j/4 the row's swizzle is 2a4 | g for every ks and for the +8 row, and the
@@ -569,7 +581,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
   f32x16 O[8];
 
-  auto compute = [&](const unsigned char* sb, uint32_t kmask) {
+  // The partner waves (same heads, other latent half) split the softmax: wave dh owns
+  // keys 16dh .. 16dh+15 of each tile (its accumulator rows 0..15).  Each sends the
+  // partner its partial logits of the partner's keys, forms the full logits of its own,
+  // and the two swap their bf16 probabilities for PV.  Both use the same per-head
+  // reference: the maximum of the pass's first tile, agreed through xm (0 if that tile
+  // has no valid key; the end-of-pass check then catches any under- or overflow).
+  const int pv_mine = 16 * ROWB * dh, pv_other = 16 * ROWB * (dh ^ 1);
+  auto compute = [&](const unsigned char* sb, uint32_t kmask, bool first) {
     const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
     f32x16 s = {};
 #pragma unroll
@@ -578,49 +597,57 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
       if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    // exchange partial logits with the partner wave
+    // send the partner's keys (rows 16..31), receive this wave's
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xb[wave][q][lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+    for (int q = 0; q < 2; ++q) xh[wave][q][lane] = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
     lds_barrier();
     // logits in unscaled units; the base-2 scale is folded into the exponent's FMA
-    float z[16];
+    float z[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 o4 = xb[wave ^ 1][q][lane];
+    for (int q = 0; q < 2; ++q) {
+      const f32x4 o4 = xh[wave ^ 1][q][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[4 * q + i] = s[4 * q + i] + o4[i];
     }
     if (kmask != 0xffffffffu) {  // wave-uniform: only partial or masked tiles pay for the mask
-      const uint32_t kml = kmask >> (4 * g);  // bit 8q + i: key 8q + 4g + i
+      const uint32_t kml = kmask >> (4 * g + 16 * dh);  // bit 8q + i: key 16dh + 8q + 4g + i
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < 8; ++e)
         if (!((kml >> (8 * (e >> 2) + (e & 3))) & 1u)) z[e] = -INFINITY;
     }
     float mt = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, z[e]);
+    for (int e = 0; e < 8; ++e) mt = fmaxf(mt, z[e]);
     mt = halves_max(mt);
     m_seen = fmaxf(m_seen, mt);
-    if (m_ref == -INFINITY) m_ref = mt;  // O and l are still zero
-    const float nbias = (m_ref == -INFINITY) ? 0.f : -m_ref * a.scale_log2;
-    bf16x8 pf[2];
+    if (first) {  // workgroup-uniform: agree on the reference
+      xm[wave][lane] = mt;
+      lds_barrier();
+      const float m0 = fmaxf(mt, xm[wave ^ 1][lane]);
+      m_ref = m0 == -INFINITY ? 0.f : m0;
+    }
+    const float nbias = -m_ref * a.scale_log2;
+    bf16x8 pm;
     float ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(z[e], a.scale_log2, nbias));
       ls += p;
-      pf[e >> 3][e & 7] = (bf16)p;
+      pm[e] = (bf16)p;
     }
     l_run += ls;
+    xp[wave][lane] = __builtin_bit_cast(u32x4, pm);
+    lds_barrier();
+    const bf16x8 po = __builtin_bit_cast(bf16x8, xp[wave ^ 1][lane]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + 16 * ROWB * ks;
+        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + (ks ? pv_other : pv_mine);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks], O[db], 0, 0, 0);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ks ? po : pm, O[db], 0, 0, 0);
       }
       // keep the transposing reads at most one block ahead of their MFMAs
       if (db & 1) __builtin_amdgcn_sched_barrier(0);
@@ -641,29 +668,37 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     for (int tile = 0; tile < ntiles; tile += 2) {
       if (tile + 1 < ntiles) km1 = issue(tile + 1, sv, st1);
       if (tile + 2 < ntiles) sv = load_idx(tile + 2);
-      compute(st0, km0);
-      __syncthreads();  // tile+1 landed in st1; every wave is done with st0 and xb
+      compute(st0, km0, pass == 0 && tile == 0);
+      __syncthreads();  // tile+1 landed in st1; every wave is done with st0 and the exchange area
       if (tile + 1 < ntiles) {
         if (tile + 2 < ntiles) km0 = issue(tile + 2, sv, st0);
         if (tile + 3 < ntiles) sv = load_idx(tile + 3);
-        compute(st1, km1);
+        compute(st1, km1, false);
         __syncthreads();
       }
     }
+    // the pair's maximum; run again with it as the reference if some probability could
+    // have overflowed, or (reference taken as 0 after an all-masked first tile) underflowed
+    xm[wave][lane] = m_seen;
     if (threadIdx.x == 0) *ovf = 0;
     __syncthreads();
-    if (__any((m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0) atomicOr(ovf, 1);
+    const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
+    const float dev = (mall - m_ref) * a.scale_log2;
+    if (__any(mall != -INFINITY && fabsf(dev) > 64.0f) && lane == 0) atomicOr(ovf, 1);
     __syncthreads();
     const int again = *ovf;
     __syncthreads();
     if (!again) break;
-    m_ref = m_seen;  // exact reference for the second pass
+    m_ref = mall;  // exact reference for the second pass
   }
 
   // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced
-  rope_table();
-  l_run = halves_sum(l_run);
+  xm[wave][lane] = l_run;
+  __syncthreads();
+  l_run = halves_sum(l_run + xm[wave ^ 1][lane]);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  __syncthreads();
+  rope_table();
   __syncthreads();
   {
     unsigned char* os = hg == 0 ? st0 : st1;

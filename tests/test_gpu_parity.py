@@ -290,6 +290,40 @@ def test_empty_batch_is_noop(bd):
     assert bd.lib.csa_sparse_mqa_fwd(ctypes.byref(p), None, None, None, None, None, None, 0, None) == bd.CSA_OK
 
 
+def test_invalid_selection_entries_are_masked(bd):
+    """Selection entries outside 0..n_t-1 (-1 padding, n_t and beyond, negative) are
+    masked out and never read.  The first 40 entries of every row are made invalid, so
+    the first 32-key tile of each query holds no valid entry, and every seventh row's
+    whole selection is invalid (window keys only).  The oracle attends over the valid
+    entries that remain."""
+    cfg = wl.C1.replace(S=1024, name="c1_masked")
+    inp = gen(cfg)
+    _, kv_c, idx, nv = run_layer(bd, cfg, inp)
+    bad = idx.clone()
+    n_t = nv[0].long()
+    junk = torch.tensor([-1, 0, 1000, -7], device=DEV)  # 0 becomes n_t below
+    for t in range(cfg.S):
+        n = min(cfg.topk, int(n_t[t]))
+        k = n if t % 7 == 0 else min(40, n)
+        if k:
+            v = junk[torch.arange(k, device=DEV) % 4].to(torch.int32)
+            v = torch.where(v == 0, n_t[t].to(torch.int32), v)
+            v = torch.where(v == 1000, n_t[t].to(torch.int32) + 1000, v)
+            bad[0, t, :k] = v
+    o = bd.sparse_mqa_fwd(bd.params(cfg), inp["q"], kv_c, inp["kv_raw"], bad)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, 16) + [(0, 7), (0, 70), (0, 700), (0, 1015)]
+    sel = {}
+    for (b, t) in rows:
+        n = min(cfg.topk, int(n_t[t]))
+        r = bad[b, t, :n].cpu().numpy()
+        sel[(b, t)] = r[(r >= 0) & (r < int(n_t[t]))]
+    ora = O.layer_rows(cfg, lazy_inputs(inp), rows, sel_override=sel)
+    got = np.stack([o[b, t].float().cpu().double().numpy() for (b, t) in rows])
+    assert np.all(np.isfinite(got))
+    assert_close_rel(got, np.stack([ora["o"][k] for k in rows]), 1e-2, "o masked selection")
+
+
 # -------------------------------------------------------------- invariants ---------
 
 def test_topk_covering_all_equals_dense_bitwise(bd):
