@@ -61,15 +61,26 @@ __device__ inline void store8(T* p, const float (&x)[8]) {
   }
 }
 
-// Rotate this lane's 8 channels c0..c0+7 in place where they fall in the last R dims.
-__device__ inline void rope8(float (&x)[8], int c0, int D, int R, int64_t P, double theta, bool inverse) {
+// Inverse frequencies of this lane's 4 channel pairs c0..c0+7 (0 outside the last R dims).
+__device__ inline void rope8_freq(double (&f)[4], int c0, int D, int R, double theta) {
+  const int lo = D - R;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = c0 + 2 * k;
+    f[k] = c >= lo ? rope_inv_freq((c - lo) >> 1, R, theta) : 0.0;
+  }
+}
+
+// Rotate this lane's 8 channels c0..c0+7 in place where they fall in the last R dims,
+// with the inverse frequencies from rope8_freq.
+__device__ inline void rope8(float (&x)[8], int c0, int D, int R, int64_t P, const double (&f)[4], bool inverse) {
   const int lo = D - R;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = c0 + 2 * k;
     if (c >= lo) {
       float cs, sn;
-      rope_cos_sin(P, rope_inv_freq((c - lo) >> 1, R, theta), &cs, &sn);
+      rope_cos_sin(P, f[k], &cs, &sn);
       if (inverse) sn = -sn;
       const float x0 = x[2 * k], x1 = x[2 * k + 1];
       x[2 * k] = x0 * cs - x1 * sn;
@@ -171,7 +182,9 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] *= inv;
   if (!lane_ok) return;
-  rope8(p, c0, a.D, a.R, entry_position(a.pos0, s, r), a.theta, false);
+  double f[4];
+  rope8_freq(f, c0, a.D, a.R, a.theta);
+  rope8(p, c0, a.D, a.R, entry_position(a.pos0, s, r), f, false);
   store8<T>(static_cast<T*>(a.kv_c) + ((int64_t)b * a.n_entries + s) * a.D + c0, p);
 }
 
@@ -185,34 +198,44 @@ struct WindowArgs {
 };
 
 // Raw window latents rotated at their own positions pos0 + t (optionally normalised
-// first); one wave per token.
+// first).  One wave rotates WR_TOKENS consecutive tokens (one 16-byte chunk per lane per
+// token), so the inverse frequencies (an fp64 pow each) are worked out once per wave.
+constexpr int WR_TOKENS = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void window_rope_kernel(WindowArgs a) {
   const int lane = threadIdx.x & 63;
-  const int tok = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= a.B * a.S) return;
+  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * WR_TOKENS;
+  const int64_t total = (int64_t)a.B * a.S;
+  if (tok0 >= total) return;
   const int c0 = lane * 8;
   const bool lane_ok = c0 < a.D;
-  const int t = tok % a.S;
-  float x[8];
-  const int64_t off = (int64_t)tok * a.D + c0;
-  if (lane_ok) load8<T>(static_cast<const T*>(a.kv_raw) + off, x);
-  else {
+  double f[4];
+  rope8_freq(f, c0, a.D, a.R, a.theta);
+  for (int j = 0; j < WR_TOKENS; ++j) {
+    const int64_t tok = tok0 + j;
+    if (tok >= total) break;  // wave-uniform
+    const int t = (int)(tok % a.S);
+    float x[8];
+    const int64_t off = tok * a.D + c0;
+    if (lane_ok) load8<T>(static_cast<const T*>(a.kv_raw) + off, x);
+    else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    if (a.norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] *= inv;
+    }
+    if (lane_ok) {
+      rope8(x, c0, a.D, a.R, a.pos0 + t, f, false);
+      store8<T>(static_cast<T*>(a.kv_w) + off, x);
+    }
   }
-  if (a.norm) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)a.D + a.eps);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] *= inv;
-  }
-  if (!lane_ok) return;
-  rope8(x, c0, a.D, a.R, a.pos0 + t, a.theta, false);
-  store8<T>(static_cast<T*>(a.kv_w) + off, x);
 }
 
 hipError_t launch_compress(const csa_params_t& p, const void* va, const void* ga, const void* vb,
@@ -239,7 +262,8 @@ hipError_t launch_window_rope(const csa_params_t& p, const void* kv_raw, void* k
                p.rms_eps, p.rope_theta, p.pos0};
   const int total = p.B * p.S;
   if (total == 0) return hipSuccess;
-  dim3 grid((total + 3) / 4), block(256);
+  const int64_t waves = ((int64_t)total + WR_TOKENS - 1) / WR_TOKENS;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   if (p.dtype == CSA_BF16) hipLaunchKernelGGL((window_rope_kernel<bf16>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((window_rope_kernel<float>), grid, block, 0, st, a);
   return hipGetLastError();
