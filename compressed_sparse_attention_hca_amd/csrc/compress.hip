@@ -11,9 +11,10 @@
 // deepseek-v4): correct V4-Flash attention math", Part 1 items 1-2.
 //
 // Memory-bound streaming: each lane owns 8 channels (16 B of bf16 per load), a wave
-// covers a 512-wide row, and the per-channel softmax runs online in registers so every
-// input byte is read once.  CSA (8 slots) uses one wave per entry; HCA (128 slots)
-// splits the slots over the 4 waves of a workgroup and merges them through LDS.
+// covers a 512-wide row, and every input byte is read once.  CSA (8 slots) uses one
+// wave per entry, with all 8 slots in registers and a two-pass softmax per channel;
+// HCA (128 slots) splits the slots over the 4 waves of a workgroup, runs the softmax
+// online in registers and merges the waves through LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -118,7 +119,45 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) { m[i] = -INFINITY; l[i] = 0.f; acc[i] = 0.f; }
 
-  if (lane_ok) {
+  if (WPE == 1 && span == 8) {
+    // 8 slots (CSA at ratio 4): every load is issued first, then a two-pass softmax
+    // per channel (one exponential per slot instead of the online form's two)
+    if (lane_ok) {
+      float lg[8][8], v[8][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tok = a.overlap ? s * r - r + j : s * r + j;  // wave-uniform
+        if (tok >= 0) {
+          const bool prev = a.overlap && j < r;
+          const int64_t off = ((int64_t)b * a.S + tok) * a.D + c0;
+          float g[8], bias[8];
+          load8<T>((prev ? gb : ga) + off, g);
+          load8<T>((prev ? vb : va) + off, v[j]);
+          load8<float>(a.bias + (int64_t)j * a.D + c0, bias);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) lg[j][i] = g[i] + bias[i];
+        } else {  // CSA entry 0: no previous group
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { lg[j][i] = -INFINITY; v[j][i] = 0.f; }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float mx = lg[0][i];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, lg[j][i]);
+        float li = 0.f, ai = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float ex = expf(lg[j][i] - mx);
+          li += ex;
+          ai += ex * v[j][i];
+        }
+        l[i] = li;
+        acc[i] = ai;
+      }
+    }
+  } else if (lane_ok) {
     for (int j = j0; j < j1; ++j) {
       const int tok = a.overlap ? s * r - r + j : s * r + j;
       if (tok < 0) continue;  // CSA entry 0: no previous group
