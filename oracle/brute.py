@@ -55,8 +55,9 @@ def brute_entry(va, ga, vb, gb, bias, s, r, overlap, D):
     return p
 
 
-def brute_layer(cfg, inp, b=0):
-    """Returns dict with o[t][h][d], sel[t] (sorted list), kv_c[s][d] for batch b."""
+def brute_layer(cfg, inp, b=0, sinks=None):
+    """Returns dict with o[t][h][d], sel[t] (sorted list), kv_c[s][d] for batch b.
+    sinks: optional per-head softmax sink logits (a key with no value)."""
     S, H, D, R, r = cfg.S, cfg.H, cfg.D, cfg.rope_dim, cfg.ratio
     theta, eps, pos0 = cfg.rope_theta, cfg.rms_eps, cfg.pos0
     scale = cfg.softmax_scale
@@ -106,9 +107,13 @@ def brute_layer(cfg, inp, b=0):
         for h in range(H):
             qh = brute_rope(q[t][h], pos0 + t, R, theta)
             z = [sum(qh[d] * k[d] for d in range(D)) * scale for k in keys]
-            mx = max(z)
+            mx = max(z) if z else float(sinks[h])
+            if sinks is not None:
+                mx = max(mx, float(sinks[h]))
             e = [math.exp(v - mx) for v in z]
             tot = sum(e)
+            if sinks is not None:
+                tot += math.exp(float(sinks[h]) - mx)
             u = [sum(e[j] / tot * keys[j][d] for j in range(len(keys))) for d in range(D)]
             o_t.append(brute_rope(u, -(pos0 + t), R, theta))
         res["o"].append(o_t)

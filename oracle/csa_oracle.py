@@ -175,15 +175,27 @@ def rotate_window(kv_raw, rope_dim, theta, eps, pos0=0, norm_window=False):
     return rope(x, pos, rope_dim, theta)
 
 
-def attend_row(qr_t, keys, scale: float):
+def attend_row(qr_t, keys, scale: float, sink=None):
     """One query's multi-query attention: z = (q.key) * scale for every head and key,
     one softmax over all keys, u = sum P key (K = V, [BLOG] "The DeepSeek-V4-Flash
     architecture").  qr_t [H, D] (already rotated), keys [nk, D].  Returns (u [H, D],
-    P [H, nk])."""
+    P [H, nk]).
+
+    sink [H] (optional): one fp32 logit per head that joins each head's softmax as a
+    key with no value, i.e. exp(sink_h) is added to the denominator.  [BLOG] "Kernel
+    fusions", row "SWA / CSA / HCA attention" (the attention kernel folds in the
+    softmax sink); [PR930] Part 1 item 6f (the sink is an FP32 logit that feeds the
+    softmax directly).  With a sink, a query with no key gives u = 0."""
     z = (qr_t @ keys.T) * scale
-    m = np.max(z, axis=1, keepdims=True)
+    if sink is None:
+        m = np.max(z, axis=1, keepdims=True)
+        e = np.exp(z - m)
+        P = e / np.sum(e, axis=1, keepdims=True)
+        return P @ keys, P
+    sk = np.asarray(sink, dtype=np.float64).reshape(-1, 1)
+    m = sk if z.shape[1] == 0 else np.maximum(np.max(z, axis=1, keepdims=True), sk)
     e = np.exp(z - m)
-    P = e / np.sum(e, axis=1, keepdims=True)
+    P = e / (np.sum(e, axis=1, keepdims=True) + np.exp(sk - m))
     return P @ keys, P
 
 
@@ -191,11 +203,12 @@ def _as64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_p=False):
+def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_p=False, sinks=None):
     """Oracle outputs for the query rows `rows` of batch 0..B-1 (rows is a list of
     (b, t) pairs).  `inp` holds numpy arrays (any float dtype) with the shapes of
     workloads.make_inputs.  `sel_override` maps (b, t) to a selection to use instead
     of the oracle's own top-k (for re-evaluating on another admissible selection).
+    `sinks` [H] (optional): per-head softmax sink logits (see attend_row).
 
     Returns a dict: o {(b,t): [H,D]}, sel {(b,t): indices}, scores {(b,t): row},
     n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, and P when
@@ -249,7 +262,7 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
                 ent_keys = kvb[sel]
             keys = np.concatenate([ent_keys, win_keys], axis=0)
             qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
-            u, P = attend_row(qr, keys, scale)
+            u, P = attend_row(qr, keys, scale, sinks)
             out["o"][(b, t)] = rope(u, -(pos0 + t), R, theta)
             out["sel"][(b, t)] = sel
             out["n_visible"][(b, t)] = n_vis
@@ -259,10 +272,10 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
     return out
 
 
-def layer_forward(cfg, inp: dict, want_p=False) -> dict:
+def layer_forward(cfg, inp: dict, want_p=False, sinks=None) -> dict:
     """Whole-layer oracle: o [B, S, H, D] plus kv_c, selections, scores and layout."""
     rows = [(b, t) for b in range(cfg.B) for t in range(cfg.S)]
-    r = layer_rows(cfg, inp, rows, want_p=want_p)
+    r = layer_rows(cfg, inp, rows, want_p=want_p, sinks=sinks)
     o = np.zeros((cfg.B, cfg.S, cfg.H, cfg.D))
     for (b, t), v in r["o"].items():
         o[b, t] = v

@@ -307,6 +307,58 @@ def test_csa_with_topk_covering_all_equals_dense():
         assert np.allclose(a["o"][k], b["o"][k], atol=0)
 
 
+# ---------------------------------------------------------------- sink -------------
+# The softmax sink: one fp32 logit per head that joins the softmax with no value
+# ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
+# "Kernel fusions", row "SWA / CSA / HCA attention"; "fix(deepseek-v4)", Part 1 item 6f).
+
+def test_sink_closed_form_scales_the_uniform_average():
+    """Zero queries make every logit 0.  A sink of ln(n * c) for n keys gives every key
+    probability 1 / (n (1 + c)), so the output is the plain mean divided by 1 + c."""
+    cfg = tiny("hca", S=40, H=3, window=5)
+    inp = to_np(wl.make_inputs(cfg))
+    inp["q"][:] = 0.0
+    t = 21
+    n = O.visible_entries(t, cfg.ratio) + min(cfg.window, t + 1)
+    c = np.array([0.5, 1.0, 3.0])
+    r0 = O.layer_rows(cfg, inp, [(0, t)])
+    r1 = O.layer_rows(cfg, inp, [(0, t)], sinks=np.log(n * c))
+    for h in range(cfg.H):
+        assert np.allclose(r1["o"][(0, t)][h], r0["o"][(0, t)][h] / (1.0 + c[h]), atol=1e-13)
+
+
+def test_sink_minus_infinity_is_no_sink_and_large_sink_silences():
+    cfg = tiny("csa", S=48)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in (3, 17, 47)]
+    a = O.layer_rows(cfg, inp, rows, want_p=True)
+    b = O.layer_rows(cfg, inp, rows, want_p=True, sinks=np.full(cfg.H, -np.inf))
+    c = O.layer_rows(cfg, inp, rows, sinks=np.full(cfg.H, 800.0))
+    for k in rows:
+        assert np.array_equal(a["o"][k], b["o"][k]) and np.array_equal(a["P"][k], b["P"][k])
+        assert np.abs(c["o"][k]).max() == 0.0  # exp(z - 800) underflows: all mass on the sink
+        assert np.all(np.asarray(b["P"][k]).sum(1) <= 1.0 + 1e-12)
+
+
+def test_sink_with_no_key_gives_zero():
+    """No key at all (window 0, t < ratio - 1): with a sink the softmax is defined and
+    all of its mass is on the sink, so the output is 0."""
+    cfg = tiny("hca", S=16, ratio=8, window=0)
+    inp = to_np(wl.make_inputs(cfg))
+    r = O.layer_rows(cfg, inp, [(0, 3)], sinks=np.zeros(cfg.H))
+    assert np.array_equal(r["o"][(0, 3)], np.zeros((cfg.H, cfg.D)))
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
+def test_oracle_with_sink_matches_brute_force(kind, rng):
+    cfg = tiny(kind, S=24, pos0=5)
+    inp = to_np(wl.make_inputs(cfg))
+    sinks = rng.normal(size=cfg.H) * 2.0
+    ora = O.layer_forward(cfg, inp, sinks=sinks)
+    bf = brute.brute_layer(cfg, inp, sinks=sinks)
+    assert np.allclose(ora["o_full"][0], np.array(bf["o"]), atol=1e-12)
+
+
 # ------------------------------------------------------------ brute force ----------
 
 @pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
