@@ -34,7 +34,7 @@ class Params(ctypes.Structure):
 class Inputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q", "kv_raw", "va", "ga", "vb", "gb", "bias", "q_idx", "w_idx", "k_idx",
-                 "kv_c_out", "idx_out", "n_visible_out")]
+                 "kv_c_out", "idx_out", "n_visible_out", "sinks")]
 
 
 class CsaError(RuntimeError):
@@ -58,6 +58,7 @@ def _load():
         "csa_index_scores": [P, V, V, V, V, I64, I32, I32, V],
         "csa_index_topk": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
+        "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "hca_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "csa_debug_layout": [P, V, V, V, V],
@@ -85,7 +86,8 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_sparse_mqa_fwd", "csa_fwd",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_sparse_mqa_fwd",
+           "csa_sparse_mqa_fwd_sink", "csa_fwd",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
@@ -172,13 +174,18 @@ def index_topk(p: Params, q_idx, w_idx, k_idx, idx=None, n_visible=None, ws=None
     return idx, n_visible
 
 
-def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream=None):
+def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream=None, sinks=None):
+    """sinks: optional [H] fp32 softmax-sink logits (csa_sparse_mqa_fwd_sink)."""
     if o is None:
         o = torch.empty_like(q)
     if ws is None:
         ws = workspace(p, OP_SPARSE_MQA, q.device)
-    check(lib.csa_sparse_mqa_fwd(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx), _ptr(o),
-                                 _ptr(ws), ws.numel(), _stream(stream)))
+    if sinks is None:
+        check(lib.csa_sparse_mqa_fwd(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx), _ptr(o),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        check(lib.csa_sparse_mqa_fwd_sink(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx),
+                                          _ptr(sinks), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
     return o
 
 
@@ -187,7 +194,7 @@ def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=Non
     return Inputs(q=_ptr(g("q")), kv_raw=_ptr(g("kv_raw")), va=_ptr(g("va")), ga=_ptr(g("ga")),
                   vb=_ptr(g("vb")), gb=_ptr(g("gb")), bias=_ptr(g("bias")), q_idx=_ptr(g("q_idx")),
                   w_idx=_ptr(g("w_idx")), k_idx=_ptr(g("k_idx")), kv_c_out=_ptr(kv_c_out),
-                  idx_out=_ptr(idx_out), n_visible_out=_ptr(n_visible_out))
+                  idx_out=_ptr(idx_out), n_visible_out=_ptr(n_visible_out), sinks=_ptr(g("sinks")))
 
 
 def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None, idx_out=None,

@@ -194,6 +194,12 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const floa
 csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
                                 const void* kv_raw, const int32_t* idx, void* o, void* ws,
                                 size_t ws_bytes, void* stream) {
+  return csa_sparse_mqa_fwd_sink(p, q, kv_c, kv_raw, idx, nullptr, o, ws, ws_bytes, stream);
+}
+
+csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const void* kv_c,
+                                     const void* kv_raw, const int32_t* idx, const float* sinks,
+                                     void* o, void* ws, size_t ws_bytes, void* stream) {
   const bool window_only = kv_c == nullptr;
   CSA_TRY(validate_params(p, uint32_t(Need::MQA) | (idx ? uint32_t(Need::SELECT) : 0u), window_only));
   if (window_only && idx) {
@@ -206,6 +212,7 @@ csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void
   CSA_TRY(check_ptr(o, "o"));
   CSA_TRY(check_optional(kv_c, "kv_c"));
   CSA_TRY(check_optional(idx, "idx"));
+  CSA_TRY(check_optional(sinks, "sinks"));
   WsPlan plan;
   CSA_TRY(check_ws(p, CSA_OP_SPARSE_MQA, ws, ws_bytes, &plan));
   unsigned char* w = static_cast<unsigned char*>(ws);
@@ -213,7 +220,7 @@ csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void
   void* kv_w = w + plan.kv_w;
   CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
   const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
-  CSA_HIP(launch_sparse_mqa(*p, mode, q, kv_c, kv_w, idx, o, st), "attention launch");
+  CSA_HIP(launch_sparse_mqa(*p, mode, q, kv_c, kv_w, idx, sinks, o, st), "attention launch");
   return CSA_OK;
 }
 
@@ -238,6 +245,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
   CSA_TRY(check_optional(in->kv_c_out, "kv_c_out"));
   CSA_TRY(check_optional(in->idx_out, "idx_out"));
   CSA_TRY(check_optional(in->n_visible_out, "n_visible_out"));
+  CSA_TRY(check_optional(in->sinks, "sinks"));
   WsPlan plan;
   CSA_TRY(check_ws(p, csa_layer ? CSA_OP_CSA_FWD : CSA_OP_HCA_FWD, ws, ws_bytes, &plan));
   unsigned char* w = static_cast<unsigned char*>(ws);
@@ -262,7 +270,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
     int32_t* nvis = in->n_visible_out ? in->n_visible_out : reinterpret_cast<int32_t*>(w + plan.nvis);
     CSA_TRY(run_index_topk(p, in->q_idx, in->w_idx, in->k_idx, idx, nvis, w, plan, st, tr));
   }
-  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, o, st),
+  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, in->sinks, o, st),
           "attention launch");
   CSA_HIP(tr->mark(CSA_KERNEL_ATTENTION, st), "event record");
   return CSA_OK;

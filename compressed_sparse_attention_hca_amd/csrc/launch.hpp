@@ -26,8 +26,10 @@ hipError_t launch_index_topk(const csa_params_t& p, const void* q_idx, const flo
 hipError_t launch_topk(const csa_params_t& p, const float* scores, int64_t ld, int32_t t0,
                        int32_t nrows, int32_t* idx, int32_t* n_visible, hipStream_t st);
 
+// sinks [H] fp32 or nullptr: per-head softmax-sink logits.
 hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
-                             const void* kv_w, const int32_t* idx, void* o, hipStream_t st);
+                             const void* kv_w, const int32_t* idx, const float* sinks, void* o,
+                             hipStream_t st);
 
 hipError_t launch_debug_layout(const csa_params_t& p, int32_t* comp_pos, int32_t* n_visible,
                                int32_t* win_lo, hipStream_t st);

@@ -38,6 +38,7 @@ struct MqaArgs {
   const void* kv_c;
   const void* kv_w;
   const int32_t* idx;
+  const float* sinks;  // [H] softmax-sink logits, or nullptr
   void* o;
   int32_t B, S, H, R, ratio, window, topk, n_entries, mode;
   float scale_log2;  // softmax_scale * log2(e)
@@ -49,6 +50,7 @@ struct MqaArgs {
 __device__ __host__ constexpr int slot_key(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
 constexpr int MQA_MAX_TOPK = 2048;
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
@@ -341,6 +343,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   // ---- normalise, de-rotate at -P, stage through LDS, write o[b,t] coalesced
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  if (a.sinks) {  // the sink joins the denominator against the same reference
+    const int h = 16 * wave + hl;
+    if (h < a.H) l_run += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_ref);
+  }
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   {
     const int h = 16 * wave + hl;
@@ -436,6 +442,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
   float2* cs = reinterpret_cast<float2*>(xbuf);  // RoPE table outside the loop
   int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
+  float* sk = reinterpret_cast<float*>(xbuf + 14336);  // softmax-sink logits [H]
 
   // workgroup -> query: as sparse_mqa_kernel (32 consecutive queries per XCD visit)
   const int total = a.B * a.S;
@@ -534,8 +541,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
                       : bf16x8{};
     if (ntiles > 0) km0 = issue(0, sv0, st0);
     if (ntiles > 1) sv = load_idx(1);
+    if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = a.sinks[threadIdx.x];
   }
-  __syncthreads();  // the RoPE table is written; q and key tile 0 have landed
+  __syncthreads();  // the RoPE table and sinks are written; q and key tile 0 have landed
   // rotate q at +P where its dims fall in the last R
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -696,6 +704,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   xm[wave][lane] = l_run;
   __syncthreads();
   l_run = halves_sum(l_run + xm[wave ^ 1][lane]);
+  if (a.sinks && 32 * hg + l32 < a.H)  // the sink joins the denominator, same reference
+    l_run += __builtin_amdgcn_exp2f(sk[32 * hg + l32] * kLog2e - m_ref * a.scale_log2);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
   __syncthreads();
   rope_table();
@@ -760,12 +770,14 @@ static hipError_t launch_t(const MqaArgs& a, int D, int H, hipStream_t st) {
 }
 
 hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
-                             const void* kv_w, const int32_t* idx, void* o, hipStream_t st) {
+                             const void* kv_w, const int32_t* idx, const float* sinks, void* o,
+                             hipStream_t st) {
   MqaArgs a{};
   a.q = q;
   a.kv_c = kv_c;
   a.kv_w = kv_w;
   a.idx = idx;
+  a.sinks = sinks;
   a.o = o;
   a.B = p.B;
   a.S = p.S;
@@ -776,7 +788,7 @@ hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q,
   a.topk = p.topk;
   a.n_entries = mode == MQA_WINDOW_ONLY ? 0 : p.S / p.ratio;
   a.mode = mode;
-  a.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = p.softmax_scale * kLog2e;
   a.theta = p.rope_theta;
   a.pos0 = p.pos0;
   if (p.B * p.S == 0) return hipSuccess;

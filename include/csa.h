@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
   CSA_OK = 0,
@@ -99,7 +99,9 @@ typedef struct {
  * va ga vb gb [B,S,D], bias [span,D] fp32 (span = 2*ratio with overlap, else ratio),
  * q_idx [B,S,idx_heads,idx_dim], w_idx [B,S,idx_heads] fp32, k_idx [B,S/ratio,idx_dim].
  * The *_out pointers are optional (NULL = keep in workspace only): kv_c_out
- * [B,S/ratio,D], idx_out [B,S,topk], n_visible_out [B,S]. */
+ * [B,S/ratio,D], idx_out [B,S,topk], n_visible_out [B,S].
+ * sinks [H] fp32 is optional (NULL = no sink): one softmax-sink logit per head, shared
+ * by every batch and token, see csa_sparse_mqa_fwd_sink. */
 typedef struct {
   const void* q;
   const void* kv_raw;
@@ -114,6 +116,7 @@ typedef struct {
   void* kv_c_out;
   int32_t* idx_out;
   int32_t* n_visible_out;
+  const float* sinks;
 } csa_inputs_t;
 
 /* Stages 1-2: gated pooling, RMSNorm and RoPE at pos0 + s*ratio.
@@ -155,6 +158,17 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const floa
 csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
                                 const void* kv_raw, const int32_t* idx, void* o, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* Stage 4 with a softmax sink ("Enabling DeepSeek-V4-Flash Training on AMD Instinct
+ * MI355X GPUs with Primus", section "Kernel fusions", row "SWA / CSA / HCA attention":
+ * the attention kernel folds in the softmax sink; "fix(deepseek-v4): correct V4-Flash
+ * attention math", Part 1 item 6f: the sink is an FP32 logit that feeds the softmax).
+ *   sinks [H] fp32, or NULL for none: head h's softmax also normalises over the logit
+ *   sinks[h], which carries no value, so exp(sinks[h]) joins the denominator and a
+ *   query with no key gets o = 0.  Other arguments and errors as csa_sparse_mqa_fwd. */
+csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const void* kv_c,
+                                     const void* kv_raw, const int32_t* idx, const float* sinks,
+                                     void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Fused CSA layer (stages 1-4, overlap must be 1). */
 csa_status_t csa_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,

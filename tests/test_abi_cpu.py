@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 1
+    assert bd.lib.csa_abi_version() == 2
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -146,6 +146,11 @@ def test_sparse_mqa_rejects():
     assert call(p_c1(), q=None) == bd.CSA_ERR_INVALID_ARG
     assert call(p_c1(), kv_raw=A + 8) == bd.CSA_ERR_INVALID_ARG
     assert call(p_c1(), ws_bytes=100) == bd.CSA_ERR_WORKSPACE
+    def call_sink(p, sinks, ws_bytes=1 << 40):
+        return bd.lib.csa_sparse_mqa_fwd_sink(ctypes.byref(p), A, A, A, A, sinks, A, A, ws_bytes, None)
+    assert call_sink(p_c1(), A + 4) == bd.CSA_ERR_INVALID_ARG and "sinks" in bd.last_error()
+    assert call_sink(p_c1(H=0), A) == bd.CSA_ERR_INVALID_ARG
+    assert call_sink(p_c1(), A, ws_bytes=100) == bd.CSA_ERR_WORKSPACE
 
 
 def test_fused_rejects():

@@ -37,7 +37,7 @@ def gen(cfg):
 def run_layer(bd, cfg, inp):
     p = bd.params(cfg)
     if cfg.kind == "swa":  # window-only layer: the attention entry point without entries
-        o = bd.sparse_mqa_fwd(p, inp["q"], None, inp["kv_raw"])
+        o = bd.sparse_mqa_fwd(p, inp["q"], None, inp["kv_raw"], sinks=inp.get("sinks"))
         torch.cuda.synchronize()
         return o, None, None, None
     B, S, n = cfg.B, cfg.S, cfg.S // cfg.ratio
@@ -154,8 +154,14 @@ def test_topk_parity_chunked_path(bd):
 
 # ------------------------------------------------------------- whole layer ---------
 
-def layer_check(bd, cfg, rows=None):
+def layer_check(bd, cfg, rows=None, sinks=None):
+    """sinks: optional [H] fp32 numpy softmax-sink logits, passed to the layer and the
+    oracle alike."""
     inp = gen(cfg)
+    if sinks is not None:
+        sinks = np.asarray(sinks, dtype=np.float32)  # the values the kernel sees
+        inp["sinks"] = torch.from_numpy(sinks).to(DEV)
+        sinks = sinks.astype(np.float64)
     o, kv_c, idx, nv = run_layer(bd, cfg, inp)
     rows = rows if rows is not None else [(b, t) for b in range(cfg.B) for t in range(cfg.S)]
     lz = lazy_inputs(inp)
@@ -163,14 +169,14 @@ def layer_check(bd, cfg, rows=None):
     swaps = 0
     if cfg.kind == "csa":
         idx_np, nv_np = idx.cpu().numpy(), nv.cpu().numpy()
-        ora = O.layer_rows(cfg, lz, rows)
+        ora = O.layer_rows(cfg, lz, rows, sinks=sinks)
         sel_override = {}
         for (b, t) in rows:
             n = O.visible_entries(t, cfg.ratio)
             assert nv_np[b, t] == n
             swaps += check_selection(idx_np[b, t], n, cfg.topk, ora["scores"][(b, t)], ora["sel"][(b, t)])
             sel_override[(b, t)] = idx_np[b, t][:min(cfg.topk, n)]
-    ora = O.layer_rows(cfg, lz, rows, sel_override=sel_override)
+    ora = O.layer_rows(cfg, lz, rows, sel_override=sel_override, sinks=sinks)
     got = np.stack([o[b, t].float().cpu().double().numpy() for (b, t) in rows])
     want = np.stack([ora["o"][k] for k in rows])
     err, scale = assert_close_rel(got, want, tol(cfg), f"o {cfg.name}")
@@ -194,6 +200,37 @@ def test_layer_parity_C2_sampled(bd):
 
 def test_layer_parity_C3_sampled(bd):
     layer_check(bd, wl.C3, sample_rows(wl.C3, 24))
+
+
+SINK_CASES = {
+    "C0": (wl.C0, None),                                          # fp32 kernel, every row
+    "C1": (wl.C1, 48),                                            # bf16 head-group kernel
+    "hca": (wl.C2.replace(S=4096, name="hca_4096"), 24),
+    "swa": (wl.C1.replace(kind="swa", topk=0, S=1024, name="swa_1024"), 24),
+}
+
+
+@pytest.mark.parametrize("name", list(SINK_CASES))
+def test_sink_layer_parity(bd, name):
+    """Softmax sink (one fp32 logit per head joining each head's softmax with no value)
+    through csa_fwd, hca_fwd and the window-only entry point, against the oracle."""
+    cfg, n = SINK_CASES[name]
+    sinks = np.random.default_rng(17).normal(size=cfg.H) * 2.0
+    rows = None if n is None else sample_rows(cfg, n)
+    layer_check(bd, cfg, rows, sinks=sinks)
+
+
+def test_sink_with_no_keys_gives_zero(bd):
+    cfg = wl.LayerConfig(name="nokeys_sink", kind="hca", B=1, S=32, H=4, D=64, rope_dim=16, ratio=8,
+                         window=0, topk=0, dtype=wl.F32, seed=5)
+    inp = gen(cfg)
+    sinks = np.array([0.0, 1.5, -3.0, 40.0])
+    inp["sinks"] = torch.from_numpy(sinks.astype(np.float32)).to(DEV)
+    o, *_ = run_layer(bd, cfg, inp)
+    assert torch.all(o[0, :7] == 0)
+    ora = O.layer_rows(cfg, full_np(inp), [(0, t) for t in range(7, 32)], sinks=sinks)
+    got = np.stack([o[0, t].cpu().double().numpy() for t in range(7, 32)])
+    assert_close_rel(got, np.stack([ora["o"][(0, t)] for t in range(7, 32)]), 1e-5, "o")
 
 
 STACK = wl.stack_layers()  # 43 layers, B=4, S=8192: SWA, SWA, then CSA/HCA alternating
