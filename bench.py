@@ -184,6 +184,7 @@ def cpu_baseline(cfg, inp, budget_s: float):
         if k in inp:
             host[k] = {0: inp[k][0].to(torch.float32).cpu().double().numpy()}
     host["bias"] = inp["bias"].cpu().double().numpy()
+    sinks = inp["sinks"].cpu().double().numpy() if inp.get("sinks") is not None else None
     S = cfg.S
 
     class B0:  # batch-0 view with the shapes layer_rows indexes
@@ -211,7 +212,7 @@ def cpu_baseline(cfg, inp, budget_s: float):
             store.update({"q_idx": RowStore(inp["q_idx"], rows), "w_idx": RowStore(inp["w_idx"], rows),
                           "k_idx": B0(host["k_idx"])})
         t0 = time.perf_counter()
-        O.layer_rows(cfg, store, rows, kv_c=[kv_c])
+        O.layer_rows(cfg, store, rows, kv_c=[kv_c], sinks=sinks)
         t_rows += time.perf_counter() - t0
         sample += rows
         if t_comp + t_rows > budget_s:
@@ -298,6 +299,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4"],
                     help="C3 (default): the CSA layer at S=65536; C4: the 43-layer stack")
+    ap.add_argument("--sink", action="store_true",
+                    help="give every head a softmax-sink logit (seeded N(0, 2^2), fp32)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -337,6 +340,9 @@ def main():
     cfg = wl.CONFIGS[args.workload]
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = wl.make_inputs(cfg, dev)
+    if args.sink:
+        g = torch.Generator().manual_seed(17)
+        inp["sinks"] = (torch.randn(cfg.H, generator=g) * 2.0).to(dev)
     p = bd.params(cfg)
     op = bd.OP_CSA_FWD if cfg.kind == "csa" else bd.OP_HCA_FWD
     ws = bd.workspace(p, op, dev)
@@ -398,7 +404,8 @@ def main():
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
-                   "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim},
+                   "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
+                   "sink": bool(args.sink)},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": f["total"],
         "page_convention_attention_tflops": round(
