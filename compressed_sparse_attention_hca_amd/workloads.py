@@ -56,6 +56,7 @@ class LayerConfig:
     rms_eps: float = 1e-6
     pos0: int = 0
     norm_window: bool = False  # RMS-normalise window latents before rotation
+    index_prologue: bool = False  # indexer RoPE + Hadamard + temperature (CSA)
     seed: int = 0
 
     @property

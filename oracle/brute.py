@@ -12,6 +12,7 @@ with Primus", subsection "Three attention types, interleaved".
 from __future__ import annotations
 
 import math
+import struct
 
 
 def _rot_pair(x0, x1, P, i, R, theta):
@@ -26,6 +27,31 @@ def brute_rope(vec, P, R, theta):
     for i in range(R // 2):
         a = D - R + 2 * i
         out[a], out[a + 1] = _rot_pair(vec[a], vec[a + 1], P, i, R, theta)
+    return out
+
+
+def _round_scalar(x, dtype):
+    """Nearest value of the activation dtype, ties to even (struct for float32; for
+    bf16, 8 significant bits from frexp and Python's round-half-even)."""
+    if dtype == "f32":
+        return struct.unpack("f", struct.pack("f", x))[0]
+    m, e = math.frexp(x)
+    if e < -125:  # below the smallest normal: fixed spacing 2**-133
+        m, e = math.ldexp(m, e + 125), -125
+    return math.ldexp(round(m * 256.0), e - 8)
+
+
+def brute_index_prologue(vec, P, R, theta, dtype):
+    """RoPE at P, then (1/sqrt(n)) * sum_j (-1)^popcount(i & j) x_j for every i (the
+    Walsh form of the Sylvester Hadamard), rounded to the activation dtype."""
+    x = brute_rope(vec, P, R, theta)
+    n = len(x)
+    out = []
+    for i in range(n):
+        acc = 0.0
+        for j in range(n):
+            acc += -x[j] if bin(i & j).count("1") % 2 else x[j]
+        out.append(_round_scalar(acc / math.sqrt(n), dtype))
     return out
 
 
@@ -81,6 +107,13 @@ def brute_layer(cfg, inp, b=0, sinks=None):
         vis = [s for s in range(len(kv_c)) if (s + 1) * r - 1 <= t]
         if cfg.kind == "csa":
             qi, wi, ki = inp["q_idx"][b][t], inp["w_idx"][b][t], inp["k_idx"][b]
+            if getattr(cfg, "index_prologue", False):
+                qi = [brute_index_prologue([float(v) for v in qi[h]], pos0 + t, R, theta, cfg.dtype)
+                      for h in range(cfg.idx_heads)]
+                ki = [brute_index_prologue([float(v) for v in ki[s]], pos0 + s * r, R, theta, cfg.dtype)
+                      for s in range(len(ki))]
+                temp = 1.0 / math.sqrt(cfg.idx_heads * cfg.idx_dim)
+                wi = [float(wi[h]) * temp for h in range(cfg.idx_heads)]
             sc = []
             for s in vis:
                 tot = 0.0

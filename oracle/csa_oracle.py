@@ -29,6 +29,11 @@ Readings taken where the pages leave a step open (listed in the design doc as well):
     their own positions and not normalised (unless norm_window is set).
   * One softmax over the union of selected entries and window keys.
   * Top-k ties break to the smaller entry index.
+  * Indexer prologue (optional, index_prologue): the RoPE of the layer (same R and
+    theta, last R dims) on q_I at pos0 + t and on k_I at pos0 + s*r, then the
+    normalised Sylvester Hadamard over D_I, the result rounded to the activation dtype
+    (the tensor the scoring consumes); the per-head weights are scaled by
+    (H_I * D_I)**-0.5.
 """
 from __future__ import annotations
 
@@ -38,6 +43,7 @@ __all__ = [
     "rope_angles", "rope", "gated_pool", "rms_norm", "compress", "visible_entries",
     "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
+    "hadamard", "round_to", "index_prologue", "index_temperature",
 ]
 
 
@@ -141,6 +147,49 @@ def indexer_scores_row(q_i_t, w_t, k_i, n_vis: int) -> np.ndarray:
     return w_t @ np.maximum(dots, 0.0)
 
 
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), built by the doubling
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]].  Symmetric, with H H^T = n I."""
+    if n < 1 or n & (n - 1):
+        raise ValueError(f"Hadamard order {n} is not a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    """Round fp64 values to the activation dtype and return them as fp64: "f32" to the
+    nearest float32; "bf16" to the nearest value with 8 significant bits (ties to
+    even), with the fixed spacing 2**-133 below the smallest normal 2**-126."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    _, e = np.frexp(x)                      # x = m * 2**e with 0.5 <= |m| < 1
+    ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    return np.rint(x / ulp) * ulp
+
+
+def index_prologue(x, pos, rope_dim: int, theta: float, dtype: str) -> np.ndarray:
+    """Indexer prologue of one set of indexer vectors ([PR930] item 6e): the partial
+    RoPE at `pos` (queries at their own position, keys at s * ratio), then the
+    normalised Hadamard H / sqrt(D_I) over the whole vector, rounded to `dtype` (the
+    activation dtype of the tensor the bf16 scoring reads, [PR930] item 4).
+    x [..., D_I]; pos broadcasts against x.shape[:-1]."""
+    n = np.asarray(x).shape[-1]
+    y = rope(x, pos, rope_dim, theta)
+    y = y @ (hadamard(n) / np.sqrt(n))      # H is symmetric: row-vector form of H y
+    return round_to(y, dtype)
+
+
+def index_temperature(idx_heads: int, idx_dim: int) -> float:
+    """Score temperature folded into the per-head weights ([PR930] item 6a):
+    idx_heads**-0.5 * idx_dim**-0.5 (1/90.5 at 64 x 128)."""
+    return float(idx_heads) ** -0.5 * float(idx_dim) ** -0.5
+
+
 def indexer_scores(q_i, w, k_i, ratio: int) -> list:
     """Scores for every query, as a list of rows of length n_t."""
     S = q_i.shape[0]
@@ -209,6 +258,8 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
     workloads.make_inputs.  `sel_override` maps (b, t) to a selection to use instead
     of the oracle's own top-k (for re-evaluating on another admissible selection).
     `sinks` [H] (optional): per-head softmax sink logits (see attend_row).
+    With cfg.index_prologue set, the indexer reads index_prologue(q_I) at pos0 + t,
+    index_prologue(k_I) at pos0 + s*r and w * index_temperature (CSA only).
 
     Returns a dict: o {(b,t): [H,D]}, sel {(b,t): indices}, scores {(b,t): row},
     n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, and P when
@@ -238,6 +289,20 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
             out["kv_c"][b] = kvb
         kv_raw_b = inp["kv_raw"][b]
         ts = [t for bb, t in rows if bb == b]
+        prologue = kind == "csa" and bool(getattr(cfg, "index_prologue", False))
+        if kind == "csa":
+            k_i_b = _as64(inp["k_idx"][b])
+            if prologue:
+                k_pos = pos0 + np.arange(k_i_b.shape[0], dtype=np.int64) * cfg.ratio
+                k_i_b = index_prologue(k_i_b, k_pos, R, theta, cfg.dtype)
+
+        def index_row(t, n_vis):
+            q_i, w_i = _as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t])
+            if prologue:
+                q_i = index_prologue(q_i, pos0 + t, R, theta, cfg.dtype)
+                w_i = w_i * index_temperature(cfg.idx_heads, cfg.idx_dim)
+            return indexer_scores_row(q_i, w_i, k_i_b, n_vis)
+
         for t in ts:
             lo, hi = window_bounds(t, cfg.window)
             win_keys = rotate_window(_as64(kv_raw_b[lo:hi + 1]), R, theta, eps, pos0 + lo, norm_window)
@@ -249,12 +314,9 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
                 if sel_override is not None and (b, t) in sel_override:
                     sel = np.sort(np.asarray(sel_override[(b, t)], dtype=np.int64))
                     if kind == "csa":
-                        out["scores"][(b, t)] = indexer_scores_row(
-                            _as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t]),
-                            _as64(inp["k_idx"][b]), n_vis)
+                        out["scores"][(b, t)] = index_row(t, n_vis)
                 elif kind == "csa":
-                    sc = indexer_scores_row(_as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t]),
-                                            _as64(inp["k_idx"][b]), n_vis)
+                    sc = index_row(t, n_vis)
                     out["scores"][(b, t)] = sc
                     sel = topk_row(sc, cfg.topk)
                 else:

@@ -384,3 +384,138 @@ def test_keys_per_query_matches_pages():
     assert wl.keys_per_query(c1, 4095) == 640
     hca_1m = wl.C2.replace(S=1_000_448)
     assert abs(wl.keys_per_query(hca_1m, hca_1m.S - 1) - 7900) < 100
+
+
+# ---------------------------------------------------- indexer prologue ----------
+# "fix(deepseek-v4): correct V4-Flash attention math", Part 1 items 6a (temperature
+# folded into the head weights) and 6e (partial RoPE at the compressed base, queries at
+# t and keys at s*ratio, then a normalised Hadamard, indexer only).
+
+def popcount(x):
+    return bin(x).count("1")
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_is_the_walsh_matrix_and_orthogonal(n):
+    """Sylvester's matrix has entry (-1)^popcount(i & j); H H^T = n I exactly in fp64
+    (the pages' test list pins the Hadamard's orthogonality in float64); and it is the
+    matrix scipy builds."""
+    import scipy.linalg
+    H = O.hadamard(n)
+    walsh = np.array([[(-1.0) ** popcount(i & j) for j in range(n)] for i in range(n)])
+    assert np.array_equal(H, walsh)
+    assert np.array_equal(H @ H.T, n * np.eye(n))
+    assert np.array_equal(H, scipy.linalg.hadamard(n).astype(np.float64))
+
+
+def test_round_to_matches_torch_casts_and_ties_to_even(rng):
+    """For values that are exactly fp32, rounding to bf16 is torch's fp32 -> bf16 cast
+    (round to nearest even), subnormals included; fp32 rounding is numpy's cast."""
+    x32 = np.concatenate([rng.normal(size=4000) * 10.0 ** rng.integers(-6, 6, size=4000),
+                          rng.normal(size=200) * 1e-39, [0.0, -0.0, 1.0, -2.5]]).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to(x32.astype(np.float64), "bf16"), want)
+    # ties go to the even neighbour: 1 + 2^-8 -> 1; 1 + 3 * 2^-8 -> 1 + 2^-6
+    got = O.round_to(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)]), "bf16")
+    assert list(got) == [1.0, 1 + 2.0 ** -6, -1.0]
+    x = rng.normal(size=100)
+    assert np.array_equal(O.round_to(x, "f32"), x.astype(np.float32).astype(np.float64))
+
+
+def test_index_temperature_constant():
+    """At Flash widths (64 heads x 128) the temperature is a factor of about 90.5."""
+    assert abs(1.0 / O.index_temperature(64, 128) - 90.5) < 0.05
+    assert O.index_temperature(4, 16) == 0.125
+
+
+@pytest.mark.parametrize("P", [0, 37, 65535, 1_000_003])
+def test_index_prologue_unit_pair_closed_form(P):
+    """A unit pair (1, 0) on the last rope pair becomes (cos phi, sin phi) with
+    phi = P * theta^-(R-2)/R, and the normalised Hadamard then gives every component i
+    the value (cos phi (-1)^popcount(i & (n-2)) + sin phi (-1)^popcount(i & (n-1))) /
+    sqrt(n).  A component outside the rope dims is not rotated: a unit vector on dim 0
+    becomes the constant 1/sqrt(n)."""
+    n, R, theta = 16, 8, 40000.0
+    x = np.zeros(n)
+    x[n - 2] = 1.0
+    phi = P * theta ** (-(R - 2) / R)
+    y = O.index_prologue(x, P, R, theta, "f32")
+    for i in range(n):
+        want = (math.cos(phi) * (-1) ** popcount(i & (n - 2)) + math.sin(phi) * (-1) ** popcount(i & (n - 1))) / 4
+        assert abs(y[i] - want) < 1e-7
+    e0 = np.zeros(n)
+    e0[0] = 1.0
+    assert np.allclose(O.index_prologue(e0, P, R, theta, "f32"), 0.25, atol=1e-12)
+    yb = O.index_prologue(x, P, R, theta, "bf16")
+    assert np.array_equal(O.round_to(yb, "bf16"), yb)        # bf16-representable
+    assert np.abs(yb - y).max() < 2.0 ** -9                  # and the nearest such value
+
+
+def prologue_cfg(**kw):
+    base = dict(idx_dim=16, rope_dim=8, idx_heads=3, index_prologue=True)
+    base.update(kw)
+    return tiny("csa", **base)
+
+
+@pytest.mark.parametrize("pos0", [0, 1000])
+def test_prologue_scores_follow_relative_position(pos0):
+    """Unit pairs on the last rope pair of every q_I head and every k_I entry, w = 1:
+    the Hadamard keeps inner products, so I[t,s] = H_I * T * ReLU(cos((t - s*r) f)),
+    with T = (H_I * D_I)^-1/2 and f = theta^-(R-2)/R, for any pos0."""
+    cfg = prologue_cfg(S=64, pos0=pos0, topk=64)
+    inp = to_np(wl.make_inputs(cfg))
+    n = cfg.idx_dim
+    inp["q_idx"][:] = 0.0
+    inp["q_idx"][..., n - 2] = 1.0
+    inp["k_idx"][:] = 0.0
+    inp["k_idx"][..., n - 2] = 1.0
+    inp["w_idx"][:] = 1.0
+    f = cfg.rope_theta ** (-(cfg.rope_dim - 2) / cfg.rope_dim)
+    T = (cfg.idx_heads * cfg.idx_dim) ** -0.5
+    rows = [(0, t) for t in (3, 17, 40, 63)]
+    r = O.layer_rows(cfg, inp, rows)
+    for (_, t) in rows:
+        sc = r["scores"][(0, t)]
+        want = [cfg.idx_heads * T * max(0.0, math.cos((t - s * cfg.ratio) * f)) for s in range(len(sc))]
+        assert np.allclose(sc, want, atol=1e-6)
+
+
+def test_prologue_pos0_shift_keeps_scores():
+    """Queries and keys move together under a pos0 shift, so the scores keep their
+    values up to the fp32 rounding of the rotated vectors."""
+    cfg = prologue_cfg(S=48)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(3, 48, 4)]
+    a = O.layer_rows(cfg, inp, rows)
+    b = O.layer_rows(cfg.replace(pos0=4 * 12345), inp, rows)
+    for k in rows:
+        assert np.allclose(a["scores"][k], b["scores"][k], rtol=1e-5, atol=1e-6)
+
+
+def test_prologue_changes_scores_but_temperature_alone_does_not_change_selection():
+    """Without RoPE (R = 0) the rotated scores are the plain scores times the
+    temperature, up to the rounding of the Hadamard outputs; the selection then agrees
+    except at near-ties.  With RoPE the scores change."""
+    cfg0 = prologue_cfg(S=64, index_prologue=False, topk=5)
+    inp = to_np(wl.make_inputs(cfg0))
+    rows = [(0, t) for t in range(7, 64, 8)]
+    plain = O.layer_rows(cfg0, inp, rows)
+    T = (cfg0.idx_heads * cfg0.idx_dim) ** -0.5
+    # rope_dim 0 leaves only the Hadamard and the temperature (main layer keys unrotated too)
+    nr = O.layer_rows(cfg0.replace(index_prologue=True, rope_dim=0), inp, rows)
+    for k in rows:
+        assert np.allclose(nr["scores"][k], T * plain["scores"][k], rtol=1e-5, atol=1e-6)
+    wr = O.layer_rows(cfg0.replace(index_prologue=True), inp, rows)
+    assert max(np.abs(wr["scores"][k] - T * plain["scores"][k]).max() for k in rows) > 1e-2
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_prologue_oracle_matches_brute_force(dtype):
+    cfg = prologue_cfg(S=24, pos0=7, dtype=dtype)
+    inp = to_np(wl.make_inputs(cfg))
+    ora = O.layer_forward(cfg, inp)
+    bf = brute.brute_layer(cfg, inp)
+    for t in range(cfg.S):
+        assert np.allclose(ora["scores"][(0, t)], bf["scores"][t], atol=1e-12)
+        assert list(ora["sel"][(0, t)]) == bf["sel"][t]
+    assert np.allclose(ora["o_full"][0], np.array(bf["o"]), atol=1e-12)
