@@ -54,6 +54,8 @@ def kernel_work(cfg, wl):
         work["indexer"] = (f["indexer"], "flops", "mfma")
         # fused indexer + selection: the indexer's FLOPs (the selection reads no scores)
         work["index_topk"] = (f["indexer"], "flops", "mfma")
+        # indexer key prologue: read and write every indexer key once
+        work["index_keys"] = (2 * B * (S // cfg.ratio) * cfg.idx_dim * es, "bytes", "hbm")
         # read every visible score once, write K indices + n_visible per row
         work["topk"] = (4 * f["visible_pairs"] + B * S * (4 * cfg.topk + 4), "bytes", "hbm")
     return work
@@ -301,6 +303,8 @@ def main():
                     help="C3 (default): the CSA layer at S=65536; C4: the 43-layer stack")
     ap.add_argument("--sink", action="store_true",
                     help="give every head a softmax-sink logit (seeded N(0, 2^2), fp32)")
+    ap.add_argument("--index-prologue", action="store_true",
+                    help="CSA: indexer prologue on (RoPE + Hadamard of q_I and k_I, temperature on w)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -338,6 +342,8 @@ def main():
         print(json.dumps(run_stack(args, dev)), flush=True)
         return
     cfg = wl.CONFIGS[args.workload]
+    if args.index_prologue:
+        cfg = cfg.replace(index_prologue=True)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = wl.make_inputs(cfg, dev)
     if args.sink:
@@ -405,7 +411,7 @@ def main():
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
                    "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
-                   "sink": bool(args.sink)},
+                   "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue)},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": f["total"],
         "page_convention_attention_tflops": round(

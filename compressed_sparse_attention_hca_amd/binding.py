@@ -21,6 +21,7 @@ CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED, CSA_ERR_HIP
 CSA_F32, CSA_BF16 = 0, 1
 OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_CSA_FWD, OP_HCA_FWD = range(5)
 FLAG_NORM_WINDOW = 1
+FLAG_INDEX_PROLOGUE = 2
 
 
 class Params(ctypes.Structure):
@@ -57,6 +58,7 @@ def _load():
         "csa_compress": [P, V, V, V, V, V, V, V],
         "csa_index_scores": [P, V, V, V, V, I64, I32, I32, V],
         "csa_index_topk": [P, V, V, V, V, V, V, SZ, V],
+        "csa_index_prologue_keys": [P, V, V, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
@@ -86,14 +88,15 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_sparse_mqa_fwd",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_prologue_keys",
+           "csa_sparse_mqa_fwd",
            "csa_sparse_mqa_fwd_sink", "csa_fwd",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
 
 KERNEL_NAMES = {0: "compress", 1: "window_rope", 2: "indexer", 3: "topk", 4: "attention",
-                5: "index_topk"}
+                5: "index_topk", 6: "index_keys"}
 
 
 def last_error() -> str:
@@ -112,7 +115,8 @@ def params(cfg: wl.LayerConfig, **over) -> Params:
                idx_heads=cfg.idx_heads, idx_dim=cfg.idx_dim,
                dtype=CSA_BF16 if cfg.dtype == wl.BF16 else CSA_F32,
                rope_theta=cfg.rope_theta, rms_eps=cfg.rms_eps, softmax_scale=cfg.softmax_scale,
-               pos0=cfg.pos0, flags=FLAG_NORM_WINDOW if cfg.norm_window else 0)
+               pos0=cfg.pos0, flags=(FLAG_NORM_WINDOW if cfg.norm_window else 0)
+               | (FLAG_INDEX_PROLOGUE if cfg.index_prologue else 0))
     for k, v in over.items():
         setattr(p, k, v)
     return p
@@ -159,6 +163,15 @@ def index_scores(p: Params, q_idx, w_idx, k_idx, t0=0, nrows=None, scores=None, 
     check(lib.csa_index_scores(ctypes.byref(p), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(scores),
                                scores.shape[-1], t0, nrows, _stream(stream)))
     return scores
+
+
+def index_prologue_keys(p: Params, k_idx, k_out=None, stream=None) -> torch.Tensor:
+    """csa_index_prologue_keys: the indexer keys rotated at pos0 + s*ratio and passed
+    through the normalised Hadamard, in the activation dtype."""
+    if k_out is None:
+        k_out = torch.empty_like(k_idx)
+    check(lib.csa_index_prologue_keys(ctypes.byref(p), _ptr(k_idx), _ptr(k_out), _stream(stream)))
+    return k_out
 
 
 def index_topk(p: Params, q_idx, w_idx, k_idx, idx=None, n_visible=None, ws=None, stream=None):

@@ -49,9 +49,12 @@ int32_t n_chunks(const WsPlan& plan, int32_t S) {
   return plan.chunk_rows > 0 ? (S + plan.chunk_rows - 1) / plan.chunk_rows : 0;
 }
 
-// Kernel launches of the indexer/top-k stage: one fused launch, or two per chunk.
+bool index_prologue(const csa_params_t& p) { return (p.flags & CSA_FLAG_INDEX_PROLOGUE) != 0; }
+
+// Kernel launches of the indexer/top-k stage: the key prologue (with the flag), then
+// one fused launch, or two per chunk.
 int32_t index_launches(const csa_params_t& p, const WsPlan& plan) {
-  return p.topk <= kFusedTopkMax ? 1 : 2 * n_chunks(plan, p.S);
+  return (index_prologue(p) ? 1 : 0) + (p.topk <= kFusedTopkMax ? 1 : 2 * n_chunks(plan, p.S));
 }
 
 csa_status_t check_ws(const csa_params_t* p, int32_t op, void* ws, size_t ws_bytes, WsPlan* plan) {
@@ -70,6 +73,12 @@ csa_status_t run_index_topk(const csa_params_t* p, const void* q_idx, const floa
                             const WsPlan& plan, hipStream_t st, Tracer* tr = nullptr) {
   Tracer none;
   if (!tr) tr = &none;
+  if (index_prologue(*p)) {  // rotated keys into the workspace; queries rotate in-kernel
+    void* k_rot = ws + plan.k_rot;
+    CSA_HIP(launch_index_keys(*p, k_idx, k_rot, st), "indexer key prologue launch");
+    CSA_HIP(tr->mark(CSA_KERNEL_INDEX_KEYS, st), "event record");
+    k_idx = k_rot;
+  }
   if (p->topk <= kFusedTopkMax) {
     CSA_HIP(launch_index_topk(*p, q_idx, w_idx, k_idx, idx, nvis, st), "indexer/top-k launch");
     CSA_HIP(tr->mark(CSA_KERNEL_INDEX_TOPK, st), "event record");
@@ -174,6 +183,23 @@ csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const fl
   CSA_TRY(check_ptr(scores, "scores"));
   CSA_HIP(launch_index_scores(*p, q_idx, w_idx, k_idx, scores, ld, t0, nrows, as_stream(stream)),
           "indexer launch");
+  return CSA_OK;
+}
+
+csa_status_t csa_index_prologue_keys(const csa_params_t* p, const void* k_idx, void* k_out,
+                                     void* stream) {
+  CSA_TRY(validate_params(p, uint32_t(Need::INDEX_KEYS), false));
+  if (empty(p)) return CSA_OK;
+  CSA_TRY(check_ptr(k_idx, "k_idx"));
+  CSA_TRY(check_ptr(k_out, "k_out"));
+  const size_t bytes = (size_t)p->B * (size_t)(p->S / p->ratio) * (size_t)p->idx_dim *
+                       (p->dtype == CSA_BF16 ? 2 : 4);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(k_idx), b = reinterpret_cast<uintptr_t>(k_out);
+  if (a < b + bytes && b < a + bytes) {
+    set_error("k_out overlaps k_idx");
+    return CSA_ERR_INVALID_ARG;
+  }
+  CSA_HIP(launch_index_keys(*p, k_idx, k_out, as_stream(stream)), "indexer key prologue launch");
   return CSA_OK;
 }
 

@@ -22,6 +22,25 @@ constexpr int IDX_TILE = 64;      // entries per LDS tile
 constexpr int IDX_CHUNK = 1024;   // entries per workgroup
 constexpr int IDX_MAX_CHUNKS = 64;
 
+// The indexer prologue's parameters ("fix(deepseek-v4): correct V4-Flash attention
+// math", Part 1 items 6a and 6e).  on = 0: plain scores (w_scale = 1 exactly).
+struct IndexPrologue {
+  double theta;     // RoPE base
+  int64_t pos0;     // position of token 0
+  int32_t on;       // rotate the queries (the keys arrive rotated)
+  int32_t rope_dim; // rotated dims: the last rope_dim of the indexer dims
+  float w_scale;    // (idx_heads * idx_dim)^-1/2 with the prologue, else 1
+};
+
+__host__ inline IndexPrologue index_prologue_args(const csa_params_t& p) {
+  IndexPrologue r{p.rope_theta, p.pos0, 0, p.rope_dim, 1.0f};
+  if (p.flags & CSA_FLAG_INDEX_PROLOGUE) {
+    r.on = 1;
+    r.w_scale = (float)(1.0 / sqrt((double)p.idx_heads * (double)p.idx_dim));
+  }
+  return r;
+}
+
 struct IndexArgs {
   const void* q_idx;
   const float* w_idx;
@@ -30,6 +49,7 @@ struct IndexArgs {
   int64_t ld;
   int32_t B, S, HI, ratio, n_entries, t0, nrows, qblocks;  // qblocks per batch
   int32_t n_chunks;
+  IndexPrologue pro;
   int32_t chunk_wg_off[IDX_MAX_CHUNKS + 1];  // prefix sums of workgroups per chunk
   int32_t chunk_qb_min[IDX_MAX_CHUNKS];      // first query block that needs the chunk
 };
@@ -54,13 +74,138 @@ __device__ inline f32x16 mfma32x32x16(const Frag<float>& a, const Frag<float>& b
   return c;
 }
 
+// A pointer the wave holds in every lane, moved to scalar registers (a global_load_lds
+// base operand).  readfirstlane works on 32-bit ints: each half is widened as an
+// unsigned value, so a low half with bit 31 set is not sign-extended into the high one.
+__device__ inline const float* wave_uniform(const float* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const float*)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// Two neighbouring fragment elements as fp32, and back (round to nearest even): bf16
+// pairs are one 32-bit word, unpacked with a shift and a mask and packed with one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ inline void frag_get2(const Frag<float>& f, int i, float& a, float& b) {
+  a = f.v[i];
+  b = f.v[i + 1];
+}
+__device__ inline void frag_get2(const Frag<bf16>& f, int i, float& a, float& b) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(f.v)[i >> 1];
+  a = __uint_as_float(w << 16);
+  b = __uint_as_float(w & 0xffff0000u);
+}
+__device__ inline void frag_set2(Frag<float>& f, int i, float a, float b) {
+  f.v[i] = a;
+  f.v[i + 1] = b;
+}
+__device__ inline void frag_set2(Frag<bf16>& f, int i, float a, float b) {
+  reinterpret_cast<uint32_t*>(f.v)[i >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Indexer prologue of one wave's query, on its A fragments in registers: RoPE on the
+// last R of the DI dims at position P, then the normalised Sylvester Hadamard
+// Hn = H / sqrt(DI), H[i][j] = (-1)^popcount(i & j) ("fix(deepseek-v4): correct
+// V4-Flash attention math", Part 1 item 6e), in fp32 and rounded once to T.  Lane
+// (g, l32) holds dims 16*ks + 8*g + i (i = 0..7) of head hb*32 + l32, so the Hadamard's
+// dim bits 0-2 are within a fragment, bits 4.. index the fragments and bit 3 is the
+// lane half.
+//   * The rotation of pair (x0, x1) by (c, s), the butterfly of dim bit 0 and the
+//     1/sqrt(DI) scale fold into h0 = x0 a + x1 b, h1 = x0 b - x1 a with
+//     a = (c + s) / sqrt(DI), b = (c - s) / sqrt(DI) (c = 1, s = 0 outside the rope
+//     dims).  `tab` is DI words of this wave's LDS: lane q writes (a, b) of dim pair q
+//     and every lane reads the four pairs of a fragment with two 16-byte loads.
+//   * Dim bit 3 goes last, two registers at a time through v_permlane32_swap (a swap
+//     between the lane halves, no trip through the LDS crossbar): swapping (u, v) puts
+//     both halves of u in the lower lanes and both halves of v in the upper lanes, one
+//     add and one subtract make the butterfly, and a second swap puts them back.
+// Every lane of the wave must call it.
 template <typename T, int DI>
+__device__ void index_query_prologue(Frag<T> (&qa)[2][DI / 16], int64_t P, int R, double theta,
+                                     uint32_t* tab) {
+  constexpr int KS = DI / 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int lo = DI - R;  // first rotated dim
+  if (lane < DI / 2) {
+    float c = 1.f, sn = 0.f;
+    if (2 * lane >= lo) rope_cos_sin(P, rope_inv_freq((2 * lane - lo) >> 1, R, theta), &c, &sn);
+    const float scale = 1.0f / __builtin_sqrtf((float)DI);
+    CSA_LDS uint32_t* tp = (CSA_LDS uint32_t*)tab + 2 * lane;
+    tp[0] = __float_as_uint((c + sn) * scale);
+    tp[1] = __float_as_uint((c - sn) * scale);
+  }
+  // the wave's own LDS writes are seen by its later reads (in-order LDS queue)
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    __builtin_amdgcn_sched_barrier(0);  // one head block's vector live at a time
+    float x[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // pairs 8ks + 4g .. +3: (a, b) interleaved, 32 bytes
+      const CSA_LDS u32x4* tp = (const CSA_LDS u32x4*)((CSA_LDS uint32_t*)tab + 2 * (8 * ks + 4 * g));
+      const u32x4 t0 = tp[0], t1 = tp[1];
+      const float ca[4] = {__uint_as_float(t0[0]), __uint_as_float(t0[2]), __uint_as_float(t1[0]), __uint_as_float(t1[2])};
+      const float cb[4] = {__uint_as_float(t0[1]), __uint_as_float(t0[3]), __uint_as_float(t1[1]), __uint_as_float(t1[3])};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x0, x1;
+        frag_get2(qa[hb][ks], 2 * j, x0, x1);
+        x[ks][2 * j] = fmaf(x0, ca[j], x1 * cb[j]);
+        x[ks][2 * j + 1] = fmaf(x0, cb[j], -(x1 * ca[j]));
+      }
+    }
+    // dim bits 1-2: within a fragment
+#pragma unroll
+    for (int m = 2; m < 8; m <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (!(i & m)) {
+            const float u = x[ks][i], v = x[ks][i | m];
+            x[ks][i] = u + v;
+            x[ks][i | m] = u - v;
+          }
+    // dim bits 4..: across fragments
+#pragma unroll
+    for (int m = 1; m < KS; m <<= 1)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        if (!(ks & m)) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float u = x[ks][i], v = x[ks | m][i];
+            x[ks][i] = u + v;
+            x[ks | m][i] = u - v;
+          }
+        }
+    // dim bit 3, registers i and i+1 of each fragment as one swap pair
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[ks][i]), __float_as_uint(x[ks][i + 1]),
+                                                        false, false);
+        const float lo_v = __uint_as_float(r[0]), hi_v = __uint_as_float(r[1]);
+        const auto back = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo_v + hi_v),
+                                                           __float_as_uint(lo_v - hi_v), false, false);
+        frag_set2(qa[hb][ks], i, __uint_as_float(back[0]), __uint_as_float(back[1]));
+      }
+  }
+}
+
+template <typename T, int DI, bool PRO>
 __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs a) {
   constexpr int KS = DI / 16;                    // k-steps of 16
   constexpr int VEC = 16 / sizeof(T);            // elements per 16-byte load
   constexpr int ROW = DI + 16 / sizeof(T);       // padded LDS row (elements)
   constexpr int HB = 2;                          // head blocks of 32 (up to 64 heads)
   __shared__ __attribute__((aligned(16))) T tile[2][IDX_TILE * ROW];
+  __shared__ __attribute__((aligned(16))) uint32_t pro_tab[PRO ? IDX_WAVES : 1][PRO ? DI : 1];
 
   // workgroup -> (chunk, batch, query block)
   const int wg = blockIdx.x;
@@ -101,13 +246,22 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
         for (int i = 0; i < 8; ++i) qa[hb][ks].v[i] = from_f32<T>(0.f);
       }
     }
+  }
+  // (a.pro.on is always set in the PRO instance; the runtime test keeps the compiler
+  // from folding the fragment loads into the prologue, which needs 40-140 more VGPRs)
+  if constexpr (PRO)
+    if (a.pro.on) index_query_prologue<T, DI>(qa, a.pro.pos0 + t, a.pro.rope_dim, a.pro.theta, pro_tab[wave]);
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
     // accumulator element 4j+i is head hb*32 + 8j + 4g + i
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = hb * 32 + 8 * j + 4 * g + i;
-        w[hb][4 * j + i] = (q_ok && hh < a.HI) ? a.w_idx[((int64_t)b * a.S + t) * a.HI + hh] : 0.f;
+        float wv = (q_ok && hh < a.HI) ? a.w_idx[((int64_t)b * a.S + t) * a.HI + hh] : 0.f;
+        if constexpr (PRO) wv *= a.pro.w_scale;
+        w[hb][4 * j + i] = wv;
       }
   }
 
@@ -229,6 +383,7 @@ struct IndexTopkArgs {
   int32_t* idx;
   int32_t* n_visible;
   int32_t B, S, HI, ratio, n_entries, topk, qblocks;  // query blocks per batch
+  IndexPrologue pro;
 };
 
 // Order-preserving key of a score: negative floats have every bit flipped, the others
@@ -420,7 +575,7 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
   return r;
 }
 
-template <typename T, int DI>
+template <typename T, int DI, bool PRO>
 __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs a) {
   using SH = FtShape<T, DI>;
   constexpr int KS = DI / 16;
@@ -465,14 +620,28 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
         for (int i = 0; i < 8; ++i) qa[hb][ks].v[i] = from_f32<T>(0.f);
       }
     }
-    // accumulator element 4j+i is head hb*32 + 8j + 4g + i
+  }
+  if constexpr (!PRO) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int hb = 0; hb < HB; ++hb) {
+      // accumulator element 4j+i is head hb*32 + 8j + 4g + i
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = hb * 32 + 8 * j + 4 * g + i;
-        w[hb][4 * j + i] = (q_ok && hh < a.HI) ? a.w_idx[((int64_t)b * a.S + t) * a.HI + hh] : 0.f;
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hh = hb * 32 + 8 * j + 4 * g + i;
+          w[hb][4 * j + i] = (q_ok && hh < a.HI) ? a.w_idx[((int64_t)b * a.S + t) * a.HI + hh] : 0.f;
+        }
+    }
+  } else {
+    // With the prologue the head weights go straight to LDS (this wave's index
+    // buffer, unused until the first tile): their latency overlaps the q loads and no
+    // register holds them while the prologue runs.  Lane l copies w[h = min(l, HI-1)];
+    // heads past HI are zeroed when read back.
+    const float* wrow = wave_uniform(a.w_idx + ((int64_t)b * a.S + min(t, a.S - 1)) * a.HI);
+    const uint32_t voff = (uint32_t)min(lane, a.HI - 1) * 4u;
+    const uint32_t lds = (uint32_t)(uintptr_t)(CSA_LDS int*)cidx[wave];
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(wrow), "{m0}"(lds) : "memory");
   }
 
   // Stage layout: row r at r * ROWP, chunk c of the row at slot r * SPR + c; the DMA
@@ -568,9 +737,26 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   };
 
   const int ntiles = (n_blk + FT_TILE - 1) / FT_TILE;
-  wait_vmcnt<0, false>();  // q and w are in registers before any copy is counted
+  wait_vmcnt<0, false>();  // q and w have arrived before any copy is counted
   if (ntiles > 0) issue(0, st0);
   if (ntiles > 1) issue(1, st1);
+  if constexpr (PRO) {
+    // the prologue runs while the first two tiles are in flight.  (a.pro.on is
+    // always set in this instance; the runtime test keeps the compiler from folding
+    // the fragment loads into the prologue, which takes 40-140 more VGPRs.)
+    if (a.pro.on) index_query_prologue<T, DI>(qa, a.pro.pos0 + t, a.pro.rope_dim, a.pro.theta, ckey[wave]);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = *(const CSA_LDS f32x4*)((CSA_LDS int*)cidx[wave] + hb * 32 + 8 * j + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hh = hb * 32 + 8 * j + 4 * g + i;
+          w[hb][4 * j + i] = (q_ok && hh < a.HI) ? v[i] * a.pro.w_scale : 0.f;
+        }
+      }
+  }
 
   // Prune when fewer than `need` + 1 slots are free (each epilogue admits up to 32
   // keys and may write one spare slot past them), or, with `early`, once the buffer
@@ -643,14 +829,91 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   for (int j = lane; j < K; j += 64) out[j] = my_idx[j];
 }
 
+// ---------------------------------------------------------------------------------
+// Indexer key prologue: k'[s] = round(Hn RoPE(k_I[s], pos0 + s*ratio)), the keys'
+// half of the prologue ("fix(deepseek-v4): correct V4-Flash attention math", Part 1
+// item 6e: keys rotate at s * compress_ratio).  DI/2 lanes per row, each holding the
+// pair of dims (2j, 2j+1): the Hadamard's dim bit 0 is within the lane and bits 1..
+// are lane bits of the row's group, exchanged by shuffles.  Streaming, HBM-bound.
+// ---------------------------------------------------------------------------------
+struct IndexKeysArgs {
+  const void* k_idx;
+  void* k_out;
+  int64_t rows;      // B * n_entries
+  int32_t n_entries, ratio;
+  IndexPrologue pro;
+};
+
+constexpr int IK_THREADS = 256;
+
+template <typename T, int DI>
+__global__ __launch_bounds__(IK_THREADS) void index_keys_kernel(IndexKeysArgs a) {
+  constexpr int LPR = DI / 2;  // lanes per row (divides 64)
+  const int64_t gid = (int64_t)blockIdx.x * IK_THREADS + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int j = (int)(gid % LPR);
+  const bool ok = row < a.rows;
+  float x0 = 0.f, x1 = 0.f;
+  const T* src = static_cast<const T*>(a.k_idx) + row * DI + 2 * j;
+  if (ok) {
+    x0 = to_f32(src[0]);
+    x1 = to_f32(src[1]);
+  }
+  const int R = a.pro.rope_dim;
+  const int lo = DI - R;
+  if (ok && 2 * j >= lo) {
+    const int s = (int)(row % a.n_entries);
+    float c, sn;
+    rope_cos_sin(entry_position(a.pro.pos0, s, a.ratio), rope_inv_freq((2 * j - lo) >> 1, R, a.pro.theta), &c, &sn);
+    const float r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
+    x0 = r0;
+    x1 = r1;
+  }
+  float h0 = x0 + x1, h1 = x0 - x1;  // dim bit 0
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {  // dim bit k = lane bit k-1
+    const float sg = (j & m) ? -1.f : 1.f;
+    h0 = fmaf(sg, h0, __shfl_xor(h0, m, 64));
+    h1 = fmaf(sg, h1, __shfl_xor(h1, m, 64));
+  }
+  if (ok) {
+    const float scale = 1.0f / __builtin_sqrtf((float)DI);
+    T* dst = static_cast<T*>(a.k_out) + row * DI + 2 * j;
+    dst[0] = from_f32<T>(h0 * scale);
+    dst[1] = from_f32<T>(h1 * scale);
+  }
+}
+
+hipError_t launch_index_keys(const csa_params_t& p, const void* k_idx, void* k_out, hipStream_t st) {
+  IndexKeysArgs a{k_idx, k_out, (int64_t)p.B * (p.S / p.ratio), p.S / p.ratio, p.ratio, index_prologue_args(p)};
+  if (a.rows == 0) return hipSuccess;
+  const int64_t threads = a.rows * (p.idx_dim / 2);
+  const dim3 grid((unsigned)((threads + IK_THREADS - 1) / IK_THREADS));
+#define CSA_IK_CASE(T, DI) hipLaunchKernelGGL((index_keys_kernel<T, DI>), grid, dim3(IK_THREADS), 0, st, a)
+  const bool bf = p.dtype == CSA_BF16;
+  switch (p.idx_dim) {
+    case 16: if (bf) CSA_IK_CASE(bf16, 16); else CSA_IK_CASE(float, 16); break;
+    case 32: if (bf) CSA_IK_CASE(bf16, 32); else CSA_IK_CASE(float, 32); break;
+    case 64: if (bf) CSA_IK_CASE(bf16, 64); else CSA_IK_CASE(float, 64); break;
+    case 128: if (bf) CSA_IK_CASE(bf16, 128); else CSA_IK_CASE(float, 128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef CSA_IK_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_index_topk(const csa_params_t& p, const void* q_idx, const float* w_idx,
                              const void* k_idx, int32_t* idx, int32_t* n_visible, hipStream_t st) {
   if (p.topk > FT_MAXK) return hipErrorInvalidValue;
   IndexTopkArgs a{q_idx, w_idx, k_idx, idx, n_visible, p.B, p.S, p.idx_heads, p.ratio,
-                  p.S / p.ratio, p.topk, (p.S + FT_WAVES - 1) / FT_WAVES};
+                  p.S / p.ratio, p.topk, (p.S + FT_WAVES - 1) / FT_WAVES, index_prologue_args(p)};
   const int grid = p.B * a.qblocks;
   if (grid == 0) return hipSuccess;
-#define CSA_FT_CASE(T, DI) hipLaunchKernelGGL((index_topk_kernel<T, DI>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a)
+#define CSA_FT_CASE(T, DI)                                                                              \
+  do {                                                                                                  \
+    if (a.pro.on) hipLaunchKernelGGL((index_topk_kernel<T, DI, true>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a); \
+    else hipLaunchKernelGGL((index_topk_kernel<T, DI, false>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a);         \
+  } while (0)
   const bool bf = p.dtype == CSA_BF16;
   switch (p.idx_dim) {
     case 16: if (bf) CSA_FT_CASE(bf16, 16); else CSA_FT_CASE(float, 16); break;
@@ -680,6 +943,7 @@ hipError_t launch_index_scores(const csa_params_t& p, const void* q_idx, const f
   a.t0 = t0;
   a.nrows = nrows;
   a.qblocks = (nrows + IDX_WAVES - 1) / IDX_WAVES;
+  a.pro = index_prologue_args(p);
   const int n_max = visible_entries(t0 + nrows - 1, p.ratio);
   a.n_chunks = (n_max + IDX_CHUNK - 1) / IDX_CHUNK;
   if (a.n_chunks == 0 || nrows == 0) return hipSuccess;
@@ -700,7 +964,11 @@ hipError_t launch_index_scores(const csa_params_t& p, const void* q_idx, const f
   a.chunk_wg_off[a.n_chunks] = off;
   if (off == 0) return hipSuccess;
   dim3 grid(off), block(IDX_WAVES * 64);
-#define CSA_IDX_CASE(T, DI) hipLaunchKernelGGL((index_scores_kernel<T, DI>), grid, block, 0, st, a)
+#define CSA_IDX_CASE(T, DI)                                                                     \
+  do {                                                                                          \
+    if (a.pro.on) hipLaunchKernelGGL((index_scores_kernel<T, DI, true>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((index_scores_kernel<T, DI, false>), grid, block, 0, st, a);         \
+  } while (0)
   const bool bf = p.dtype == CSA_BF16;
   switch (p.idx_dim) {
     case 16: if (bf) CSA_IDX_CASE(bf16, 16); else CSA_IDX_CASE(float, 16); break;

@@ -38,8 +38,10 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
   if (p->B < 0 || p->S < 0) CSA_FAIL(CSA_ERR_INVALID_ARG, "B=%d S=%d must be >= 0", p->B, p->S);
   if (p->dtype != CSA_F32 && p->dtype != CSA_BF16)
     CSA_FAIL(CSA_ERR_INVALID_ARG, "dtype=%d is not CSA_F32 or CSA_BF16", p->dtype);
-  if (p->flags & ~CSA_FLAG_NORM_WINDOW) CSA_FAIL(CSA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
-  const bool compressed = (need & uint32_t(Need::COMPRESS)) || (need & uint32_t(Need::INDEX)) ||
+  if (p->flags & ~(CSA_FLAG_NORM_WINDOW | CSA_FLAG_INDEX_PROLOGUE))
+    CSA_FAIL(CSA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  const uint32_t index_any = uint32_t(Need::INDEX) | uint32_t(Need::INDEX_KEYS);
+  const bool compressed = (need & uint32_t(Need::COMPRESS)) || (need & index_any) ||
                           ((need & uint32_t(Need::MQA)) && !window_only);
   if (need & (uint32_t(Need::COMPRESS) | uint32_t(Need::MQA))) {
     if (p->D <= 0 || p->D % 64 || p->D > 512)
@@ -71,7 +73,7 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
     if (p->topk < 1 || p->topk > kMaxTopk)
       CSA_FAIL(CSA_ERR_INVALID_ARG, "topk=%d must be in 1..%d", p->topk, kMaxTopk);
   }
-  if (need & uint32_t(Need::INDEX)) {
+  if (need & index_any) {
     if (p->idx_heads < 1 || p->idx_heads > 64)
       CSA_FAIL(CSA_ERR_INVALID_ARG, "idx_heads=%d must be in 1..64", p->idx_heads);
     if (p->idx_dim < 16 || p->idx_dim % 16)
@@ -80,6 +82,14 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
       CSA_FAIL(CSA_ERR_UNSUPPORTED, "idx_dim=%d: compiled for 16, 32, 64, 128", p->idx_dim);
     if (p->S / p->ratio > kMaxEntries)
       CSA_FAIL(CSA_ERR_UNSUPPORTED, "S/ratio=%d entries exceeds %d", p->S / p->ratio, kMaxEntries);
+  }
+  // the indexer prologue rotates with the layer's RoPE inside the indexer dims
+  if ((need & uint32_t(Need::INDEX_KEYS)) || ((need & uint32_t(Need::INDEX)) && (p->flags & CSA_FLAG_INDEX_PROLOGUE))) {
+    if (p->rope_dim < 0 || p->rope_dim % 2 || p->rope_dim > p->idx_dim)
+      CSA_FAIL(CSA_ERR_INVALID_ARG, "indexer prologue: rope_dim=%d must be even and <= idx_dim=%d",
+               p->rope_dim, p->idx_dim);
+    if (!(p->rope_theta > 0.0) || !isfinite(p->rope_theta))
+      CSA_FAIL(CSA_ERR_INVALID_ARG, "rope_theta must be positive and finite");
   }
   return CSA_OK;
 }
@@ -103,6 +113,7 @@ WsPlan plan_workspace(const csa_params_t& p, int32_t op) {
     w.idx = take(B * S * (size_t)p.topk * 4);
     w.nvis = take(B * S * 4);
   }
+  if (idx && (p.flags & CSA_FLAG_INDEX_PROLOGUE)) w.k_rot = take(B * n * (size_t)p.idx_dim * es);
   if (idx && p.topk > kFusedTopkMax) {  // separate scores + top-k kernels over chunks
     w.ld = (int64_t)align_up(n > 0 ? n : 1, 32);
     const size_t row_bytes = B * (size_t)w.ld * 4;

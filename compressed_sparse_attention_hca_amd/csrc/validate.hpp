@@ -22,6 +22,7 @@ enum class Need : uint32_t {
   INDEX = 1u << 1,
   MQA = 1u << 2,
   SELECT = 1u << 3,  // a top-k selection is read (topk range only)
+  INDEX_KEYS = 1u << 4,  // the indexer key prologue alone
 };
 inline uint32_t operator|(Need a, Need b) { return uint32_t(a) | uint32_t(b); }
 inline uint32_t operator|(uint32_t a, Need b) { return a | uint32_t(b); }
@@ -38,7 +39,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout of each op.
 struct WsPlan {
-  size_t kv_c = 0, kv_w = 0, idx = 0, nvis = 0, scores = 0;  // offsets
+  size_t kv_c = 0, kv_w = 0, idx = 0, nvis = 0, scores = 0, k_rot = 0;  // offsets
   size_t total = 0;
   int64_t ld = 0;         // scores row stride (floats)
   int32_t chunk_rows = 0; // query rows per indexer/top-k chunk (0: fused, no scores)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum {
   CSA_OK = 0,
@@ -74,6 +74,15 @@ typedef enum {
 
 /* flags */
 #define CSA_FLAG_NORM_WINDOW 1u /* RMS-normalise window latents before their RoPE */
+/* Indexer prologue ("fix(deepseek-v4): correct V4-Flash attention math", Part 1
+ * items 6e and 6a), CSA only.  The indexer scores
+ *   I[t,s] = sum_h (T w[t,h]) ReLU(q'[t,h] . k'[s]),   T = (idx_heads * idx_dim)**-0.5,
+ *   q'[t,h] = round(Hn RoPE(q_I[t,h], pos0 + t)),  k'[s] = round(Hn RoPE(k_I[s], pos0 + s*ratio)),
+ * where RoPE is the layer's (interleaved pairs on the last rope_dim dims, base
+ * rope_theta; rope_dim must be <= idx_dim), Hn = H / sqrt(idx_dim) is the normalised
+ * Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), and round() rounds to the
+ * activation dtype.  The top-k is unchanged by T but not by the rotation. */
+#define CSA_FLAG_INDEX_PROLOGUE 2u
 
 typedef struct {
   int32_t B;          /* batch */
@@ -133,17 +142,27 @@ csa_status_t csa_compress(const csa_params_t* p, const void* va, const void* ga,
 
 /* Stage 3, scores only (for checking): rows t0 .. t0+nrows-1 of every batch;
  * scores[b][t - t0][s] for s < n_visible(t), row stride ld floats (ld >= S/ratio);
- * entries s >= n_visible(t) are not written. */
+ * entries s >= n_visible(t) are not written.  With CSA_FLAG_INDEX_PROLOGUE the
+ * queries are rotated and the weights scaled inside the kernel, and k_idx must hold
+ * keys already passed through csa_index_prologue_keys. */
 csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const float* w_idx,
                               const void* k_idx, float* scores, int64_t ld, int32_t t0,
                               int32_t nrows, void* stream);
+
+/* Indexer key prologue (CSA_FLAG_INDEX_PROLOGUE, see there):
+ *   k_out[b,s] = round(Hn RoPE(k_idx[b,s], pos0 + s*ratio)), both [B,S/ratio,idx_dim]
+ *   in the activation dtype; k_out must not overlap k_idx.  The flag need not be set
+ *   in p; the other indexer fields and rope_dim, rope_theta, pos0 are used. */
+csa_status_t csa_index_prologue_keys(const csa_params_t* p, const void* k_idx, void* k_out,
+                                     void* stream);
 
 /* Stage 3: indexer scores over visible entries and the top-k per query.
  *   idx [B,S,topk] int32: the min(topk, n_visible(t)) selected entries in ascending
  *   order, then -1 padding; ties at the k-th score go to the smaller entry index.
  *   n_visible [B,S] int32.  ws: csa_workspace_bytes(p, CSA_OP_INDEX_TOPK) bytes (none
  *   when topk <= 512: the selection is made inside the indexer kernel and no score
- *   leaves the chip; larger topk scores query chunks into the workspace, then selects). */
+ *   leaves the chip; larger topk scores query chunks into the workspace, then selects).
+ *   With CSA_FLAG_INDEX_PROLOGUE the rotated keys are also kept in the workspace. */
 csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const float* w_idx,
                             const void* k_idx, int32_t* idx, int32_t* n_visible, void* ws,
                             size_t ws_bytes, void* stream);
@@ -186,7 +205,8 @@ typedef enum {
   CSA_KERNEL_INDEXER = 2,     /* indexer scores (one launch per query chunk, topk > 512) */
   CSA_KERNEL_TOPK = 3,        /* top-k selection (one launch per query chunk, topk > 512) */
   CSA_KERNEL_ATTENTION = 4,   /* sparse MQA + de-rotation */
-  CSA_KERNEL_INDEX_TOPK = 5   /* indexer scores fused with top-k (topk <= 512) */
+  CSA_KERNEL_INDEX_TOPK = 5,  /* indexer scores fused with top-k (topk <= 512) */
+  CSA_KERNEL_INDEX_KEYS = 6   /* indexer key prologue (CSA_FLAG_INDEX_PROLOGUE) */
 } csa_kernel_t;
 
 /* Number of events the traced variant of `op` (CSA_OP_CSA_FWD or CSA_OP_HCA_FWD)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 2
+    assert bd.lib.csa_abi_version() == 3
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -124,6 +124,39 @@ def test_index_topk_rejects():
     assert need >= 64 * 1024 * 4  # at least 64 query rows of 1024 fp32 scores
     assert call(p_c1(topk=1024), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
     assert call(p_c1(topk=1024), ws=None) == bd.CSA_ERR_INVALID_ARG
+
+
+def test_index_prologue_validation_and_workspace():
+    """The indexer prologue rotates inside the indexer dims (rope_dim <= idx_dim), keeps
+    the rotated keys in the workspace, and adds one launch to the traced fused call."""
+    pro = dict(flags=bd.FLAG_INDEX_PROLOGUE)
+
+    def topk(p, ws_bytes=1 << 40, ws=A):
+        return bd.lib.csa_index_topk(ctypes.byref(p), A, A, A, A, A, ws, ws_bytes, None)
+    assert topk(p_c1(rope_dim=130, D=512, **pro)) == bd.CSA_ERR_INVALID_ARG
+    assert "rope_dim" in bd.last_error()
+    c0 = bd.params(wl.C0, flags=bd.FLAG_INDEX_PROLOGUE, rope_dim=18)   # idx_dim 16
+    assert topk(c0) == bd.CSA_ERR_INVALID_ARG
+    need = bd.workspace_bytes(p_c1(**pro), bd.OP_INDEX_TOPK)
+    assert need >= 1024 * 128 * 2                     # the rotated keys of C1, bf16
+    assert bd.workspace_bytes(p_c1(), bd.OP_INDEX_TOPK) == 0
+    assert topk(p_c1(**pro), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
+    assert topk(p_c1(**pro), ws=None) == bd.CSA_ERR_INVALID_ARG
+    assert (bd.workspace_bytes(p_c1(**pro), bd.OP_CSA_FWD)
+            == bd.workspace_bytes(p_c1(), bd.OP_CSA_FWD) + need)
+    assert bd.lib.csa_trace_events(ctypes.byref(p_c1(**pro)), bd.OP_CSA_FWD) == \
+        bd.lib.csa_trace_events(ctypes.byref(p_c1()), bd.OP_CSA_FWD) + 1
+
+    def keys(p, k=A, out=A + (1 << 30)):
+        return bd.lib.csa_index_prologue_keys(ctypes.byref(p), k, out, None)
+    assert keys(p_c1(), out=A + 16) == bd.CSA_ERR_INVALID_ARG       # overlapping
+    assert "overlaps" in bd.last_error()
+    assert keys(p_c1(), k=None) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(), out=A + 8) == bd.CSA_ERR_INVALID_ARG        # misaligned
+    assert keys(p_c1(rope_dim=130)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(idx_dim=24)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(rope_theta=-1.0)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(flags=4)) == bd.CSA_ERR_INVALID_ARG
 
 
 def test_index_scores_rejects_rows_and_ld():
