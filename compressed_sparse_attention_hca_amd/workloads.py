@@ -57,6 +57,7 @@ class LayerConfig:
     pos0: int = 0
     norm_window: bool = False  # RMS-normalise window latents before rotation
     index_prologue: bool = False  # indexer RoPE + Hadamard + temperature (CSA)
+    index_fp8: bool = False  # indexer QK on per-row E4M3 operands (CSA)
     seed: int = 0
 
     @property

@@ -55,6 +55,45 @@ def brute_index_prologue(vec, P, R, theta, dtype):
     return out
 
 
+def _f32(x):
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def _e4m3_table():
+    """Every finite non-negative OCP E4M3 value with its code: exponent field E and
+    mantissa M give M * 2**-9 for E = 0, else (1 + M/8) * 2**(E - 7); E = 15, M = 7 is
+    NaN and left out, so the largest is 448."""
+    vals = []
+    for E in range(16):
+        for M in range(8):
+            if E == 15 and M == 7:
+                continue
+            v = M * 2.0 ** -9 if E == 0 else (1 + M / 8) * 2.0 ** (E - 7)
+            vals.append((v, E * 8 + M))
+    return vals
+
+
+_E4M3 = _e4m3_table()
+
+
+def brute_e4m3(x):
+    """Nearest E4M3 value by search over the table; a tie takes the code with an even
+    mantissa."""
+    a = abs(x)
+    best = min(_E4M3, key=lambda vc: (abs(vc[0] - a), vc[1] & 1))
+    return math.copysign(best[0], x) if best[0] else 0.0
+
+
+def brute_quant_row(row):
+    """Per-row E4M3 codes and scale, each step rounded to fp32 (a float64 result of
+    one division or product rounds to the correctly rounded fp32 value)."""
+    m = max(abs(_f32(v)) for v in row)
+    if m == 0:
+        return [0.0] * len(row), 0.0
+    inv = _f32(448.0 / m)
+    return [brute_e4m3(_f32(_f32(v) * inv)) for v in row], _f32(m / 448.0)
+
+
 def brute_entry(va, ga, vb, gb, bias, s, r, overlap, D):
     """Pooled entry s (list of D floats).  Slots enumerated token by token."""
     slots = []  # (value row, gate row, bias row index)
@@ -114,6 +153,12 @@ def brute_layer(cfg, inp, b=0, sinks=None):
                       for s in range(len(ki))]
                 temp = 1.0 / math.sqrt(cfg.idx_heads * cfg.idx_dim)
                 wi = [float(wi[h]) * temp for h in range(cfg.idx_heads)]
+            if getattr(cfg, "index_fp8", False):
+                def deq(row):
+                    codes, sc = brute_quant_row([float(v) for v in row])
+                    return [c * sc for c in codes]
+                qi = [deq(qi[h]) for h in range(cfg.idx_heads)]
+                ki = [deq(ki[s]) for s in range(len(ki))]
             sc = []
             for s in vis:
                 tot = 0.0

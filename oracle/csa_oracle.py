@@ -34,6 +34,10 @@ Readings taken where the pages leave a step open (listed in the design doc as well):
     normalised Sylvester Hadamard over D_I, the result rounded to the activation dtype
     (the tensor the scoring consumes); the per-head weights are scaled by
     (H_I * D_I)**-0.5.
+  * FP8 indexer (optional, index_fp8): each q_I[t,h] and k_I[s] row is quantized to
+    OCP E4M3 (max 448, round to nearest even) with its own scale, absmax / 448; the
+    code is decided in fp32 (the multiplier 448 / absmax and the product rounded to
+    fp32, as the kernel does); the scores use the decoded values code * scale.
 """
 from __future__ import annotations
 
@@ -43,7 +47,7 @@ __all__ = [
     "rope_angles", "rope", "gated_pool", "rms_norm", "compress", "visible_entries",
     "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
-    "hadamard", "round_to", "index_prologue", "index_temperature",
+    "hadamard", "round_to", "index_prologue", "index_temperature", "e4m3", "quant_e4m3_rows",
 ]
 
 
@@ -190,6 +194,37 @@ def index_temperature(idx_heads: int, idx_dim: int) -> float:
     return float(idx_heads) ** -0.5 * float(idx_dim) ** -0.5
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3(x) -> np.ndarray:
+    """Nearest OCP E4M3 value (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+    largest finite 448), ties to even.  Normal numbers |x| >= 2**-6 keep 4 significant
+    bits; below that the spacing is 2**-9.  Magnitudes above 448 saturate to 448 (the
+    quantizer below never produces them)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    ulp = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    return np.clip(np.rint(x / ulp) * ulp, -E4M3_MAX, E4M3_MAX)
+
+
+def quant_e4m3_rows(x):
+    """Per-row E4M3 quantization of the indexer operands ("Enabling DeepSeek-V4-Flash
+    Training ...", closing remarks: an E4M3 path for the indexer QK; "fix(deepseek-v4)
+    ...", Part 1 item 4: it changes the selection, so it is opt-in).  Over the last
+    axis: m = max |x|, codes = E4M3(fp32(x * fp32(448 / m))) and scale = fp32(m / 448),
+    both divisions and the product rounded to fp32; a zero row gets codes 0 and scale 0.
+    x holds fp32-representable values.  Returns (codes, scale) as fp64 arrays; the row
+    decodes to codes * scale."""
+    x32 = np.asarray(x, dtype=np.float32)
+    m = np.max(np.abs(x32), axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        inv = np.where(m > 0, np.float32(E4M3_MAX) / np.where(m > 0, m, 1), np.float32(0)).astype(np.float32)
+    y = (x32 * inv).astype(np.float32)
+    scale = (m / np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3(y.astype(np.float64)), scale[..., 0].astype(np.float64)
+
+
 def indexer_scores(q_i, w, k_i, ratio: int) -> list:
     """Scores for every query, as a list of rows of length n_t."""
     S = q_i.shape[0]
@@ -259,7 +294,9 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
     of the oracle's own top-k (for re-evaluating on another admissible selection).
     `sinks` [H] (optional): per-head softmax sink logits (see attend_row).
     With cfg.index_prologue set, the indexer reads index_prologue(q_I) at pos0 + t,
-    index_prologue(k_I) at pos0 + s*r and w * index_temperature (CSA only).
+    index_prologue(k_I) at pos0 + s*r and w * index_temperature (CSA only).  With
+    cfg.index_fp8 set it scores the E4M3-decoded operands (quant_e4m3_rows), after the
+    prologue when both are set.
 
     Returns a dict: o {(b,t): [H,D]}, sel {(b,t): indices}, scores {(b,t): row},
     n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, and P when
@@ -290,17 +327,24 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
         kv_raw_b = inp["kv_raw"][b]
         ts = [t for bb, t in rows if bb == b]
         prologue = kind == "csa" and bool(getattr(cfg, "index_prologue", False))
+        fp8 = kind == "csa" and bool(getattr(cfg, "index_fp8", False))
         if kind == "csa":
             k_i_b = _as64(inp["k_idx"][b])
             if prologue:
                 k_pos = pos0 + np.arange(k_i_b.shape[0], dtype=np.int64) * cfg.ratio
                 k_i_b = index_prologue(k_i_b, k_pos, R, theta, cfg.dtype)
+            if fp8:
+                codes, sc = quant_e4m3_rows(k_i_b)
+                k_i_b = codes * sc[:, None]
 
         def index_row(t, n_vis):
             q_i, w_i = _as64(inp["q_idx"][b, t]), _as64(inp["w_idx"][b, t])
             if prologue:
                 q_i = index_prologue(q_i, pos0 + t, R, theta, cfg.dtype)
                 w_i = w_i * index_temperature(cfg.idx_heads, cfg.idx_dim)
+            if fp8:
+                codes, sc = quant_e4m3_rows(q_i)
+                q_i = codes * sc[:, None]
             return indexer_scores_row(q_i, w_i, k_i_b, n_vis)
 
         for t in ts:

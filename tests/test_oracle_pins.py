@@ -519,3 +519,88 @@ def test_prologue_oracle_matches_brute_force(dtype):
         assert np.allclose(ora["scores"][(0, t)], bf["scores"][t], atol=1e-12)
         assert list(ora["sel"][(0, t)]) == bf["sel"][t]
     assert np.allclose(ora["o_full"][0], np.array(bf["o"]), atol=1e-12)
+
+
+# -------------------------------------------------------------- FP8 indexer ----------
+# "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
+# closing remarks (an E4M3 path for the indexer QK); "fix(deepseek-v4): correct
+# V4-Flash attention math", Part 1 item 4 (quantization changes the selection).
+
+def test_e4m3_matches_torch_cast_and_the_code_table(rng):
+    """Rounding to E4M3 is torch's float8_e4m3fn cast (round to nearest even) on
+    in-range fp32 values, normal and subnormal, and the table search of the brute force."""
+    x = np.concatenate([rng.normal(size=3000) * 60.0, rng.normal(size=1000) * 2.0 ** -8,
+                        [448.0, -448.0, 0.0, 2.0 ** -9, 3 * 2.0 ** -10, 1.0625, 1.1875]])
+    x32 = x[np.abs(x) < 440].astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3(x32.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(got[:300], [brute.brute_e4m3(float(v)) for v in x32[:300]])
+    # ties: 1 + 1/16 is halfway between 1 and 1.125 -> 1 (even); 1.1875 -> 1.25
+    assert list(O.e4m3(np.array([1.0625, 1.1875, 3 * 2.0 ** -10]))) == [1.0, 1.25, 2.0 ** -8]
+
+
+def test_quant_rows_closed_forms():
+    """The largest magnitude of a row maps to +-448 and the scale is absmax / 448;
+    values that are E4M3 numbers times the scale come back exactly; a zero row has
+    codes 0 and scale 0; scaling a row by a power of two keeps its codes."""
+    row = np.array([[3.5, -1.75, 0.4375, 0.0, 2.0 ** -7]]) * 0.5
+    codes, sc = O.quant_e4m3_rows(row)
+    assert codes[0, 0] == 448.0 and sc[0] == np.float32(1.75 / 448.0)
+    assert np.allclose(codes[0] * sc[0], row[0], rtol=0, atol=1e-12)
+    z, zs = O.quant_e4m3_rows(np.zeros((2, 8)))
+    assert not z.any() and not zs.any()
+    r = np.random.default_rng(3).normal(size=(4, 64)).astype(np.float32)
+    c1, s1 = O.quant_e4m3_rows(r)
+    c2, s2 = O.quant_e4m3_rows(r * np.float32(8.0))
+    assert np.array_equal(c1, c2) and np.array_equal(s2, s1 * 8)
+
+
+def test_quant_rows_error_bound_and_brute_force(rng):
+    """Decoding loses at most half a unit of the 3-bit mantissa (2^-4 relative) plus
+    half the subnormal spacing (2^-10 times the scale); the brute force's per-step fp32
+    quantization gives the same codes and scales."""
+    x = (rng.normal(size=(16, 128)) * np.exp(rng.normal(size=(16, 1)))).astype(np.float32).astype(np.float64)
+    codes, sc = O.quant_e4m3_rows(x)
+    err = np.abs(codes * sc[:, None] - x)
+    assert np.all(err <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * sc[:, None] * 1.0000001)
+    for i in range(4):
+        bc, bs = brute.brute_quant_row(list(x[i]))
+        assert list(codes[i]) == bc and sc[i] == bs
+
+
+@pytest.mark.parametrize("prologue", [False, True])
+def test_fp8_indexer_oracle_matches_brute_force(prologue):
+    cfg = tiny("csa", S=24, pos0=3, idx_dim=16, rope_dim=8, idx_heads=3, dtype=wl.BF16,
+               index_fp8=True, index_prologue=prologue)
+    inp = to_np(wl.make_inputs(cfg))
+    ora = O.layer_forward(cfg, inp)
+    bf = brute.brute_layer(cfg, inp)
+    for t in range(cfg.S):
+        assert np.allclose(ora["scores"][(0, t)], bf["scores"][t], atol=1e-12)
+        assert list(ora["sel"][(0, t)]) == bf["sel"][t]
+    assert np.allclose(ora["o_full"][0], np.array(bf["o"]), atol=1e-12)
+
+
+def test_fp8_scores_track_the_exact_scores():
+    """The quantized scores stay within the error bound of the operands (each element
+    within 2^-4 of itself plus 2^-10 of its row scale; ReLU and the positive weights
+    do not enlarge the difference), and most of the selection survives."""
+    cfg = tiny("csa", S=256, idx_dim=64, rope_dim=8, idx_heads=8, topk=16, dtype=wl.BF16)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(150, 256, 15)]
+    a = O.layer_rows(cfg, inp, rows)
+    b = O.layer_rows(cfg.replace(index_fp8=True), inp, rows)
+    q, k, w = inp["q_idx"][0], inp["k_idx"][0], inp["w_idx"][0]
+    keep = []
+    for (_, t) in rows:
+        n = len(a["scores"][(0, t)])
+        # per element |error| <= 2^-4 |x| + 2^-10 * scale (normal and subnormal range)
+        sq = np.abs(q[t]).max(1, keepdims=True) / 448
+        sk = np.abs(k[:n]).max(1, keepdims=True) / 448
+        eq, ek = 2.0 ** -4 * np.abs(q[t]) + 2.0 ** -10 * sq, 2.0 ** -4 * np.abs(k[:n]) + 2.0 ** -10 * sk
+        dot_err = eq @ (np.abs(k[:n]) + ek).T + np.abs(q[t]) @ ek.T
+        bound = np.abs(w[t]) @ dot_err * 1.001
+        assert np.all(np.abs(b["scores"][(0, t)] - a["scores"][(0, t)]) <= bound)
+        keep.append(len(set(a["sel"][(0, t)]) & set(b["sel"][(0, t)])) / cfg.topk)
+    assert np.mean(keep) > 0.6
