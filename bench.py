@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "CSA layer fwd tokens/s + TFLOP/s at S=64K (1 GPU); % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -61,11 +62,12 @@ def kernel_work(cfg, wl):
     return work
 
 
-def roofline_entry(amount, unit, bound, ms):
+def roofline_entry(amount, unit, bound, ms, peak_tflops=PEAK_BF16_TFLOPS):
+    """peak_tflops: the MFMA peak of the contraction's own dtype."""
     if unit == "flops":
         achieved = amount / (ms * 1e-3) / 1e12
-        return {"bound": bound, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        return {"bound": bound, "achieved": round(achieved, 2), "peak": peak_tflops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4)}
     achieved = amount / (ms * 1e-3) / 1e9
     return {"bound": bound, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4)}
@@ -282,7 +284,8 @@ def run_stack(args, dev) -> dict:
         "metric": "43-layer V4-Flash attention stack fwd tokens/s (B=4, S=8192, 1 GPU)",
         "value": round(B * S / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16, indexer QK fp8 (e4m3)" if cfg.index_fp8 else "bf16",
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": "v4flash_stack43_bf16_B4_S8192", "B": B, "S": S, "layers": len(layers),
                    "csa": counts.get("csa", 0), "hca": counts.get("hca", 0), "swa": counts.get("swa", 0)},
@@ -305,6 +308,8 @@ def main():
                     help="give every head a softmax-sink logit (seeded N(0, 2^2), fp32)")
     ap.add_argument("--index-prologue", action="store_true",
                     help="CSA: indexer prologue on (RoPE + Hadamard of q_I and k_I, temperature on w)")
+    ap.add_argument("--index-fp8", action="store_true",
+                    help="CSA: FP8 (E4M3, per-row scales) indexer operands")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -344,6 +349,8 @@ def main():
     cfg = wl.CONFIGS[args.workload]
     if args.index_prologue:
         cfg = cfg.replace(index_prologue=True)
+    if args.index_fp8:
+        cfg = cfg.replace(index_fp8=True)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     inp = wl.make_inputs(cfg, dev)
     if args.sink:
@@ -386,7 +393,8 @@ def main():
     kernels = {}
     for k, v in tot.items():
         amt, unit, bound = work[k]
-        e = roofline_entry(amt, unit, bound, v)
+        fp8_qk = cfg.index_fp8 and k in ("index_topk", "indexer")
+        e = roofline_entry(amt, unit, bound, v, PEAK_FP8_TFLOPS if fp8_qk else PEAK_BF16_TFLOPS)
         e.update({"ms_per_step": round(v, 4), "launches_per_step": launches[k],
                   "avg_launch_ms": round(v / launches[k], 4)})
         kernels[k] = e
@@ -411,7 +419,8 @@ def main():
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
                    "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
-                   "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue)},
+                   "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue),
+                   "index_fp8": bool(cfg.index_fp8)},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_step": f["total"],
         "page_convention_attention_tflops": round(

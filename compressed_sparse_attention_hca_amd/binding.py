@@ -22,6 +22,7 @@ CSA_F32, CSA_BF16 = 0, 1
 OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_CSA_FWD, OP_HCA_FWD = range(5)
 FLAG_NORM_WINDOW = 1
 FLAG_INDEX_PROLOGUE = 2
+FLAG_INDEX_FP8 = 4
 
 
 class Params(ctypes.Structure):
@@ -58,7 +59,7 @@ def _load():
         "csa_compress": [P, V, V, V, V, V, V, V],
         "csa_index_scores": [P, V, V, V, V, I64, I32, I32, V],
         "csa_index_topk": [P, V, V, V, V, V, V, SZ, V],
-        "csa_index_prologue_keys": [P, V, V, V],
+        "csa_index_keys": [P, V, V, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
@@ -88,7 +89,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_prologue_keys",
+EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_keys",
            "csa_sparse_mqa_fwd",
            "csa_sparse_mqa_fwd_sink", "csa_fwd",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
@@ -116,7 +117,8 @@ def params(cfg: wl.LayerConfig, **over) -> Params:
                dtype=CSA_BF16 if cfg.dtype == wl.BF16 else CSA_F32,
                rope_theta=cfg.rope_theta, rms_eps=cfg.rms_eps, softmax_scale=cfg.softmax_scale,
                pos0=cfg.pos0, flags=(FLAG_NORM_WINDOW if cfg.norm_window else 0)
-               | (FLAG_INDEX_PROLOGUE if cfg.index_prologue else 0))
+               | (FLAG_INDEX_PROLOGUE if cfg.index_prologue else 0)
+               | (FLAG_INDEX_FP8 if cfg.index_fp8 else 0))
     for k, v in over.items():
         setattr(p, k, v)
     return p
@@ -165,12 +167,16 @@ def index_scores(p: Params, q_idx, w_idx, k_idx, t0=0, nrows=None, scores=None, 
     return scores
 
 
-def index_prologue_keys(p: Params, k_idx, k_out=None, stream=None) -> torch.Tensor:
-    """csa_index_prologue_keys: the indexer keys rotated at pos0 + s*ratio and passed
-    through the normalised Hadamard, in the activation dtype."""
+def index_keys(p: Params, k_idx, k_out=None, stream=None) -> torch.Tensor:
+    """csa_index_keys: the key pass of the indexer prologue and/or the FP8 indexer
+    (p.flags).  Returns the activation-dtype keys, or with FP8 a uint8 tensor of
+    [B, S/ratio, idx_dim + 16] rows (codes in the MFMA order, fp32 scale, padding)."""
     if k_out is None:
-        k_out = torch.empty_like(k_idx)
-    check(lib.csa_index_prologue_keys(ctypes.byref(p), _ptr(k_idx), _ptr(k_out), _stream(stream)))
+        if p.flags & FLAG_INDEX_FP8:
+            k_out = torch.empty((p.B, p.S // p.ratio, p.idx_dim + 16), dtype=torch.uint8, device=k_idx.device)
+        else:
+            k_out = torch.empty_like(k_idx)
+    check(lib.csa_index_keys(ctypes.byref(p), _ptr(k_idx), _ptr(k_out), _stream(stream)))
     return k_out
 
 

@@ -49,7 +49,10 @@ int32_t n_chunks(const WsPlan& plan, int32_t S) {
   return plan.chunk_rows > 0 ? (S + plan.chunk_rows - 1) / plan.chunk_rows : 0;
 }
 
-bool index_prologue(const csa_params_t& p) { return (p.flags & CSA_FLAG_INDEX_PROLOGUE) != 0; }
+// the indexer options that need a key pass before the scoring kernel
+bool index_prologue(const csa_params_t& p) {
+  return (p.flags & (CSA_FLAG_INDEX_PROLOGUE | CSA_FLAG_INDEX_FP8)) != 0;
+}
 
 // Kernel launches of the indexer/top-k stage: the key prologue (with the flag), then
 // one fused launch, or two per chunk.
@@ -73,7 +76,7 @@ csa_status_t run_index_topk(const csa_params_t* p, const void* q_idx, const floa
                             const WsPlan& plan, hipStream_t st, Tracer* tr = nullptr) {
   Tracer none;
   if (!tr) tr = &none;
-  if (index_prologue(*p)) {  // rotated keys into the workspace; queries rotate in-kernel
+  if (index_prologue(*p)) {  // transformed keys into the workspace; queries transform in-kernel
     void* k_rot = ws + plan.k_rot;
     CSA_HIP(launch_index_keys(*p, k_idx, k_rot, st), "indexer key prologue launch");
     CSA_HIP(tr->mark(CSA_KERNEL_INDEX_KEYS, st), "event record");
@@ -186,16 +189,16 @@ csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const fl
   return CSA_OK;
 }
 
-csa_status_t csa_index_prologue_keys(const csa_params_t* p, const void* k_idx, void* k_out,
-                                     void* stream) {
+csa_status_t csa_index_keys(const csa_params_t* p, const void* k_idx, void* k_out, void* stream) {
   CSA_TRY(validate_params(p, uint32_t(Need::INDEX_KEYS), false));
   if (empty(p)) return CSA_OK;
   CSA_TRY(check_ptr(k_idx, "k_idx"));
   CSA_TRY(check_ptr(k_out, "k_out"));
-  const size_t bytes = (size_t)p->B * (size_t)(p->S / p->ratio) * (size_t)p->idx_dim *
-                       (p->dtype == CSA_BF16 ? 2 : 4);
+  const size_t rows = (size_t)p->B * (size_t)(p->S / p->ratio);
+  const size_t in_bytes = rows * (size_t)p->idx_dim * (p->dtype == CSA_BF16 ? 2 : 4);
+  const size_t out_bytes = (p->flags & CSA_FLAG_INDEX_FP8) ? rows * (size_t)(p->idx_dim + 16) : in_bytes;
   const uintptr_t a = reinterpret_cast<uintptr_t>(k_idx), b = reinterpret_cast<uintptr_t>(k_out);
-  if (a < b + bytes && b < a + bytes) {
+  if (a < b + out_bytes && b < a + in_bytes) {
     set_error("k_out overlaps k_idx");
     return CSA_ERR_INVALID_ARG;
   }

@@ -30,10 +30,11 @@ struct IndexPrologue {
   int32_t on;       // rotate the queries (the keys arrive rotated)
   int32_t rope_dim; // rotated dims: the last rope_dim of the indexer dims
   float w_scale;    // (idx_heads * idx_dim)^-1/2 with the prologue, else 1
+  int32_t fp8;      // E4M3 operands: queries quantized in-kernel, keys arrive as fp8 rows
 };
 
 __host__ inline IndexPrologue index_prologue_args(const csa_params_t& p) {
-  IndexPrologue r{p.rope_theta, p.pos0, 0, p.rope_dim, 1.0f};
+  IndexPrologue r{p.rope_theta, p.pos0, 0, p.rope_dim, 1.0f, (p.flags & CSA_FLAG_INDEX_FP8) ? 1 : 0};
   if (p.flags & CSA_FLAG_INDEX_PROLOGUE) {
     r.on = 1;
     r.w_scale = (float)(1.0 / sqrt((double)p.idx_heads * (double)p.idx_dim));
@@ -72,6 +73,37 @@ __device__ inline f32x16 mfma32x32x16(const Frag<float>& a, const Frag<float>& b
 #pragma unroll
   for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[i], b.v[i], c, 0, 0, 0);
   return c;
+}
+
+// ---------------------------------------------------------------------------------
+// FP8 (E4M3) indexer operands ("Enabling DeepSeek-V4-Flash Training on AMD Instinct
+// MI355X GPUs with Primus", closing remarks: an E4M3 path for the indexer QK).  Each
+// q_I[t,h] and k_I[s] row is quantized with its own scale: m = max |x|, codes =
+// E4M3(x * (448 / m)) rounded to nearest even by v_cvt_pk_fp8_f32, scale = m / 448
+// (both divisions IEEE fp32); a zero row has codes 0 and scale 0.  The scales factor
+// out of the ReLU: score = sk[s] * sum_h (w[h] sq[h]) ReLU(codes_q[h] . codes_k[s]).
+// The MFMA is v_mfma_f32_32x32x64_f8f6f4: lane (g, l32) holds 32 codes of row l32 in
+// k-slot order p = 0..31, p -> dim 64*kk + 16*(p/8) + 8*g + p%8 for k-step kk; this is
+// the bf16 fragment layout (fragment ks = 4*kk + p/8, element p%8), so the queries
+// convert in place, and the key rows are stored in that order (byte 64*kk + 32*g + p
+// of a row), followed by the fp32 scale and 12 bytes of padding: DI + 16 bytes a row.
+// ---------------------------------------------------------------------------------
+constexpr float kE4M3Max = 448.0f;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline int key_fp8_pos(int d) {  // byte of dim d in a key row
+  return (d & ~63) + 32 * ((d >> 3) & 1) + 8 * ((d & 63) >> 4) + (d & 7);
+}
+
+// Four E4M3 codes of x[0..3] * inv packed into one word (byte i = x[i]).
+__device__ inline uint32_t pack_fp8x4(float x0, float x1, float x2, float x3, float inv) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * inv, x1 * inv, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2 * inv, x3 * inv, w, true);
+  return (uint32_t)w;
+}
+
+__device__ inline f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // A pointer the wave holds in every lane, moved to scalar registers (a global_load_lds
@@ -198,14 +230,56 @@ __device__ void index_query_prologue(Frag<T> (&qa)[2][DI / 16], int64_t P, int R
   }
 }
 
-template <typename T, int DI, bool PRO>
+// E4M3 codes of one wave's query fragments (after the prologue, if any), in the MFMA
+// k-slot order described above.  Per head row: the maximum of the lane's 8*KS values
+// and of the partner half's (v_permlane32_swap), the multiplier 448 / max, the codes.
+// The lower-half lane of head hb*32 + l32 writes the row's scale max / 448 to tab[h].
+// Every lane of the wave must call it.
+template <typename T, int DI>
+__device__ void index_query_fp8(const Frag<T> (&qa)[2][DI / 16], i32x8 (&q8)[2][DI / 64], uint32_t* tab) {
+  constexpr int KS = DI / 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float m = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        float x0, x1;
+        frag_get2(qa[hb][ks], i, x0, x1);
+        m = fmaxf(m, fmaxf(fabsf(x0), fabsf(x1)));
+      }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float inv = m > 0.f ? kE4M3Max / m : 0.f;
+    if (g == 0) ((CSA_LDS uint32_t*)tab)[hb * 32 + l32] = __float_as_uint(m / kE4M3Max);
+#pragma unroll
+    for (int kk = 0; kk < DI / 64; ++kk)
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) frag_get2(qa[hb][4 * kk + m4], i, x[i], x[i + 1]);
+        q8[hb][kk][2 * m4] = (int)pack_fp8x4(x[0], x[1], x[2], x[3], inv);
+        q8[hb][kk][2 * m4 + 1] = (int)pack_fp8x4(x[4], x[5], x[6], x[7], inv);
+      }
+  }
+}
+
+template <typename T, int DI, bool PRO, bool F8>
 __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs a) {
   constexpr int KS = DI / 16;                    // k-steps of 16
   constexpr int VEC = 16 / sizeof(T);            // elements per 16-byte load
   constexpr int ROW = DI + 16 / sizeof(T);       // padded LDS row (elements)
   constexpr int HB = 2;                          // head blocks of 32 (up to 64 heads)
-  __shared__ __attribute__((aligned(16))) T tile[2][IDX_TILE * ROW];
-  __shared__ __attribute__((aligned(16))) uint32_t pro_tab[PRO ? IDX_WAVES : 1][PRO ? DI : 1];
+  __shared__ __attribute__((aligned(16))) T tile[F8 ? 1 : 2][F8 ? 8 : IDX_TILE * ROW];
+  __shared__ __attribute__((aligned(16))) uint32_t pro_tab[(PRO || F8) ? IDX_WAVES : 1][(PRO || F8) ? DI : 1];
+  // fp8 key rows: DI codes, the scale and padding (RB8 bytes), one pad chunk in LDS
+  constexpr int RB8 = DI + 16, RP8 = RB8 + 16, KK = F8 ? DI / 64 : 1;
+  __shared__ __attribute__((aligned(16))) unsigned char tile8[F8 ? 2 : 1][F8 ? IDX_TILE * RP8 : 16];
 
   // workgroup -> (chunk, batch, query block)
   const int wg = blockIdx.x;
@@ -233,6 +307,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
 
   // A operand: q_I[b, t, h, :] with h = hb*32 + l32; zero for h >= HI.
   Frag<T> qa[HB][KS];
+  i32x8 q8[HB][KK];  // E4M3 codes (F8)
   float w[HB][16];
   const T* qrow = static_cast<const T*>(a.q_idx) + ((int64_t)b * a.S + t) * a.HI * DI;
 #pragma unroll
@@ -251,6 +326,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
   // from folding the fragment loads into the prologue, which needs 40-140 more VGPRs)
   if constexpr (PRO)
     if (a.pro.on) index_query_prologue<T, DI>(qa, a.pro.pos0 + t, a.pro.rope_dim, a.pro.theta, pro_tab[wave]);
+  if constexpr (F8)
+    if (a.pro.fp8) index_query_fp8<T, DI>(qa, q8, pro_tab[wave]);  // head scales -> pro_tab[wave][0..63]
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     // accumulator element 4j+i is head hb*32 + 8j + 4g + i
@@ -261,6 +338,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
         const int hh = hb * 32 + 8 * j + 4 * g + i;
         float wv = (q_ok && hh < a.HI) ? a.w_idx[((int64_t)b * a.S + t) * a.HI + hh] : 0.f;
         if constexpr (PRO) wv *= a.pro.w_scale;
+        if constexpr (F8) wv *= __uint_as_float(pro_tab[wave][hh]);
         w[hb][4 * j + i] = wv;
       }
   }
@@ -272,6 +350,27 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
   constexpr int CHUNKS_PER_TILE = IDX_TILE * DI / VEC;   // 16-byte pieces per tile
   constexpr int PER_THREAD = (CHUNKS_PER_TILE + NT - 1) / NT;
   uint4 pf[PER_THREAD];
+  constexpr int CH8 = IDX_TILE * RB8 / 16;                  // 16-byte pieces per fp8 tile
+  constexpr int PER8 = (CH8 + NT - 1) / NT;
+  uint4 pf8[PER8];
+  const unsigned char* kbase8 = static_cast<const unsigned char*>(a.k_idx) + (int64_t)b * a.n_entries * RB8;
+  auto fetch8 = [&](int e0) {
+#pragma unroll
+    for (int k = 0; k < PER8; ++k) {
+      const int c = threadIdx.x + k * NT;
+      const int row = c / (RB8 / 16);
+      pf8[k] = (c < CH8 && e0 + row < e_end)
+                   ? *reinterpret_cast<const uint4*>(kbase8 + (int64_t)(e0 + row) * RB8 + (c % (RB8 / 16)) * 16)
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto commit8 = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < PER8; ++k) {
+      const int c = threadIdx.x + k * NT;
+      if (c < CH8) *reinterpret_cast<uint4*>(&tile8[buf][(c / (RB8 / 16)) * RP8 + (c % (RB8 / 16)) * 16]) = pf8[k];
+    }
+  };
   auto fetch = [&](int e0) {
 #pragma unroll
     for (int k = 0; k < PER_THREAD; ++k) {
@@ -298,14 +397,23 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
   float* srow = a.scores + ((int64_t)b * a.nrows + trow) * a.ld;
   const int ntiles = (e_end - e_begin + IDX_TILE - 1) / IDX_TILE;
   if (ntiles > 0) {
-    fetch(e_begin);
-    commit(0);
+    if constexpr (F8) {
+      fetch8(e_begin);
+      commit8(0);
+    } else {
+      fetch(e_begin);
+      commit(0);
+    }
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int e0 = e_begin + it * IDX_TILE;
-    if (it + 1 < ntiles) fetch(e0 + IDX_TILE);
-    const T* tb = tile[it & 1];
+    if (it + 1 < ntiles) {
+      if constexpr (F8) fetch8(e0 + IDX_TILE);
+      else fetch(e0 + IDX_TILE);
+    }
+    const T* tb = tile[F8 ? 0 : (it & 1)];
+    const unsigned char* tb8 = tile8[F8 ? (it & 1) : 0];
 #pragma unroll
     for (int nb = 0; nb < IDX_TILE / 32; ++nb) {
       const int eb = e0 + nb * 32;
@@ -315,11 +423,26 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+      float sk = 1.f;
+      if constexpr (F8) {
+        const unsigned char* rp = tb8 + (nb * 32 + l32) * RP8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const Frag<T> kb = load_frag(tb + (nb * 32 + l32) * ROW + ks * 16 + g * 8);
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 lo4 = *reinterpret_cast<const uint4*>(rp + kk * 64 + g * 32);
+          const uint4 hi4 = *reinterpret_cast<const uint4*>(rp + kk * 64 + g * 32 + 16);
+          const i32x8 kb = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                            (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb, acc[hb]);
+          for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x64_fp8(q8[hb][kk], kb, acc[hb]);
+        }
+        sk = *reinterpret_cast<const float*>(rp + DI);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const Frag<T> kb = load_frag(tb + (nb * 32 + l32) * ROW + ks * 16 + g * 8);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(qa[hb][ks], kb, acc[hb]);
+        }
       }
       float v = 0.f;
 #pragma unroll
@@ -327,10 +450,14 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
 #pragma unroll
         for (int i = 0; i < 16; ++i) v = fmaf(w[hb][i], relu(acc[hb][i]), v);
       v += __shfl_xor(v, 32, 64);
+      if constexpr (F8) v *= sk;  // the entry's scale (sq is folded into w)
       const int e = eb + l32;
       if (g == 0 && e < n_t) srow[e] = v;
     }
-    if (it + 1 < ntiles) commit((it + 1) & 1);
+    if (it + 1 < ntiles) {
+      if constexpr (F8) commit8((it + 1) & 1);
+      else commit((it + 1) & 1);
+    }
     __syncthreads();
   }
 }
@@ -361,8 +488,9 @@ constexpr int FT_TILE = 64;    // entries per LDS stage (two 32-entry MFMA block
 constexpr int FT_MAXK = 512;   // largest top-k of the fused path
 constexpr int FT_LDS = 160 * 1024;
 
-template <typename T, int DI> struct FtShape {
-  static constexpr int ROWB = DI * (int)sizeof(T);       // bytes per k_I row
+template <typename T, int DI, bool F8> struct FtShape {
+  // bytes per k_I row: DI elements, or DI E4M3 codes then the fp32 scale (16 bytes)
+  static constexpr int ROWB = F8 ? DI + 16 : DI * (int)sizeof(T);
   static constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
   static constexpr int SPR = CPR + 1;                    // LDS slots per row (one pad)
   static constexpr int ROWP = SPR * 16;                  // padded row pitch in LDS
@@ -575,9 +703,10 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
   return r;
 }
 
-template <typename T, int DI, bool PRO>
+template <typename T, int DI, bool PRO, bool F8>
 __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs a) {
-  using SH = FtShape<T, DI>;
+  using SH = FtShape<T, DI, F8>;
+  constexpr int KK = F8 ? DI / 64 : 1;  // fp8 k-steps of 64
   constexpr int KS = DI / 16;
   constexpr int HB = 2;
   constexpr int CAP = SH::CAP;
@@ -607,6 +736,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   const bool select_all = n_t <= K;
 
   Frag<T> qa[HB][KS];
+  i32x8 q8[HB][KK];  // E4M3 codes (F8)
   float w[HB][16];
   const T* qrow = static_cast<const T*>(a.q_idx) + ((int64_t)b * a.S + t) * a.HI * DI;
 #pragma unroll
@@ -621,7 +751,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       }
     }
   }
-  if constexpr (!PRO) {
+  if constexpr (!PRO && !F8) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       // accumulator element 4j+i is head hb*32 + 8j + 4g + i
@@ -634,9 +764,9 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
         }
     }
   } else {
-    // With the prologue the head weights go straight to LDS (this wave's index
-    // buffer, unused until the first tile): their latency overlaps the q loads and no
-    // register holds them while the prologue runs.  Lane l copies w[h = min(l, HI-1)];
+    // With the prologue or fp8 operands the head weights go straight to LDS (this
+    // wave's index buffer, unused until the first tile): their latency overlaps the q
+    // loads and no register holds them while the query is transformed.  Lane l copies w[h = min(l, HI-1)];
     // heads past HI are zeroed when read back.
     const float* wrow = wave_uniform(a.w_idx + ((int64_t)b * a.S + min(t, a.S - 1)) * a.HI);
     const uint32_t voff = (uint32_t)min(lane, a.HI - 1) * 4u;
@@ -683,6 +813,32 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   // The fragment reads run two k-steps ahead of the MFMAs that consume them, so the
   // LDS latency hides behind the matrix work of the same wave.
   constexpr int LA = KS < 3 ? KS : 3;
+  // fp8: B fragment of block nb, k-step kk: 32 codes of row nb*32 + l32 at byte
+  // 64kk + 32g (two 16-byte reads); the row's scale sits at byte DI.
+  auto frag8 = [&](const unsigned char* st, int nb, int kk) -> i32x8 {
+    const CSA_LDS unsigned char* p = (const CSA_LDS unsigned char*)st + (nb * 32 + l32) * SH::ROWP + kk * 64 + g * 32;
+    const u32x4 lo4 = *(const CSA_LDS u32x4*)p, hi4 = *(const CSA_LDS u32x4*)(p + 16);
+    i32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = (int)lo4[i];
+      r[4 + i] = (int)hi4[i];
+    }
+    return r;
+  };
+  auto mfma_block8 = [&](const unsigned char* st, int nb, f32x16* acc, float& sk) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const i32x8 kb = frag8(st, nb, kk);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x64_fp8(q8[hb][kk], kb, acc[hb]);
+    }
+    sk = __uint_as_float(*(const CSA_LDS uint32_t*)((const CSA_LDS unsigned char*)st + (nb * 32 + l32) * SH::ROWP + DI));
+  };
   auto mfma_block = [&](const unsigned char* st, int nb, f32x16* acc) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -711,7 +867,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
 
   // ReLU(.) * w summed over the lane's 16 heads of each block (four independent
   // partial sums), then across the two lane halves; admit into the buffer.
-  auto epilogue = [&](const f32x16* acc, int eb) {
+  auto epilogue = [&](const f32x16* acc, int eb, float sk) {
     float v4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -719,7 +875,8 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       for (int i = 0; i < 16; ++i) v4[i & 3] = fmaf(w[hb][i], relu(acc[hb][i]), v4[i & 3]);
     const float v = (v4[0] + v4[1]) + (v4[2] + v4[3]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (F8) s *= sk;  // the entry's scale (sq is folded into w)
     const int e = eb + l32;
     const uint32_t key = score_key(s);
     const bool admit = g == 0 && e >= 0 && e < n_t && key > theta;
@@ -740,20 +897,29 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   wait_vmcnt<0, false>();  // q and w have arrived before any copy is counted
   if (ntiles > 0) issue(0, st0);
   if (ntiles > 1) issue(1, st1);
-  if constexpr (PRO) {
-    // the prologue runs while the first two tiles are in flight.  (a.pro.on is
-    // always set in this instance; the runtime test keeps the compiler from folding
-    // the fragment loads into the prologue, which takes 40-140 more VGPRs.)
-    if (a.pro.on) index_query_prologue<T, DI>(qa, a.pro.pos0 + t, a.pro.rope_dim, a.pro.theta, ckey[wave]);
+  if constexpr (PRO || F8) {
+    // the query transforms run while the first two tiles are in flight.  (a.pro.on /
+    // a.pro.fp8 are always set in these instances; the runtime tests keep the compiler
+    // from folding the fragment loads into the transforms, which takes 40-140 more
+    // VGPRs.)
+    if constexpr (PRO)
+      if (a.pro.on) index_query_prologue<T, DI>(qa, a.pro.pos0 + t, a.pro.rope_dim, a.pro.theta, ckey[wave]);
+    if constexpr (F8)
+      if (a.pro.fp8) index_query_fp8<T, DI>(qa, q8, ckey[wave]);  // head scales -> ckey[wave][0..63]
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 v = *(const CSA_LDS f32x4*)((CSA_LDS int*)cidx[wave] + hb * 32 + 8 * j + 4 * g);
+        f32x4 sq = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (F8) sq = *(const CSA_LDS f32x4*)((CSA_LDS uint32_t*)ckey[wave] + hb * 32 + 8 * j + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int hh = hb * 32 + 8 * j + 4 * g + i;
-          w[hb][4 * j + i] = (q_ok && hh < a.HI) ? v[i] * a.pro.w_scale : 0.f;
+          float wv = v[i];
+          if constexpr (PRO) wv *= a.pro.w_scale;
+          if constexpr (F8) wv *= sq[i];
+          w[hb][4 * j + i] = (q_ok && hh < a.HI) ? wv : 0.f;
         }
       }
   }
@@ -777,6 +943,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   };
 
   f32x16 accA[HB], accB[HB];
+  float skA = 0.f, skB = 0.f;  // fp8: scales of the entries of the blocks in accA / accB
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -800,10 +967,12 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     if (it + 2 < ntiles) issue(it + 2, refill);
     if (select_all) return;
     const int e0 = it * FT_TILE;
-    mfma_block(cur, 0, accA);
-    epilogue(accB, e0 - 32);
-    mfma_block(cur, 1, accB);
-    epilogue(accA, e0);
+    if constexpr (F8) mfma_block8(cur, 0, accA, skA);
+    else mfma_block(cur, 0, accA);
+    epilogue(accB, e0 - 32, skB);
+    if constexpr (F8) mfma_block8(cur, 1, accB, skB);
+    else mfma_block(cur, 1, accB);
+    epilogue(accA, e0, skA);
     // two more tiles could fill the buffer: ask every wave to prune at the next tile
     if (c > CAP - 3 * FT_TILE - 1 && lane == 0) vote[wave] = it;
   };
@@ -814,7 +983,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   }
   if (!select_all && ntiles > 0) {
     make_room(32, false);
-    epilogue(accB, ntiles * FT_TILE - 32);
+    epilogue(accB, ntiles * FT_TILE - 32, skB);
   }
 
   if (!q_ok) return;
@@ -830,11 +999,13 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
 }
 
 // ---------------------------------------------------------------------------------
-// Indexer key prologue: k'[s] = round(Hn RoPE(k_I[s], pos0 + s*ratio)), the keys'
-// half of the prologue ("fix(deepseek-v4): correct V4-Flash attention math", Part 1
-// item 6e: keys rotate at s * compress_ratio).  DI/2 lanes per row, each holding the
-// pair of dims (2j, 2j+1): the Hadamard's dim bit 0 is within the lane and bits 1..
-// are lane bits of the row's group, exchanged by shuffles.  Streaming, HBM-bound.
+// Indexer key pass, for the prologue and/or fp8 operands: k'[s] = round(Hn RoPE(k_I[s],
+// pos0 + s*ratio)) ("fix(deepseek-v4): correct V4-Flash attention math", Part 1 item
+// 6e: keys rotate at s * compress_ratio), then, with fp8, the row's E4M3 codes in the
+// MFMA k-slot order and its fp32 scale (DI + 16 bytes a row).  DI/2 lanes per row, each
+// holding the pair of dims (2j, 2j+1): the Hadamard's dim bit 0 is within the lane and
+// bits 1.. are lane bits of the row's group, exchanged by shuffles, as is the row's
+// maximum.  Streaming, HBM-bound.
 // ---------------------------------------------------------------------------------
 struct IndexKeysArgs {
   const void* k_idx;
@@ -846,7 +1017,7 @@ struct IndexKeysArgs {
 
 constexpr int IK_THREADS = 256;
 
-template <typename T, int DI>
+template <typename T, int DI, bool PRO, bool F8>
 __global__ __launch_bounds__(IK_THREADS) void index_keys_kernel(IndexKeysArgs a) {
   constexpr int LPR = DI / 2;  // lanes per row (divides 64)
   const int64_t gid = (int64_t)blockIdx.x * IK_THREADS + threadIdx.x;
@@ -859,46 +1030,75 @@ __global__ __launch_bounds__(IK_THREADS) void index_keys_kernel(IndexKeysArgs a)
     x0 = to_f32(src[0]);
     x1 = to_f32(src[1]);
   }
-  const int R = a.pro.rope_dim;
-  const int lo = DI - R;
-  if (ok && 2 * j >= lo) {
-    const int s = (int)(row % a.n_entries);
-    float c, sn;
-    rope_cos_sin(entry_position(a.pro.pos0, s, a.ratio), rope_inv_freq((2 * j - lo) >> 1, R, a.pro.theta), &c, &sn);
-    const float r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
-    x0 = r0;
-    x1 = r1;
-  }
-  float h0 = x0 + x1, h1 = x0 - x1;  // dim bit 0
+  if constexpr (PRO) {
+    const int R = a.pro.rope_dim;
+    const int lo = DI - R;
+    if (ok && 2 * j >= lo) {
+      const int s = (int)(row % a.n_entries);
+      float c, sn;
+      rope_cos_sin(entry_position(a.pro.pos0, s, a.ratio), rope_inv_freq((2 * j - lo) >> 1, R, a.pro.theta), &c, &sn);
+      const float r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
+      x0 = r0;
+      x1 = r1;
+    }
+    float h0 = x0 + x1, h1 = x0 - x1;  // dim bit 0
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {  // dim bit k = lane bit k-1
-    const float sg = (j & m) ? -1.f : 1.f;
-    h0 = fmaf(sg, h0, __shfl_xor(h0, m, 64));
-    h1 = fmaf(sg, h1, __shfl_xor(h1, m, 64));
-  }
-  if (ok) {
+    for (int m = 1; m < LPR; m <<= 1) {  // dim bit k = lane bit k-1
+      const float sg = (j & m) ? -1.f : 1.f;
+      h0 = fmaf(sg, h0, __shfl_xor(h0, m, 64));
+      h1 = fmaf(sg, h1, __shfl_xor(h1, m, 64));
+    }
     const float scale = 1.0f / __builtin_sqrtf((float)DI);
-    T* dst = static_cast<T*>(a.k_out) + row * DI + 2 * j;
-    dst[0] = from_f32<T>(h0 * scale);
-    dst[1] = from_f32<T>(h1 * scale);
+    x0 = to_f32(from_f32<T>(h0 * scale));  // the prologue's output is in the activation dtype
+    x1 = to_f32(from_f32<T>(h1 * scale));
+  }
+  if constexpr (!F8) {
+    if (ok) {
+      T* dst = static_cast<T*>(a.k_out) + row * DI + 2 * j;
+      dst[0] = from_f32<T>(x0);
+      dst[1] = from_f32<T>(x1);
+    }
+  } else {
+    float m = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int k = 1; k < LPR; k <<= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+    const float inv = m > 0.f ? kE4M3Max / m : 0.f;
+    if (ok) {
+      unsigned char* dst = static_cast<unsigned char*>(a.k_out) + row * (DI + 16);
+      const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * inv, x1 * inv, 0, false);
+      *reinterpret_cast<uint16_t*>(dst + key_fp8_pos(2 * j)) = (uint16_t)(w & 0xffff);
+      if (j == 0) *reinterpret_cast<uint4*>(dst + DI) = make_uint4(__float_as_uint(m / kE4M3Max), 0u, 0u, 0u);
+    }
   }
 }
 
 hipError_t launch_index_keys(const csa_params_t& p, const void* k_idx, void* k_out, hipStream_t st) {
   IndexKeysArgs a{k_idx, k_out, (int64_t)p.B * (p.S / p.ratio), p.S / p.ratio, p.ratio, index_prologue_args(p)};
   if (a.rows == 0) return hipSuccess;
+  const bool pro = (p.flags & CSA_FLAG_INDEX_PROLOGUE) != 0, f8 = (p.flags & CSA_FLAG_INDEX_FP8) != 0;
+  if (!pro && !f8) return hipErrorInvalidValue;
+  if (f8 && p.idx_dim != 64 && p.idx_dim != 128) return hipErrorInvalidValue;
   const int64_t threads = a.rows * (p.idx_dim / 2);
   const dim3 grid((unsigned)((threads + IK_THREADS - 1) / IK_THREADS));
-#define CSA_IK_CASE(T, DI) hipLaunchKernelGGL((index_keys_kernel<T, DI>), grid, dim3(IK_THREADS), 0, st, a)
+#define CSA_IK_LAUNCH(T, DI, PRO, F8) hipLaunchKernelGGL((index_keys_kernel<T, DI, PRO, F8>), grid, dim3(IK_THREADS), 0, st, a)
+#define CSA_IK_CASE(T, DI)                      \
+  do {                                          \
+    if (!f8) CSA_IK_LAUNCH(T, DI, true, false); \
+    else if (pro) CSA_IK_LAUNCH(T, DI, true, true); \
+    else CSA_IK_LAUNCH(T, DI, false, true);     \
+  } while (0)
+#define CSA_IK_CASE_NO8(T, DI) CSA_IK_LAUNCH(T, DI, true, false)
   const bool bf = p.dtype == CSA_BF16;
   switch (p.idx_dim) {
-    case 16: if (bf) CSA_IK_CASE(bf16, 16); else CSA_IK_CASE(float, 16); break;
-    case 32: if (bf) CSA_IK_CASE(bf16, 32); else CSA_IK_CASE(float, 32); break;
+    case 16: if (bf) CSA_IK_CASE_NO8(bf16, 16); else CSA_IK_CASE_NO8(float, 16); break;
+    case 32: if (bf) CSA_IK_CASE_NO8(bf16, 32); else CSA_IK_CASE_NO8(float, 32); break;
     case 64: if (bf) CSA_IK_CASE(bf16, 64); else CSA_IK_CASE(float, 64); break;
     case 128: if (bf) CSA_IK_CASE(bf16, 128); else CSA_IK_CASE(float, 128); break;
     default: return hipErrorInvalidValue;
   }
 #undef CSA_IK_CASE
+#undef CSA_IK_CASE_NO8
+#undef CSA_IK_LAUNCH
   return hipGetLastError();
 }
 
@@ -909,20 +1109,33 @@ hipError_t launch_index_topk(const csa_params_t& p, const void* q_idx, const flo
                   p.S / p.ratio, p.topk, (p.S + FT_WAVES - 1) / FT_WAVES, index_prologue_args(p)};
   const int grid = p.B * a.qblocks;
   if (grid == 0) return hipSuccess;
-#define CSA_FT_CASE(T, DI)                                                                              \
-  do {                                                                                                  \
-    if (a.pro.on) hipLaunchKernelGGL((index_topk_kernel<T, DI, true>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a); \
-    else hipLaunchKernelGGL((index_topk_kernel<T, DI, false>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a);         \
+  if (a.pro.fp8 && p.idx_dim != 64 && p.idx_dim != 128) return hipErrorInvalidValue;
+#define CSA_FT_LAUNCH(T, DI, PRO, F8) \
+  hipLaunchKernelGGL((index_topk_kernel<T, DI, PRO, F8>), dim3(grid), dim3(FT_WAVES * 64), 0, st, a)
+#define CSA_FT_CASE(T, DI)                          \
+  do {                                              \
+    if (a.pro.fp8) {                                \
+      if (a.pro.on) CSA_FT_LAUNCH(T, DI, true, true); \
+      else CSA_FT_LAUNCH(T, DI, false, true);       \
+    } else if (a.pro.on) CSA_FT_LAUNCH(T, DI, true, false); \
+    else CSA_FT_LAUNCH(T, DI, false, false);        \
+  } while (0)
+#define CSA_FT_CASE_NO8(T, DI)                      \
+  do {                                              \
+    if (a.pro.on) CSA_FT_LAUNCH(T, DI, true, false); \
+    else CSA_FT_LAUNCH(T, DI, false, false);        \
   } while (0)
   const bool bf = p.dtype == CSA_BF16;
   switch (p.idx_dim) {
-    case 16: if (bf) CSA_FT_CASE(bf16, 16); else CSA_FT_CASE(float, 16); break;
-    case 32: if (bf) CSA_FT_CASE(bf16, 32); else CSA_FT_CASE(float, 32); break;
+    case 16: if (bf) CSA_FT_CASE_NO8(bf16, 16); else CSA_FT_CASE_NO8(float, 16); break;
+    case 32: if (bf) CSA_FT_CASE_NO8(bf16, 32); else CSA_FT_CASE_NO8(float, 32); break;
     case 64: if (bf) CSA_FT_CASE(bf16, 64); else CSA_FT_CASE(float, 64); break;
     case 128: if (bf) CSA_FT_CASE(bf16, 128); else CSA_FT_CASE(float, 128); break;
     default: return hipErrorInvalidValue;
   }
 #undef CSA_FT_CASE
+#undef CSA_FT_CASE_NO8
+#undef CSA_FT_LAUNCH
   return hipGetLastError();
 }
 
@@ -964,20 +1177,32 @@ hipError_t launch_index_scores(const csa_params_t& p, const void* q_idx, const f
   a.chunk_wg_off[a.n_chunks] = off;
   if (off == 0) return hipSuccess;
   dim3 grid(off), block(IDX_WAVES * 64);
-#define CSA_IDX_CASE(T, DI)                                                                     \
-  do {                                                                                          \
-    if (a.pro.on) hipLaunchKernelGGL((index_scores_kernel<T, DI, true>), grid, block, 0, st, a); \
-    else hipLaunchKernelGGL((index_scores_kernel<T, DI, false>), grid, block, 0, st, a);         \
+  if (a.pro.fp8 && p.idx_dim != 64 && p.idx_dim != 128) return hipErrorInvalidValue;
+#define CSA_IDX_LAUNCH(T, DI, PRO, F8) hipLaunchKernelGGL((index_scores_kernel<T, DI, PRO, F8>), grid, block, 0, st, a)
+#define CSA_IDX_CASE(T, DI)                          \
+  do {                                               \
+    if (a.pro.fp8) {                                 \
+      if (a.pro.on) CSA_IDX_LAUNCH(T, DI, true, true); \
+      else CSA_IDX_LAUNCH(T, DI, false, true);       \
+    } else if (a.pro.on) CSA_IDX_LAUNCH(T, DI, true, false); \
+    else CSA_IDX_LAUNCH(T, DI, false, false);        \
+  } while (0)
+#define CSA_IDX_CASE_NO8(T, DI)                      \
+  do {                                               \
+    if (a.pro.on) CSA_IDX_LAUNCH(T, DI, true, false); \
+    else CSA_IDX_LAUNCH(T, DI, false, false);        \
   } while (0)
   const bool bf = p.dtype == CSA_BF16;
   switch (p.idx_dim) {
-    case 16: if (bf) CSA_IDX_CASE(bf16, 16); else CSA_IDX_CASE(float, 16); break;
-    case 32: if (bf) CSA_IDX_CASE(bf16, 32); else CSA_IDX_CASE(float, 32); break;
+    case 16: if (bf) CSA_IDX_CASE_NO8(bf16, 16); else CSA_IDX_CASE_NO8(float, 16); break;
+    case 32: if (bf) CSA_IDX_CASE_NO8(bf16, 32); else CSA_IDX_CASE_NO8(float, 32); break;
     case 64: if (bf) CSA_IDX_CASE(bf16, 64); else CSA_IDX_CASE(float, 64); break;
     case 128: if (bf) CSA_IDX_CASE(bf16, 128); else CSA_IDX_CASE(float, 128); break;
     default: return hipErrorInvalidValue;
   }
 #undef CSA_IDX_CASE
+#undef CSA_IDX_CASE_NO8
+#undef CSA_IDX_LAUNCH
   return hipGetLastError();
 }
 

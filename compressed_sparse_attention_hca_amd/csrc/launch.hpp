@@ -19,7 +19,8 @@ hipError_t launch_index_scores(const csa_params_t& p, const void* q_idx, const f
                                const void* k_idx, float* scores, int64_t ld, int32_t t0,
                                int32_t nrows, hipStream_t st);
 
-// Indexer key prologue: k_out = round(Hn RoPE(k_idx, pos0 + s*ratio)).
+// Indexer key pass: k_out = round(Hn RoPE(k_idx, pos0 + s*ratio)) (prologue) and/or
+// the E4M3 rows (fp8), per p.flags.
 hipError_t launch_index_keys(const csa_params_t& p, const void* k_idx, void* k_out, hipStream_t st);
 
 // Indexer scores fused with the top-k selection (topk <= 512); scores stay on chip.

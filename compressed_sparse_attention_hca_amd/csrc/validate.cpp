@@ -38,7 +38,7 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
   if (p->B < 0 || p->S < 0) CSA_FAIL(CSA_ERR_INVALID_ARG, "B=%d S=%d must be >= 0", p->B, p->S);
   if (p->dtype != CSA_F32 && p->dtype != CSA_BF16)
     CSA_FAIL(CSA_ERR_INVALID_ARG, "dtype=%d is not CSA_F32 or CSA_BF16", p->dtype);
-  if (p->flags & ~(CSA_FLAG_NORM_WINDOW | CSA_FLAG_INDEX_PROLOGUE))
+  if (p->flags & ~(CSA_FLAG_NORM_WINDOW | CSA_FLAG_INDEX_PROLOGUE | CSA_FLAG_INDEX_FP8))
     CSA_FAIL(CSA_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   const uint32_t index_any = uint32_t(Need::INDEX) | uint32_t(Need::INDEX_KEYS);
   const bool compressed = (need & uint32_t(Need::COMPRESS)) || (need & index_any) ||
@@ -83,8 +83,14 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
     if (p->S / p->ratio > kMaxEntries)
       CSA_FAIL(CSA_ERR_UNSUPPORTED, "S/ratio=%d entries exceeds %d", p->S / p->ratio, kMaxEntries);
   }
+  if (need & uint32_t(Need::INDEX_KEYS)) {
+    if (!(p->flags & (CSA_FLAG_INDEX_PROLOGUE | CSA_FLAG_INDEX_FP8)))
+      CSA_FAIL(CSA_ERR_INVALID_ARG, "the key pass needs CSA_FLAG_INDEX_PROLOGUE or CSA_FLAG_INDEX_FP8");
+  }
+  if ((need & index_any) && (p->flags & CSA_FLAG_INDEX_FP8) && p->idx_dim != 64 && p->idx_dim != 128)
+    CSA_FAIL(CSA_ERR_UNSUPPORTED, "the FP8 indexer is compiled for idx_dim 64 and 128, not %d", p->idx_dim);
   // the indexer prologue rotates with the layer's RoPE inside the indexer dims
-  if ((need & uint32_t(Need::INDEX_KEYS)) || ((need & uint32_t(Need::INDEX)) && (p->flags & CSA_FLAG_INDEX_PROLOGUE))) {
+  if ((need & index_any) && (p->flags & CSA_FLAG_INDEX_PROLOGUE)) {
     if (p->rope_dim < 0 || p->rope_dim % 2 || p->rope_dim > p->idx_dim)
       CSA_FAIL(CSA_ERR_INVALID_ARG, "indexer prologue: rope_dim=%d must be even and <= idx_dim=%d",
                p->rope_dim, p->idx_dim);
@@ -113,7 +119,8 @@ WsPlan plan_workspace(const csa_params_t& p, int32_t op) {
     w.idx = take(B * S * (size_t)p.topk * 4);
     w.nvis = take(B * S * 4);
   }
-  if (idx && (p.flags & CSA_FLAG_INDEX_PROLOGUE)) w.k_rot = take(B * n * (size_t)p.idx_dim * es);
+  if (idx && (p.flags & CSA_FLAG_INDEX_FP8)) w.k_rot = take(B * n * (size_t)(p.idx_dim + 16));
+  else if (idx && (p.flags & CSA_FLAG_INDEX_PROLOGUE)) w.k_rot = take(B * n * (size_t)p.idx_dim * es);
   if (idx && p.topk > kFusedTopkMax) {  // separate scores + top-k kernels over chunks
     w.ld = (int64_t)align_up(n > 0 ? n : 1, 32);
     const size_t row_bytes = B * (size_t)w.ld * 4;

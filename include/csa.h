@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum {
   CSA_OK = 0,
@@ -83,6 +83,15 @@ typedef enum {
  * Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), and round() rounds to the
  * activation dtype.  The top-k is unchanged by T but not by the rotation. */
 #define CSA_FLAG_INDEX_PROLOGUE 2u
+/* FP8 indexer ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+ * Primus", closing remarks: an E4M3 path for the indexer QK; "fix(deepseek-v4) ...",
+ * Part 1 item 4: it changes the selection, so it is opt-in), CSA only, idx_dim 64 or
+ * 128.  Each q_I[t,h] and k_I[s] row (after the prologue, when both flags are set) is
+ * quantized to OCP E4M3 with its own scale: m = max |x|, codes = E4M3(x * (448 / m)),
+ * round to nearest even, scale = m / 448 (both divisions and the product in IEEE
+ * fp32; a zero row has codes 0, scale 0); the scores use the decoded operands
+ * codes * scale, accumulated in fp32 by the fp8 MFMA. */
+#define CSA_FLAG_INDEX_FP8 4u
 
 typedef struct {
   int32_t B;          /* batch */
@@ -142,19 +151,24 @@ csa_status_t csa_compress(const csa_params_t* p, const void* va, const void* ga,
 
 /* Stage 3, scores only (for checking): rows t0 .. t0+nrows-1 of every batch;
  * scores[b][t - t0][s] for s < n_visible(t), row stride ld floats (ld >= S/ratio);
- * entries s >= n_visible(t) are not written.  With CSA_FLAG_INDEX_PROLOGUE the
- * queries are rotated and the weights scaled inside the kernel, and k_idx must hold
- * keys already passed through csa_index_prologue_keys. */
+ * entries s >= n_visible(t) are not written.  With CSA_FLAG_INDEX_PROLOGUE and/or
+ * CSA_FLAG_INDEX_FP8 the queries are transformed and the weights scaled inside the
+ * kernel, and k_idx must hold the output of csa_index_keys for the same flags. */
 csa_status_t csa_index_scores(const csa_params_t* p, const void* q_idx, const float* w_idx,
                               const void* k_idx, float* scores, int64_t ld, int32_t t0,
                               int32_t nrows, void* stream);
 
-/* Indexer key prologue (CSA_FLAG_INDEX_PROLOGUE, see there):
- *   k_out[b,s] = round(Hn RoPE(k_idx[b,s], pos0 + s*ratio)), both [B,S/ratio,idx_dim]
- *   in the activation dtype; k_out must not overlap k_idx.  The flag need not be set
- *   in p; the other indexer fields and rope_dim, rope_theta, pos0 are used. */
-csa_status_t csa_index_prologue_keys(const csa_params_t* p, const void* k_idx, void* k_out,
-                                     void* stream);
+/* Indexer key pass for CSA_FLAG_INDEX_PROLOGUE and/or CSA_FLAG_INDEX_FP8 (at least one
+ * must be set in p->flags; see both).  k_idx [B,S/ratio,idx_dim] in the activation
+ * dtype.  k_out, which must not overlap k_idx:
+ *   - prologue only: [B,S/ratio,idx_dim] in the activation dtype,
+ *     k_out[b,s] = round(Hn RoPE(k_idx[b,s], pos0 + s*ratio));
+ *   - FP8: [B,S/ratio] rows of idx_dim + 16 bytes: the E4M3 codes of the row (after
+ *     the prologue, if set) with dim d at byte 64*(d/64) + 32*((d/8)%2) +
+ *     8*((d%64)/16) + d%8 (the fp8 MFMA operand order), then the fp32 scale, then 12
+ *     zero bytes.
+ * The other indexer fields and rope_dim, rope_theta, pos0 are used. */
+csa_status_t csa_index_keys(const csa_params_t* p, const void* k_idx, void* k_out, void* stream);
 
 /* Stage 3: indexer scores over visible entries and the top-k per query.
  *   idx [B,S,topk] int32: the min(topk, n_visible(t)) selected entries in ascending
@@ -162,7 +176,8 @@ csa_status_t csa_index_prologue_keys(const csa_params_t* p, const void* k_idx, v
  *   n_visible [B,S] int32.  ws: csa_workspace_bytes(p, CSA_OP_INDEX_TOPK) bytes (none
  *   when topk <= 512: the selection is made inside the indexer kernel and no score
  *   leaves the chip; larger topk scores query chunks into the workspace, then selects).
- *   With CSA_FLAG_INDEX_PROLOGUE the rotated keys are also kept in the workspace. */
+ *   With CSA_FLAG_INDEX_PROLOGUE or CSA_FLAG_INDEX_FP8 the key pass's output is also
+ *   kept in the workspace. */
 csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const float* w_idx,
                             const void* k_idx, int32_t* idx, int32_t* n_visible, void* ws,
                             size_t ws_bytes, void* stream);
@@ -206,7 +221,7 @@ typedef enum {
   CSA_KERNEL_TOPK = 3,        /* top-k selection (one launch per query chunk, topk > 512) */
   CSA_KERNEL_ATTENTION = 4,   /* sparse MQA + de-rotation */
   CSA_KERNEL_INDEX_TOPK = 5,  /* indexer scores fused with top-k (topk <= 512) */
-  CSA_KERNEL_INDEX_KEYS = 6   /* indexer key prologue (CSA_FLAG_INDEX_PROLOGUE) */
+  CSA_KERNEL_INDEX_KEYS = 6   /* indexer key pass (CSA_FLAG_INDEX_PROLOGUE / _FP8) */
 } csa_kernel_t;
 
 /* Number of events the traced variant of `op` (CSA_OP_CSA_FWD or CSA_OP_HCA_FWD)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 3
+    assert bd.lib.csa_abi_version() == 4
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -86,7 +86,7 @@ def call_compress(p, va=A, ga=A, vb=A, gb=A, bias=A, out=A):
     (dict(ratio=0), bd.CSA_ERR_INVALID_ARG),
     (dict(overlap=2), bd.CSA_ERR_INVALID_ARG),
     (dict(dtype=5), bd.CSA_ERR_INVALID_ARG),
-    (dict(flags=6), bd.CSA_ERR_INVALID_ARG),
+    (dict(flags=8), bd.CSA_ERR_INVALID_ARG),
     (dict(B=-1), bd.CSA_ERR_INVALID_ARG),
     (dict(rope_theta=0.0), bd.CSA_ERR_INVALID_ARG),
     (dict(rms_eps=float("nan")), bd.CSA_ERR_INVALID_ARG),
@@ -148,15 +148,39 @@ def test_index_prologue_validation_and_workspace():
         bd.lib.csa_trace_events(ctypes.byref(p_c1()), bd.OP_CSA_FWD) + 1
 
     def keys(p, k=A, out=A + (1 << 30)):
-        return bd.lib.csa_index_prologue_keys(ctypes.byref(p), k, out, None)
-    assert keys(p_c1(), out=A + 16) == bd.CSA_ERR_INVALID_ARG       # overlapping
+        return bd.lib.csa_index_keys(ctypes.byref(p), k, out, None)
+    assert keys(p_c1(**pro), out=A + 16) == bd.CSA_ERR_INVALID_ARG       # overlapping
     assert "overlaps" in bd.last_error()
-    assert keys(p_c1(), k=None) == bd.CSA_ERR_INVALID_ARG
-    assert keys(p_c1(), out=A + 8) == bd.CSA_ERR_INVALID_ARG        # misaligned
-    assert keys(p_c1(rope_dim=130)) == bd.CSA_ERR_INVALID_ARG
-    assert keys(p_c1(idx_dim=24)) == bd.CSA_ERR_INVALID_ARG
-    assert keys(p_c1(rope_theta=-1.0)) == bd.CSA_ERR_INVALID_ARG
-    assert keys(p_c1(flags=4)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(**pro), k=None) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(**pro), out=A + 8) == bd.CSA_ERR_INVALID_ARG        # misaligned
+    assert keys(p_c1(rope_dim=130, **pro)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(idx_dim=24, **pro)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(rope_theta=-1.0, **pro)) == bd.CSA_ERR_INVALID_ARG
+    assert keys(p_c1(flags=8)) == bd.CSA_ERR_INVALID_ARG                # unknown flag
+    assert keys(p_c1()) == bd.CSA_ERR_INVALID_ARG and "needs" in bd.last_error()
+
+
+def test_index_fp8_validation_and_workspace():
+    """The FP8 indexer runs on idx_dim 64 and 128; its key rows (codes, scale and
+    padding: idx_dim + 16 bytes) live in the workspace; the key pass's output rows
+    must not overlap its input."""
+    f8 = dict(flags=bd.FLAG_INDEX_FP8)
+
+    def topk(p, ws_bytes=1 << 40, ws=A):
+        return bd.lib.csa_index_topk(ctypes.byref(p), A, A, A, A, A, ws, ws_bytes, None)
+    assert topk(p_c1(idx_dim=32, **f8)) == bd.CSA_ERR_UNSUPPORTED
+    assert "FP8" in bd.last_error()
+    assert bd.workspace_bytes(p_c1(**f8), bd.OP_INDEX_TOPK) == 1024 * (128 + 16)
+    both = dict(flags=bd.FLAG_INDEX_FP8 | bd.FLAG_INDEX_PROLOGUE)
+    assert bd.workspace_bytes(p_c1(**both), bd.OP_INDEX_TOPK) == 1024 * (128 + 16)
+    need = bd.workspace_bytes(p_c1(**f8), bd.OP_INDEX_TOPK)
+    assert topk(p_c1(**f8), ws_bytes=need - 1) == bd.CSA_ERR_WORKSPACE
+    assert bd.lib.csa_trace_events(ctypes.byref(p_c1(**f8)), bd.OP_CSA_FWD) == \
+        bd.lib.csa_trace_events(ctypes.byref(p_c1()), bd.OP_CSA_FWD) + 1
+    # an output that starts inside the input (1024 rows of 256 bytes) overlaps it
+    assert bd.lib.csa_index_keys(ctypes.byref(p_c1(**f8)), A, A + 1024 * 256 - 16, None) == bd.CSA_ERR_INVALID_ARG
+    assert bd.lib.csa_index_keys(ctypes.byref(p_c1(idx_dim=16, **f8)), A, A + (1 << 30), None) == \
+        bd.CSA_ERR_UNSUPPORTED
 
 
 def test_index_scores_rejects_rows_and_ld():

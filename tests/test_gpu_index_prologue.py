@@ -70,7 +70,7 @@ def assert_rounded_alike(got, want, dtype, what):
 def test_key_prologue_parity(bd, name):
     cfg = KEY_CASES[name]
     inp = gen(cfg)
-    kr = bd.index_prologue_keys(bd.params(cfg), inp["k_idx"])
+    kr = bd.index_keys(bd.params(cfg), inp["k_idx"])
     torch.cuda.synchronize()
     for b in range(cfg.B):
         got = kr[b].float().cpu().double().numpy()
@@ -87,11 +87,11 @@ def oracle_scores(cfg, inp, b, t, k_rot):
 @pytest.mark.parametrize("name", ["C0", "C1", "idx64_rope32_B2"])
 def test_prologue_scores_parity(bd, name):
     """csa_index_scores with the flag (queries rotated and weights scaled in-kernel) on
-    keys from csa_index_prologue_keys, against the oracle's prologue scores."""
+    keys from csa_index_keys, against the oracle's prologue scores."""
     cfg = KEY_CASES[name]
     inp = gen(cfg)
     p = bd.params(cfg)
-    kr = bd.index_prologue_keys(p, inp["k_idx"])
+    kr = bd.index_keys(p, inp["k_idx"])
     sc = bd.index_scores(p, inp["q_idx"], inp["w_idx"], kr)
     torch.cuda.synchronize()
     got = sc.cpu().double().numpy()

@@ -154,9 +154,9 @@ def test_topk_parity_chunked_path(bd):
 
 # ------------------------------------------------------------- whole layer ---------
 
-def layer_check(bd, cfg, rows=None, sinks=None):
+def layer_check(bd, cfg, rows=None, sinks=None, sel_rel=1e-3):
     """sinks: optional [H] fp32 numpy softmax-sink logits, passed to the layer and the
-    oracle alike."""
+    oracle alike.  sel_rel: the near-tie bound of the selection check."""
     inp = gen(cfg)
     if sinks is not None:
         sinks = np.asarray(sinks, dtype=np.float32)  # the values the kernel sees
@@ -174,7 +174,8 @@ def layer_check(bd, cfg, rows=None, sinks=None):
         for (b, t) in rows:
             n = O.visible_entries(t, cfg.ratio)
             assert nv_np[b, t] == n
-            swaps += check_selection(idx_np[b, t], n, cfg.topk, ora["scores"][(b, t)], ora["sel"][(b, t)])
+            swaps += check_selection(idx_np[b, t], n, cfg.topk, ora["scores"][(b, t)], ora["sel"][(b, t)],
+                                     sel_rel)
             sel_override[(b, t)] = idx_np[b, t][:min(cfg.topk, n)]
     ora = O.layer_rows(cfg, lz, rows, sel_override=sel_override, sinks=sinks)
     got = np.stack([o[b, t].float().cpu().double().numpy() for (b, t) in rows])
