@@ -196,3 +196,19 @@ def brute_layer(cfg, inp, b=0, sinks=None):
             o_t.append(brute_rope(u, -(pos0 + t), R, theta))
         res["o"].append(o_t)
     return res
+
+
+def brute_kl_target(cfg, inp, kv_c, t, sel, b=0):
+    """Head-mean of the per-head softmax over the selected entries' logits, scalar loops."""
+    H, D = cfg.H, cfg.D
+    q = [[float(x) for x in inp["q"][b][t][h]] for h in range(H)]
+    tot = [0.0] * len(sel)
+    for h in range(H):
+        qh = brute_rope(q[h], cfg.pos0 + t, cfg.rope_dim, cfg.rope_theta)
+        z = [sum(qh[d] * kv_c[s][d] for d in range(D)) * cfg.softmax_scale for s in sel]
+        mx = max(z)
+        e = [math.exp(v - mx) for v in z]
+        den = sum(e)
+        for k in range(len(sel)):
+            tot[k] += e[k] / den / H
+    return tot

@@ -48,6 +48,7 @@ __all__ = [
     "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
     "hadamard", "round_to", "index_prologue", "index_temperature", "e4m3", "quant_e4m3_rows",
+    "kl_target_row", "kl_target",
 ]
 
 
@@ -281,6 +282,33 @@ def attend_row(qr_t, keys, scale: float, sink=None):
     e = np.exp(z - m)
     P = e / (np.sum(e, axis=1, keepdims=True) + np.exp(sk - m))
     return P @ keys, P
+
+
+def kl_target_row(qr_t, kv_c, sel, scale: float) -> np.ndarray:
+    """Target distribution of the indexer's distillation loss for one query
+    ("fix(deepseek-v4): correct V4-Flash attention math", Part 1 item 5: KL(attention
+    || indexer) over the selected entries, kept in [B, S, K]; item 11: the head sum
+    taken inside the loop, never forming the per-head tensor).  The main attention's
+    logits over the selected entries only, z[h,k] = (q~[h] . kv_c[sel[k]]) * scale, a
+    softmax per head over those entries, then the mean over heads:
+        T[k] = (1/H) sum_h softmax_k(z[h, :])[k],  summing to 1 over the selection.
+    qr_t [H, D] rotated query, kv_c [n, D], sel the selected indices.  Returns [len(sel)]."""
+    if len(sel) == 0:
+        return np.zeros(0)
+    z = (qr_t @ kv_c[np.asarray(sel)].T) * scale
+    m = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return np.mean(e / np.sum(e, axis=1, keepdims=True), axis=0)
+
+
+def kl_target(cfg, inp: dict, rows, sel: dict, kv_c: dict) -> dict:
+    """kl_target_row for each (b, t) in rows, with the query rotated at pos0 + t, the
+    scale D**-0.5, and sel[(b, t)] / kv_c[b] from the layer (layer_rows)."""
+    out = {}
+    for (b, t) in rows:
+        qr = rope(_as64(inp["q"][b, t]), cfg.pos0 + t, cfg.rope_dim, cfg.rope_theta)
+        out[(b, t)] = kl_target_row(qr, np.asarray(kv_c[b], dtype=np.float64), sel[(b, t)], cfg.D ** -0.5)
+    return out
 
 
 def _as64(a):

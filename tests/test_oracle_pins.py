@@ -604,3 +604,44 @@ def test_fp8_scores_track_the_exact_scores():
         assert np.all(np.abs(b["scores"][(0, t)] - a["scores"][(0, t)]) <= bound)
         keep.append(len(set(a["sel"][(0, t)]) & set(b["sel"][(0, t)])) / cfg.topk)
     assert np.mean(keep) > 0.6
+
+
+# ----------------------------------------------------------- KL target ----------
+# "fix(deepseek-v4): correct V4-Flash attention math", Part 1 items 5 and 11.
+
+def test_kl_target_closed_forms(rng):
+    """Zero queries give the uniform target 1/|Sel|; one selected entry gets 1; the
+    target sums to 1 and is positive; relabelling the selection permutes it."""
+    H, D, n = 3, 16, 9
+    kv = rng.normal(size=(n, D))
+    sel = np.array([1, 4, 5, 8])
+    assert np.allclose(O.kl_target_row(np.zeros((H, D)), kv, sel, 0.25), 0.25, atol=1e-15)
+    q = rng.normal(size=(H, D))
+    assert np.allclose(O.kl_target_row(q, kv, [6], 0.25), [1.0], atol=1e-15)
+    t = O.kl_target_row(q, kv, sel, 0.25)
+    assert abs(t.sum() - 1) < 1e-14 and np.all(t > 0)
+    perm = np.array([2, 0, 3, 1])
+    assert np.allclose(O.kl_target_row(q, kv, sel[perm], 0.25), t[perm], atol=1e-15)
+
+
+def test_kl_target_is_the_attention_restricted_to_the_selection():
+    """Without a window the layer's softmax runs over the selected entries alone, so the
+    target is the head mean of the layer's own probabilities P."""
+    cfg = tiny("csa", S=40, window=0, topk=4)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in (7, 23, 39)]
+    r = O.layer_rows(cfg, inp, rows, want_p=True)
+    kt = O.kl_target(cfg, inp, rows, r["sel"], r["kv_c"])
+    for k in rows:
+        assert np.allclose(kt[k], np.mean(r["P"][k], axis=0), atol=1e-14)
+
+
+def test_kl_target_matches_brute_force():
+    cfg = tiny("csa", S=24, pos0=11)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(3, 24, 4)]
+    r = O.layer_rows(cfg, inp, rows)
+    kt = O.kl_target(cfg, inp, rows, r["sel"], r["kv_c"])
+    for (b, t) in rows:
+        want = brute.brute_kl_target(cfg, inp, r["kv_c"][0], t, list(r["sel"][(b, t)]))
+        assert np.allclose(kt[(b, t)], want, atol=1e-13)
