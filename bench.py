@@ -55,6 +55,8 @@ def kernel_work(cfg, wl):
         work["indexer"] = (f["indexer"], "flops", "mfma")
         # fused indexer + selection: the indexer's FLOPs (the selection reads no scores)
         work["index_topk"] = (f["indexer"], "flops", "mfma")
+        # distillation target: one QK product per (query, selected entry) pair
+        work["kl_target"] = (2 * cfg.H * cfg.D * wl.layer_flops(cfg)["selected_pairs"], "flops", "mfma")
         # indexer key prologue: read and write every indexer key once
         work["index_keys"] = (2 * B * (S // cfg.ratio) * cfg.idx_dim * es, "bytes", "hbm")
         # read every visible score once, write K indices + n_visible per row
@@ -310,6 +312,8 @@ def main():
                     help="CSA: indexer prologue on (RoPE + Hadamard of q_I and k_I, temperature on w)")
     ap.add_argument("--index-fp8", action="store_true",
                     help="CSA: FP8 (E4M3, per-row scales) indexer operands")
+    ap.add_argument("--kl-target", action="store_true",
+                    help="CSA: each step also forms the indexer distillation target (csa_kl_target)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -361,6 +365,24 @@ def main():
     ws = bd.workspace(p, op, dev)
     o = torch.empty_like(inp["q"])
     traces = [bd.LayerTrace(p) for _ in range(args.steps)]
+    kl = None
+    if args.kl_target and cfg.kind == "csa":
+        n = cfg.S // cfg.ratio
+        kl = {"kv_c_out": torch.empty((cfg.B, n, cfg.D), dtype=inp["q"].dtype, device=dev),
+              "idx_out": torch.empty((cfg.B, cfg.S, cfg.topk), dtype=torch.int32, device=dev),
+              "target": torch.empty((cfg.B, cfg.S, cfg.topk), dtype=torch.float32, device=dev),
+              "ev": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.steps)]}
+
+    def kl_step(k=None):
+        if kl is None:
+            return
+        if k is not None:
+            kl["ev"][k][0].record()
+        bd.kl_target(p, inp["q"], kl["kv_c_out"], kl["idx_out"], kl["target"])
+        if k is not None:
+            kl["ev"][k][1].record()
+    layer_out = {} if kl is None else {"kv_c_out": kl["kv_c_out"], "idx_out": kl["idx_out"]}
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -372,12 +394,14 @@ def main():
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        bd.layer_fwd(p, inp, o=o, ws=ws)
+        bd.layer_fwd(p, inp, o=o, ws=ws, **layer_out)
+        kl_step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for k in range(args.steps):
-        bd.layer_fwd_traced(p, inp, traces[k], o=o, ws=ws)
+        bd.layer_fwd_traced(p, inp, traces[k], o=o, ws=ws, **layer_out)
+        kl_step(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -389,6 +413,9 @@ def main():
         for k, v in ms.items():
             tot[k] = tot.get(k, 0.0) + v / args.steps
             launches[k] = nl[k]
+    if kl is not None:
+        tot["kl_target"] = sum(a.elapsed_time(b) for a, b in kl["ev"]) / args.steps
+        launches["kl_target"] = 1
     work = kernel_work(cfg, wl)
     kernels = {}
     for k, v in tot.items():
@@ -408,6 +435,8 @@ def main():
             "avg_launch_ms": d["avg_launch_ms"]}
 
     f = wl.layer_flops(cfg)
+    if kl is not None:  # the step also forms the distillation target
+        f = dict(f, total=f["total"] + work["kl_target"][0])
     tokens = cfg.B * cfg.S
     value = tokens / (ms_step * 1e-3)
     tflops = f["total"] / (ms_step * 1e-3) / 1e12
@@ -416,7 +445,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
+        "config": {"workload": cfg.name + ("+kl_target" if kl is not None else ""), "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
                    "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
                    "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue),

@@ -60,6 +60,7 @@ def _load():
         "csa_index_scores": [P, V, V, V, V, I64, I32, I32, V],
         "csa_index_topk": [P, V, V, V, V, V, V, SZ, V],
         "csa_index_keys": [P, V, V, V],
+        "csa_kl_target": [P, V, V, V, V, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
@@ -91,7 +92,7 @@ lib = _load()
 
 EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_keys",
            "csa_sparse_mqa_fwd",
-           "csa_sparse_mqa_fwd_sink", "csa_fwd",
+           "csa_sparse_mqa_fwd_sink", "csa_kl_target", "csa_fwd",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
@@ -208,6 +209,14 @@ def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream
     return o
 
 
+def kl_target(p: Params, q, kv_c, idx, target=None, stream=None) -> torch.Tensor:
+    """csa_kl_target: [B, S, topk] fp32 target of the indexer's distillation loss."""
+    if target is None:
+        target = torch.empty((p.B, p.S, p.topk), dtype=torch.float32, device=q.device)
+    check(lib.csa_kl_target(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(idx), _ptr(target), _stream(stream)))
+    return target
+
+
 def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=None) -> Inputs:
     g = inp.get
     return Inputs(q=_ptr(g("q")), kv_raw=_ptr(g("kv_raw")), va=_ptr(g("va")), ga=_ptr(g("ga")),
@@ -257,14 +266,15 @@ class LayerTrace:
         return ms, launches
 
 
-def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, stream=None):
+def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, stream=None,
+                     kv_c_out=None, idx_out=None, n_visible_out=None):
     q = inp["q"]
     if o is None:
         o = torch.empty_like(q)
     op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
     if ws is None:
         ws = workspace(p, op, q.device)
-    s = make_inputs_struct(inp)
+    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
     f = lib.csa_fwd_traced if p.overlap else lib.hca_fwd_traced
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream),
             trace.handles, trace.kinds, trace.n))

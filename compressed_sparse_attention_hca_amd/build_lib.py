@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["abi.cpp", "validate.cpp", "compress.hip", "indexer.hip", "topk.hip", "sparse_mqa.hip"]
+SOURCES = ["abi.cpp", "validate.cpp", "compress.hip", "indexer.hip", "topk.hip", "sparse_mqa.hip",
+           "kl_target.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

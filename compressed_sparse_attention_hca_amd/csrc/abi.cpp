@@ -253,6 +253,18 @@ csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const
   return CSA_OK;
 }
 
+csa_status_t csa_kl_target(const csa_params_t* p, const void* q, const void* kv_c,
+                           const int32_t* idx, float* target, void* stream) {
+  CSA_TRY(validate_params(p, Need::MQA | Need::SELECT, false));
+  if (empty(p)) return CSA_OK;
+  CSA_TRY(check_ptr(q, "q"));
+  CSA_TRY(check_ptr(kv_c, "kv_c"));
+  CSA_TRY(check_ptr(idx, "idx"));
+  CSA_TRY(check_ptr(target, "target"));
+  CSA_HIP(launch_kl_target(*p, q, kv_c, idx, target, as_stream(stream)), "KL target launch");
+  return CSA_OK;
+}
+
 static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
                           size_t ws_bytes, void* stream, bool csa_layer, Tracer* tr) {
   const uint32_t need = csa_layer ? (Need::COMPRESS | Need::INDEX | Need::MQA) : (Need::COMPRESS | Need::MQA);

@@ -35,6 +35,10 @@ hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q,
                              const void* kv_w, const int32_t* idx, const float* sinks, void* o,
                              hipStream_t st);
 
+// Target of the indexer's distillation loss over the selected entries ([B,S,topk] fp32).
+hipError_t launch_kl_target(const csa_params_t& p, const void* q, const void* kv_c, const int32_t* idx,
+                            float* target, hipStream_t st);
+
 hipError_t launch_debug_layout(const csa_params_t& p, int32_t* comp_pos, int32_t* n_visible,
                                int32_t* win_lo, hipStream_t st);
 

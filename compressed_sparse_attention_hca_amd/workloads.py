@@ -233,7 +233,8 @@ def layer_flops(cfg: LayerConfig) -> Dict[str, float]:
     attn = 4.0 * cfg.H * cfg.D * (sel + win) * B
     idx = 2.0 * cfg.idx_heads * cfg.idx_dim * vis * B if cfg.kind == CSA else 0.0
     return {"attention": attn, "indexer": idx, "total": attn + idx,
-            "keys": float((sel + win) * B), "visible_pairs": float(vis * B)}
+            "keys": float((sel + win) * B), "visible_pairs": float(vis * B),
+            "selected_pairs": float(sel * B)}
 
 
 def page_convention_attention_flops(cfg: LayerConfig) -> float:

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum {
   CSA_OK = 0,
@@ -203,6 +203,19 @@ csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void
 csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const void* kv_c,
                                      const void* kv_raw, const int32_t* idx, const float* sinks,
                                      void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Target distribution of the indexer's distillation loss ("fix(deepseek-v4): correct
+ * V4-Flash attention math", Part 1 item 5: KL(attention || indexer) over the selected
+ * entries, kept in [B, S, K]; item 11: the head sum inside the loop, so the per-head
+ * tensor never exists):
+ *   target[b,t,k] = (1/H) sum_h softmax_k( (RoPE(q[b,t,h], pos0 + t) . kv_c[b, idx[b,t,k]]) * softmax_scale )
+ * for k < min(topk, n_visible(t)), the softmax over those selected entries only (no
+ * window), the logits as the attention forms them (activation-dtype operands, fp32
+ * accumulation).  q [B,S,H,D], kv_c [B,S/ratio,D] rotated entries, idx [B,S,topk] as
+ * csa_index_topk writes it; target [B,S,topk] fp32, 0 past the selection.  An index
+ * outside 0..n_visible(t)-1 is left out of the softmax and gets 0. */
+csa_status_t csa_kl_target(const csa_params_t* p, const void* q, const void* kv_c,
+                           const int32_t* idx, float* target, void* stream);
 
 /* Fused CSA layer (stages 1-4, overlap must be 1). */
 csa_status_t csa_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 4
+    assert bd.lib.csa_abi_version() == 5
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -245,3 +245,14 @@ def test_empty_problem_is_a_noop():
     assert call_compress(p, va=None, ga=None, vb=None, gb=None, bias=None, out=None) == bd.CSA_OK
     p = p_c1(B=0)
     assert bd.lib.csa_sparse_mqa_fwd(ctypes.byref(p), None, None, None, None, None, None, 0, None) == bd.CSA_OK
+
+
+def test_kl_target_rejects():
+    def call(p, q=A, kv=A, idx=A, out=A):
+        return bd.lib.csa_kl_target(ctypes.byref(p), q, kv, idx, out, None)
+    assert call(p_c1(), idx=None) == bd.CSA_ERR_INVALID_ARG and "idx" in bd.last_error()
+    assert call(p_c1(), out=None) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), q=A + 4) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(topk=0)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(H=65)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
