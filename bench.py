@@ -337,7 +337,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the layer's multi-GPU sharding is a "
+        print("bench.py: runs on one GPU only; the layer's multi-GPU sharding is a "
               "design note, not built. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

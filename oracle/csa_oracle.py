@@ -16,7 +16,7 @@ beyond looping over queries.  Sources, cited by page title and section:
           section "Kernel fusions" (compressor pooling, interleaved partial RoPE,
           RMSNorm).
 
-Readings taken where the pages leave a step open (listed in the design doc as well):
+Readings taken where the pages leave a step open:
   * CSA entry 0 has no previous group: those slots get logit -inf.
   * Bias row j is pooling slot j in token order (CSA: rows 0..r-1 are the previous
     group read from the b projections, rows r..2r-1 the entry's own group read from
