@@ -916,8 +916,12 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int hh = hb * 32 + 8 * j + 4 * g + i;
+          // The prologue's temperature is left out here: it scales every score of the
+          // query by one positive constant, which leaves the top-k unchanged, and this
+          // kernel writes only the selection.  (The selection's work depends on the
+          // scores' bit patterns: at C3 a scale of 1/90.5 costs 0.5 ms more than any
+          // power of two.)  index_scores_kernel, whose scores are its output, applies it.
           float wv = v[i];
-          if constexpr (PRO) wv *= a.pro.w_scale;
           if constexpr (F8) wv *= sq[i];
           w[hb][4 * j + i] = (q_ok && hh < a.HI) ? wv : 0.f;
         }
