@@ -81,7 +81,9 @@ typedef enum {
  * where RoPE is the layer's (interleaved pairs on the last rope_dim dims, base
  * rope_theta; rope_dim must be <= idx_dim), Hn = H / sqrt(idx_dim) is the normalised
  * Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), and round() rounds to the
- * activation dtype.  The top-k is unchanged by T but not by the rotation. */
+ * activation dtype.  The top-k is unchanged by T but not by the rotation:
+ * csa_index_scores writes the scores with T, while the fused selection of
+ * csa_index_topk / csa_fwd (topk <= 512) ranks them without it. */
 #define CSA_FLAG_INDEX_PROLOGUE 2u
 /* FP8 indexer ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
  * Primus", closing remarks: an E4M3 path for the indexer QK; "fix(deepseek-v4) ...",
