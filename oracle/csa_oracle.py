@@ -48,7 +48,7 @@ __all__ = [
     "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
     "hadamard", "round_to", "index_prologue", "index_temperature", "e4m3", "quant_e4m3_rows",
-    "kl_target_row", "kl_target",
+    "kl_target_row", "kl_target", "attend_row_bwd_dq", "layer_dq_rows",
 ]
 
 
@@ -308,6 +308,51 @@ def kl_target(cfg, inp: dict, rows, sel: dict, kv_c: dict) -> dict:
     for (b, t) in rows:
         qr = rope(_as64(inp["q"][b, t]), cfg.pos0 + t, cfg.rope_dim, cfg.rope_theta)
         out[(b, t)] = kl_target_row(qr, np.asarray(kv_c[b], dtype=np.float64), sel[(b, t)], cfg.D ** -0.5)
+    return out
+
+
+def attend_row_bwd_dq(qr_t, keys, scale: float, du):
+    """Gradient of one query's attention output with respect to its rotated query
+    (the dQ part of the backward, "Enabling DeepSeek-V4-Flash Training on AMD Instinct
+    MI355X GPUs with Primus", section "Attention kernels for the three layer types":
+    dQ, with delta = rowsum(O * dO) computed inside it).  With P = softmax(z),
+    z = (qr . key) * scale and u = sum P key:
+        dP[h,k] = du[h] . key_k,  delta[h] = sum_k P dP = du[h] . u[h],
+        dz = P (dP - delta),      dqr[h] = scale * sum_k dz[h,k] key_k.
+    qr_t [H, D] rotated query, keys [nk, D], du [H, D] the gradient of u.  Returns
+    (dqr [H, D], delta [H])."""
+    z = (qr_t @ keys.T) * scale
+    m = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - m)
+    P = e / np.sum(e, axis=1, keepdims=True)
+    dP = du @ keys.T
+    delta = np.sum(P * dP, axis=1)
+    dz = P * (dP - delta[:, None])
+    return scale * (dz @ keys), delta
+
+
+def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None) -> dict:
+    """dL/dq for the query rows `rows` given dL/do[(b, t)] [H, D]: the output's
+    de-rotation transposes to a rotation of do by +(pos0 + t) (du), the query's
+    rotation to a rotation of dqr by -(pos0 + t).  Keys, selection and window as in
+    layer_rows (`sel` and `kv_c` may come from a layer_rows result)."""
+    R, theta, pos0 = cfg.rope_dim, cfg.rope_theta, cfg.pos0
+    scale = cfg.D ** -0.5
+    if sel is None or kv_c is None:
+        r = layer_rows(cfg, inp, rows)
+        sel, kv_c = r["sel"], r["kv_c"]
+    out = {}
+    for (b, t) in rows:
+        lo, hi = window_bounds(t, cfg.window)
+        win = rotate_window(_as64(inp["kv_raw"][b][lo:hi + 1]), R, theta, cfg.rms_eps, pos0 + lo,
+                            bool(getattr(cfg, "norm_window", False)))
+        ent = np.asarray(kv_c[b], dtype=np.float64)[np.asarray(sel[(b, t)], dtype=np.int64)] \
+            if cfg.kind != "swa" else np.zeros((0, cfg.D))
+        keys = np.concatenate([ent, win], axis=0)
+        qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
+        du = rope(np.asarray(do[(b, t)], dtype=np.float64), pos0 + t, R, theta)
+        dqr, _ = attend_row_bwd_dq(qr, keys, scale, du)
+        out[(b, t)] = rope(dqr, -(pos0 + t), R, theta)
     return out
 
 

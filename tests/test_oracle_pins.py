@@ -645,3 +645,57 @@ def test_kl_target_matches_brute_force():
     for (b, t) in rows:
         want = brute.brute_kl_target(cfg, inp, r["kv_c"][0], t, list(r["sel"][(b, t)]))
         assert np.allclose(kt[(b, t)], want, atol=1e-13)
+
+
+# ------------------------------------------------------------ dQ backward ----------
+# "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
+# "Attention kernels for the three layer types": the backward's dQ kernel with delta.
+
+@pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
+def test_dq_matches_finite_differences(kind, rng):
+    """Central differences of the forward oracle's loss L = sum(o * do) in each query
+    coordinate (the selection is held fixed, as the backward holds it)."""
+    cfg = tiny(kind, S=24, pos0=5, H=2, D=8, rope_dim=4)
+    inp = to_np(wl.make_inputs(cfg))
+    t = 17
+    rows = [(0, t)]
+    base = O.layer_rows(cfg, inp, rows)
+    sel = base["sel"]
+    do = {(0, t): rng.normal(size=(cfg.H, cfg.D))}
+    dq = O.layer_dq_rows(cfg, inp, rows, do, sel, base["kv_c"])[(0, t)]
+    eps = 1e-6
+    for h in range(cfg.H):
+        for d in range(cfg.D):
+            qp, qm = inp["q"].copy(), inp["q"].copy()
+            qp[0, t, h, d] += eps
+            qm[0, t, h, d] -= eps
+            lp = np.sum(O.layer_rows(cfg, dict(inp, q=qp), rows, sel_override=sel)["o"][(0, t)] * do[(0, t)])
+            lm = np.sum(O.layer_rows(cfg, dict(inp, q=qm), rows, sel_override=sel)["o"][(0, t)] * do[(0, t)])
+            assert abs((lp - lm) / (2 * eps) - dq[h, d]) < 1e-7
+
+
+def test_dq_matches_torch_autograd(rng):
+    """torch autograd through an fp64 softmax attention written with torch ops."""
+    H, D, nk, scale = 3, 16, 11, 0.25
+    q = rng.normal(size=(H, D))
+    keys = rng.normal(size=(nk, D))
+    du = rng.normal(size=(H, D))
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(keys)
+    u = torch.softmax((qt @ kt.T) * scale, dim=1) @ kt
+    (u * torch.tensor(du)).sum().backward()
+    dqr, delta = O.attend_row_bwd_dq(q, keys, scale, du)
+    assert np.allclose(dqr, qt.grad.numpy(), atol=1e-12)
+    assert np.allclose(delta, np.sum(u.detach().numpy() * du, axis=1), atol=1e-12)
+
+
+def test_dq_closed_forms(rng):
+    """One key: the softmax is constant, so dq = 0; equal keys: likewise; delta is
+    rowsum(u * du)."""
+    H, D = 2, 6
+    q, du = rng.normal(size=(H, D)), rng.normal(size=(H, D))
+    k1 = rng.normal(size=(1, D))
+    dq, delta = O.attend_row_bwd_dq(q, k1, 0.5, du)
+    assert np.allclose(dq, 0, atol=1e-15) and np.allclose(delta, du @ k1[0], atol=1e-15)
+    dq2, _ = O.attend_row_bwd_dq(q, np.repeat(k1, 4, axis=0), 0.5, du)
+    assert np.allclose(dq2, 0, atol=1e-14)
