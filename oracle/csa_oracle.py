@@ -311,7 +311,7 @@ def kl_target(cfg, inp: dict, rows, sel: dict, kv_c: dict) -> dict:
     return out
 
 
-def attend_row_bwd_dq(qr_t, keys, scale: float, du):
+def attend_row_bwd_dq(qr_t, keys, scale: float, du, sink=None):
     """Gradient of one query's attention output with respect to its rotated query
     (the dQ part of the backward, "Enabling DeepSeek-V4-Flash Training on AMD Instinct
     MI355X GPUs with Primus", section "Attention kernels for the three layer types":
@@ -319,25 +319,23 @@ def attend_row_bwd_dq(qr_t, keys, scale: float, du):
     z = (qr . key) * scale and u = sum P key:
         dP[h,k] = du[h] . key_k,  delta[h] = sum_k P dP = du[h] . u[h],
         dz = P (dP - delta),      dqr[h] = scale * sum_k dz[h,k] key_k.
-    qr_t [H, D] rotated query, keys [nk, D], du [H, D] the gradient of u.  Returns
-    (dqr [H, D], delta [H])."""
-    z = (qr_t @ keys.T) * scale
-    m = np.max(z, axis=1, keepdims=True)
-    e = np.exp(z - m)
-    P = e / np.sum(e, axis=1, keepdims=True)
+    qr_t [H, D] rotated query, keys [nk, D], du [H, D] the gradient of u.  A sink
+    (attend_row) only changes P's denominator: it carries no value, so it adds no term
+    to dP or delta.  Returns (dqr [H, D], delta [H])."""
+    _, P = attend_row(qr_t, keys, scale, sink)
     dP = du @ keys.T
     delta = np.sum(P * dP, axis=1)
     dz = P * (dP - delta[:, None])
     return scale * (dz @ keys), delta
 
 
-def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None) -> dict:
+def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None, sinks=None) -> dict:
     """dL/dq for the query rows `rows` given dL/do[(b, t)] [H, D]: the output's
     de-rotation transposes to a rotation of do by +(pos0 + t) (du), the query's
     rotation to a rotation of dqr by -(pos0 + t).  Keys, selection and window as in
     layer_rows (`sel` and `kv_c` may come from a layer_rows result)."""
     R, theta, pos0 = cfg.rope_dim, cfg.rope_theta, cfg.pos0
-    scale = cfg.D ** -0.5
+    scale = cfg.D ** -0.5 if getattr(cfg, "softmax_scale", None) is None else cfg.softmax_scale
     if sel is None or kv_c is None:
         r = layer_rows(cfg, inp, rows)
         sel, kv_c = r["sel"], r["kv_c"]
@@ -351,7 +349,7 @@ def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None) -
         keys = np.concatenate([ent, win], axis=0)
         qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
         du = rope(np.asarray(do[(b, t)], dtype=np.float64), pos0 + t, R, theta)
-        dqr, _ = attend_row_bwd_dq(qr, keys, scale, du)
+        dqr, _ = attend_row_bwd_dq(qr, keys, scale, du, sinks)
         out[(b, t)] = rope(dqr, -(pos0 + t), R, theta)
     return out
 

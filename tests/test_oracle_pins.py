@@ -651,8 +651,8 @@ def test_kl_target_matches_brute_force():
 # "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
 # "Attention kernels for the three layer types": the backward's dQ kernel with delta.
 
-@pytest.mark.parametrize("kind", ["csa", "hca", "swa"])
-def test_dq_matches_finite_differences(kind, rng):
+@pytest.mark.parametrize("kind,with_sink", [("csa", False), ("hca", False), ("swa", False), ("csa", True)])
+def test_dq_matches_finite_differences(kind, with_sink, rng):
     """Central differences of the forward oracle's loss L = sum(o * do) in each query
     coordinate (the selection is held fixed, as the backward holds it)."""
     cfg = tiny(kind, S=24, pos0=5, H=2, D=8, rope_dim=4)
@@ -662,15 +662,18 @@ def test_dq_matches_finite_differences(kind, rng):
     base = O.layer_rows(cfg, inp, rows)
     sel = base["sel"]
     do = {(0, t): rng.normal(size=(cfg.H, cfg.D))}
-    dq = O.layer_dq_rows(cfg, inp, rows, do, sel, base["kv_c"])[(0, t)]
+    sinks = rng.normal(size=cfg.H) if with_sink else None
+    dq = O.layer_dq_rows(cfg, inp, rows, do, sel, base["kv_c"], sinks=sinks)[(0, t)]
     eps = 1e-6
     for h in range(cfg.H):
         for d in range(cfg.D):
             qp, qm = inp["q"].copy(), inp["q"].copy()
             qp[0, t, h, d] += eps
             qm[0, t, h, d] -= eps
-            lp = np.sum(O.layer_rows(cfg, dict(inp, q=qp), rows, sel_override=sel)["o"][(0, t)] * do[(0, t)])
-            lm = np.sum(O.layer_rows(cfg, dict(inp, q=qm), rows, sel_override=sel)["o"][(0, t)] * do[(0, t)])
+            lp = np.sum(O.layer_rows(cfg, dict(inp, q=qp), rows, sel_override=sel,
+                                     sinks=sinks)["o"][(0, t)] * do[(0, t)])
+            lm = np.sum(O.layer_rows(cfg, dict(inp, q=qm), rows, sel_override=sel,
+                                     sinks=sinks)["o"][(0, t)] * do[(0, t)])
             assert abs((lp - lm) / (2 * eps) - dq[h, d]) < 1e-7
 
 
