@@ -63,6 +63,7 @@ def _load():
         "csa_kl_target": [P, V, V, V, V, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
+        "csa_sparse_mqa_bwd_dq": [P, V, V, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "hca_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "csa_debug_layout": [P, V, V, V, V],
@@ -92,7 +93,7 @@ lib = _load()
 
 EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_keys",
            "csa_sparse_mqa_fwd",
-           "csa_sparse_mqa_fwd_sink", "csa_kl_target", "csa_fwd",
+           "csa_sparse_mqa_fwd_sink", "csa_sparse_mqa_bwd_dq", "csa_kl_target", "csa_fwd",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
@@ -207,6 +208,20 @@ def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream
         check(lib.csa_sparse_mqa_fwd_sink(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx),
                                           _ptr(sinks), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
     return o
+
+
+def sparse_mqa_bwd_dq(p: Params, q, kv_c, kv_raw, idx, o, d_o, dq=None, ws=None, stream=None,
+                      sinks=None) -> torch.Tensor:
+    """csa_sparse_mqa_bwd_dq: dL/dq [B,S,H,D] of sparse_mqa_fwd (same arguments and
+    sinks), given its output o and dL/do."""
+    if dq is None:
+        dq = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(p, OP_SPARSE_MQA, q.device)
+    check(lib.csa_sparse_mqa_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx),
+                                    _ptr(sinks), _ptr(o), _ptr(d_o), _ptr(dq), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return dq
 
 
 def kl_target(p: Params, q, kv_c, idx, target=None, stream=None) -> torch.Tensor:

@@ -4,6 +4,7 @@
 
 #include "csa.h"
 #include "launch.hpp"
+#include "mqa_bwd.hpp"
 #include "validate.hpp"
 
 using namespace csa;
@@ -250,6 +251,36 @@ csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const
   CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
   const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
   CSA_HIP(launch_sparse_mqa(*p, mode, q, kv_c, kv_w, idx, sinks, o, st), "attention launch");
+  return CSA_OK;
+}
+
+csa_status_t csa_sparse_mqa_bwd_dq(const csa_params_t* p, const void* q, const void* kv_c,
+                                   const void* kv_raw, const int32_t* idx, const float* sinks,
+                                   const void* o, const void* d_o, void* dq, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const bool window_only = kv_c == nullptr;
+  CSA_TRY(validate_params(p, uint32_t(Need::MQA) | (idx ? uint32_t(Need::SELECT) : 0u), window_only));
+  if (window_only && idx) {
+    set_error("idx given without kv_c");
+    return CSA_ERR_INVALID_ARG;
+  }
+  if (empty(p)) return CSA_OK;
+  CSA_TRY(check_ptr(q, "q"));
+  CSA_TRY(check_ptr(kv_raw, "kv_raw"));
+  CSA_TRY(check_ptr(o, "o"));
+  CSA_TRY(check_ptr(d_o, "d_o"));
+  CSA_TRY(check_ptr(dq, "dq"));
+  CSA_TRY(check_optional(kv_c, "kv_c"));
+  CSA_TRY(check_optional(idx, "idx"));
+  CSA_TRY(check_optional(sinks, "sinks"));
+  WsPlan plan;
+  CSA_TRY(check_ws(p, CSA_OP_SPARSE_MQA, ws, ws_bytes, &plan));
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  const hipStream_t st = as_stream(stream);
+  void* kv_w = w + plan.kv_w;
+  CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
+  const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
+  CSA_HIP(launch_mqa_bwd_dq(*p, mode, q, kv_c, kv_w, idx, sinks, o, d_o, dq, st), "dq launch");
   return CSA_OK;
 }
 

@@ -1,0 +1,448 @@
+// Backward of stage 4, query side, on gfx950: dL/dq of the sparse multi-query
+// attention, with delta = rowsum(o * do) computed inside the same kernel.
+//
+// Sources: "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+// Primus", section "Attention kernels for the three layer types": the backward splits
+// into dQ, interm (the key-side head contraction) and delta, and delta is folded into
+// dQ; dQ runs at one wave per SIMD (its register set is large) and hides the latency
+// of the key gather by keeping the per-tile chain of products interleaved.  The
+// forward it differentiates is the one of sparse_mqa.hip:
+//   z[h,k] = (RoPE(q[h], P) . key_k) * scale,  u[h] = sum_k softmax_k(z) key_k,
+//   o[h]   = RoPE(u[h], -P)                     (P = pos0 + t)
+// With du = RoPE(do, +P) (the transpose of the de-rotation), dP[h,k] = du[h] . key_k,
+// delta[h] = du[h] . u[h] = do[h] . o[h] (a rotation preserves the dot product) and
+// dz = P_hk (dP - delta):
+//   dq[h] = RoPE( scale * sum_k dz[h,k] key_k , -P ).
+//
+// One pass over the keys.  P = e / l with e = exp2(z*log2e - m_ref) against a fixed
+// reference m_ref (the first tile's max, exact by shift invariance, with a second pass
+// when a later logit could overflow, as in the forward) and delta known before the
+// loop, so the kernel accumulates sum_k e_k (dP_k - delta) key_k and divides by l at
+// the end: no statistics pass.  A sink only joins l.
+//
+// Mapping (as the forward's 16-head kernel): one workgroup per query, wave w owns heads
+// 16w .. 16w+15 and all D dims.  Keys stream through LDS in tiles of 32 rows, staged by
+// direct-to-LDS loads into two stages.  Per tile, from the same K fragments:
+//   S^T[key, head]  = K . Q^T     and   dP^T[key, head] = K . dU^T
+//   (v_mfma_f32_16x16x32_bf16, keys on M, heads on N with q and du in registers)
+//   dz^T = e (dP - delta) in registers, rounded to the activation type
+//   dQ^T[dim, head] += K^T . dz^T  (K^T by transposing LDS reads, dz^T as B operand)
+// The accumulator layout of S^T gives lane (head, g) exactly the keys that are its
+// B-operand k-slots in the last product, so dz never leaves registers.
+#include "common.hpp"
+#include "mqa_bwd.hpp"
+
+namespace csa {
+namespace {
+
+struct DqArgs {
+  const void* q;
+  const void* kv_c;
+  const void* kv_w;
+  const int32_t* idx;
+  const float* sinks;  // [H] softmax-sink logits, or nullptr
+  const void* o;       // forward output [B,S,H,D]
+  const void* d_o;     // dL/do [B,S,H,D]
+  void* dq;            // dL/dq [B,S,H,D]
+  int32_t B, S, H, R, ratio, window, topk, n_entries, mode;
+  float scale_log2;  // softmax_scale * log2(e)
+  float scale;       // softmax_scale
+  double theta;
+  int64_t pos0;
+};
+
+constexpr int kMaxTopk = 2048;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Key slot (within a tile of 32) held at k-slot i of lane group g: the rows of the
+// S^T accumulator that lane group g holds (4g..4g+3, then 16+4g..16+4g+3).
+__device__ constexpr int dz_slot_key(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int HP = NW * 16;
+  constexpr int ES = (int)sizeof(T);
+  constexpr int KT = 32;
+  constexpr int ROWB = D * ES;
+  constexpr int NCH = ROWB / 16;
+  // Tile layout as in the forward: 1 KB lines, one direct-to-LDS wave load each; a
+  // 1 KB row (D = 512 bf16) is XOR-swizzled by 16-byte chunk so that the row reads and
+  // the transposing reads are free of bank conflicts; other row sizes pad the lines.
+  constexpr int RPL = ROWB < 1024 ? 1024 / ROWB : 1;
+  constexpr int LPR = ROWB > 1024 ? ROWB / 1024 : 1;
+  constexpr int NL = KT * LPR / RPL;
+  constexpr bool SWZ = ROWB == 1024 && ES == 2;
+  constexpr int LSTRIDE = SWZ ? 1024 : 1024 + 48;
+  constexpr int QROWB = ROWB + 16;
+  constexpr int TILEB = NL * LSTRIDE;
+  constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
+  __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
+  __shared__ int kv0[KT], kv1[KT];
+  __shared__ int sidx[kMaxTopk];
+  __shared__ float2 cs[64];
+  __shared__ int overflow;
+
+  // workgroup -> query: 32 consecutive queries per XCD visit, XCDs interleaved across
+  // the sequence, latest (heaviest) queries first.
+  const int total = a.B * a.S;
+  int gi = blockIdx.x;
+  const int nfull = total & ~255;
+  if (gi < nfull) {
+    const int xcd = gi & 7, j = gi >> 3;
+    gi = (((j >> 5) << 3) + xcd) * 32 + (j & 31);
+  }
+  gi = total - 1 - gi;
+  const int b = gi / a.S;
+  const int t = gi % a.S;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hl = lane & 15;
+  const int g = lane >> 4;
+  const int h = 16 * wave + hl;
+  const int n_t = a.mode == MQA_WINDOW_ONLY ? 0 : visible_entries(t, a.ratio);
+  const int nsel = a.mode == MQA_SELECTED ? min(a.topk, n_t) : n_t;
+  const int nwin = window_count(t, a.window);
+  const int wlo = window_lo(t, a.window);
+  const int nk = nsel + nwin;
+  const int64_t P = a.pos0 + t;
+  const int rlo = D - a.R;
+
+  if (threadIdx.x < a.R / 2) {
+    float c, s;
+    rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
+    cs[threadIdx.x] = make_float2(c, s);
+  }
+  if (a.mode == MQA_SELECTED) {
+    const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+    for (int i = threadIdx.x; i < nsel; i += NT) sidx[i] = irow[i];
+  }
+
+  const int64_t row0 = ((int64_t)b * a.S + t) * a.H * ROWB;  // byte offset of [b,t,0,0]
+  const unsigned char* qg = reinterpret_cast<const unsigned char*>(a.q) + row0;
+  const unsigned char* dog = reinterpret_cast<const unsigned char*>(a.d_o) + row0;
+  const unsigned char* og = reinterpret_cast<const unsigned char*>(a.o) + row0;
+
+  // H rows of D elements (heads >= H zero) -> LDS, heads 0..HP/2-1 in st0.
+  auto stage_rows = [&](const unsigned char* src) {
+    for (int c = threadIdx.x; c < HP * NCH; c += NT) {
+      const int row = c / NCH, col = (c % NCH) * 16;
+      const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(src + (int64_t)row * ROWB + col)
+                                : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>((row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col) = v;
+    }
+  };
+  auto my_row = [&]() -> const unsigned char* {
+    return (h < HP / 2 ? st0 : st1) + (h % (HP / 2)) * QROWB;
+  };
+  // Rotate the pairs of a fragment (dims d0 .. d0+7) that fall in the last R dims by +P.
+  auto rotate_frag = [&](Frag<T>& f, int d0) {
+    if (d0 + 8 > rlo) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int d = d0 + i;
+        if (d >= rlo) {
+          const float2 r = cs[(d - rlo) >> 1];
+          const float x0 = to_f32(f.v[i]), x1 = to_f32(f.v[i + 1]);
+          f.v[i] = from_f32<T>(x0 * r.x - x1 * r.y);
+          f.v[i + 1] = from_f32<T>(x0 * r.y + x1 * r.x);
+        }
+      }
+    }
+  };
+
+  // ---- B operands: lane (head h, group g), k-step k holds dims 32k + 8g .. +7.
+  Frag<T> qf[D / 32], uf[D / 32];
+  stage_rows(qg);
+  __syncthreads();
+  {
+    const unsigned char* r = my_row();
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      qf[k] = load_frag(reinterpret_cast<const T*>(r) + 32 * k + 8 * g);
+      rotate_frag(qf[k], 32 * k + 8 * g);
+    }
+  }
+  __syncthreads();
+  stage_rows(dog);
+  __syncthreads();
+  float delta = 0.f;
+  {
+    const unsigned char* r = my_row();
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      const int d0 = 32 * k + 8 * g;
+      uf[k] = load_frag(reinterpret_cast<const T*>(r) + d0);
+      if (h < a.H) {
+        const Frag<T> of = load_frag(reinterpret_cast<const T*>(og + (int64_t)h * ROWB) + d0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) delta = fmaf(to_f32(uf[k].v[i]), to_f32(of.v[i]), delta);
+      }
+      rotate_frag(uf[k], d0);
+    }
+  }
+  delta += __shfl_xor(delta, 16, 64);
+  delta += __shfl_xor(delta, 32, 64);
+  __syncthreads();  // the staging area becomes the key tiles
+
+  const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
+  const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
+  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
+  auto eoff = [&](int r, int d) -> int {
+    const int byte = d * ES;
+    if constexpr (SWZ) return r * 1024 + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15));
+    return ((r / RPL) * LPR + byte / 1024) * LSTRIDE + (r % RPL) * ROWB + (byte % 1024);
+  };
+  // Source row of key kk; masked keys read this query's own q row (finite data whose
+  // weight e is 0).
+  auto key_src = [&](int kk, int* ok) -> const unsigned char* {
+    if (kk < nsel) {
+      const int s = a.mode == MQA_SELECTED ? sidx[kk] : kk;
+      if (s >= 0 && s < n_t) {
+        *ok = 1;
+        return kv_c + ((int64_t)b * a.n_entries + s) * ROWB;
+      }
+    } else if (kk < nk) {
+      *ok = 1;
+      return kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
+    }
+    *ok = 0;
+    return qg;
+  };
+  auto issue = [&](int tile, unsigned char* sb, int* kv) {
+#pragma unroll
+    for (int L = wave; L < NL; L += NW) {
+      int r, byte;
+      if constexpr (RPL > 1) {
+        r = L * RPL + lane / NCH;
+        byte = (lane % NCH) * 16;
+      } else if constexpr (SWZ) {
+        r = L;
+        byte = (lane ^ swz(r)) * 16;
+      } else {
+        r = L / LPR;
+        byte = (L % LPR) * 1024 + lane * 16;
+      }
+      int ok;
+      const unsigned char* src = key_src(tile * KT + r, &ok);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
+                                       (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
+      if (byte == 0) kv[r] = ok;
+    }
+  };
+
+  float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
+  f32x4 acc[D / 16];
+
+  // Per-lane LDS offsets of the K (row) and K^T (transposing) fragments, as in the
+  // forward's 16-head kernel.
+  int qk_base[2], tr_base[4];
+  if constexpr (SWZ) {
+    const int s = swz(hl), s2 = s >> 2;
+    const int lo = hl * 1024 + (((g ^ s) & 3) << 4);
+    qk_base[0] = lo + (s2 ? 64 : 0);
+    qk_base[1] = lo - (s2 ? 64 : 0);
+    const int a4 = hl >> 2, c = g & 1, hb = (hl >> 1) & 1;
+    const int row = 4 * g + a4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      tr_base[m] = row * 1024 + ((m ^ a4) - m) * 32 + ((hb ^ c) << 4) + ((hl & 1) << 3);
+  } else {
+    qk_base[0] = qk_base[1] = eoff(hl, 8 * g);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tr_base[m] = eoff(4 * g + (hl >> 2), 4 * (hl & 3));
+  }
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+  auto compute = [&](const unsigned char* sb, const int* kv) {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
+    auto ld_k = [&](int row16, int k) {
+      Frag<T> f;
+      const CSA_LDS unsigned char* p =
+          lb + qk_base[k & 1] + (SWZ ? row16 * 1024 + 64 * k : eoff(row16, 32 * k) - eoff(0, 0));
+      *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
+      if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
+      return f;
+    };
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+    Frag<T> n0 = ld_k(0, 0), n1 = ld_k(16, 0);
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      const Frag<T> a0 = n0, a1 = n1;
+      if (k + 1 < D / 32) {
+        n0 = ld_k(0, k + 1);
+        n1 = ld_k(16, k + 1);
+      }
+      s0 = mfma16x16x32(a0, qf[k], s0);
+      s1 = mfma16x16x32(a1, qf[k], s1);
+      p0 = mfma16x16x32(a0, uf[k], p0);
+      p1 = mfma16x16x32(a1, uf[k], p1);
+    }
+    float z[8], dp[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = kv[4 * g + i] ? s0[i] * a.scale_log2 : -INFINITY;
+      z[4 + i] = kv[16 + 4 * g + i] ? s1[i] * a.scale_log2 : -INFINITY;
+      dp[i] = p0[i];
+      dp[4 + i] = p1[i];
+    }
+    float mt = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    m_seen = fmaxf(m_seen, mt);
+    if (m_ref == -INFINITY) m_ref = mt;  // acc and l are still zero
+    const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+    Frag<T> dzf;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = __builtin_amdgcn_exp2f(z[i] - mref);
+      ls += e;
+      dzf.v[i] = from_f32<T>(e * (dp[i] - delta));
+    }
+    l_run += ls;
+
+    // dQ^T += K^T . dz^T: lane (dim 16db+hl, group g) takes keys dz_slot_key(g, 0..7)
+    // of that dim from two transposing 8-byte reads.
+    auto ld_t = [&](int db) {
+      Frag<T> f;
+      if constexpr (ES == 2) {
+        const CSA_LDS unsigned char* p =
+            lb + tr_base[db & 3] + (SWZ ? 32 * db : eoff(0, 16 * db) - eoff(0, 0));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (CSA_LDS i16x4*)(p + (SWZ ? 16 * 1024 : eoff(16, 0) - eoff(0, 0))));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<i16x8*>(f.v) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          f.v[i] = *(const CSA_LDS T*)(lb + eoff(dz_slot_key(g, i), 16 * db + hl));
+      }
+      return f;
+    };
+    Frag<T> nv = ld_t(0);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const Frag<T> av = nv;
+      if (db + 1 < D / 16) nv = ld_t(db + 1);
+      acc[db] = mfma16x16x32(av, dzf, acc[db]);
+    }
+  };
+
+  const int ntiles = (nk + KT - 1) / KT;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    if (threadIdx.x == 0) overflow = 0;
+    if (ntiles > 0) issue(0, st0, kv0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      if (tile + 1 < ntiles) issue(tile + 1, st1, kv1);
+      compute(st0, kv0);
+      __syncthreads();
+      if (tile + 1 < ntiles) {
+        if (tile + 2 < ntiles) issue(tile + 2, st0, kv0);
+        compute(st1, kv1);
+        __syncthreads();
+      }
+    }
+    if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(&overflow, 1);
+    __syncthreads();
+    if (!overflow) break;
+    m_ref = m_seen;
+  }
+
+  // ---- dq = RoPE(scale / l * acc, -P), staged through LDS, written coalesced.
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (a.sinks && h < a.H) l_run += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_ref);
+  const float f = l_run > 0.f ? a.scale / l_run : 0.f;
+  {
+    unsigned char* orow = (h < HP / 2 ? st0 : st1) + (h % (HP / 2)) * QROWB;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = acc[db][i] * f;
+      if (d0 >= rlo) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float2 r = cs[(d0 + i - rlo) >> 1];
+          const float x0 = x[i], x1 = x[i + 1];
+          x[i] = x0 * r.x + x1 * r.y;
+          x[i + 1] = -x0 * r.y + x1 * r.x;
+        }
+      }
+      T* dst = reinterpret_cast<T*>(orow) + d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(x[i]);
+    }
+  }
+  __syncthreads();
+  unsigned char* dqg = reinterpret_cast<unsigned char*>(a.dq) + row0;
+  for (int c = threadIdx.x; c < a.H * NCH; c += NT) {
+    const int row = c / NCH, col = (c % NCH) * 16;
+    const unsigned char* src = (row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col;
+    *reinterpret_cast<uint4*>(dqg + (int64_t)row * ROWB + col) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+template <typename T, int D>
+void launch_d(const DqArgs& a, int H, hipStream_t st) {
+  const dim3 grid(a.B * a.S);
+  if (H <= 16) hipLaunchKernelGGL((mqa_bwd_dq_kernel<T, D, 1>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((mqa_bwd_dq_kernel<T, D, 4>), grid, dim3(256), 0, st, a);
+}
+
+template <typename T>
+hipError_t launch_t(const DqArgs& a, int D, int H, hipStream_t st) {
+  switch (D) {
+    case 64: launch_d<T, 64>(a, H, st); break;
+    case 128: launch_d<T, 128>(a, H, st); break;
+    case 256: launch_d<T, 256>(a, H, st); break;
+    case 512: launch_d<T, 512>(a, H, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mqa_bwd_dq(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
+                             const void* kv_w, const int32_t* idx, const float* sinks, const void* o,
+                             const void* d_o, void* dq, hipStream_t st) {
+  DqArgs a{};
+  a.q = q;
+  a.kv_c = kv_c;
+  a.kv_w = kv_w;
+  a.idx = idx;
+  a.sinks = sinks;
+  a.o = o;
+  a.d_o = d_o;
+  a.dq = dq;
+  a.B = p.B;
+  a.S = p.S;
+  a.H = p.H;
+  a.R = p.rope_dim;
+  a.ratio = p.ratio;
+  a.window = p.window;
+  a.topk = p.topk;
+  a.n_entries = mode == MQA_WINDOW_ONLY ? 0 : p.S / p.ratio;
+  a.mode = mode;
+  a.scale_log2 = p.softmax_scale * kLog2e;
+  a.scale = p.softmax_scale;
+  a.theta = p.rope_theta;
+  a.pos0 = p.pos0;
+  if (p.B * p.S == 0) return hipSuccess;
+  return p.dtype == CSA_BF16 ? launch_t<bf16>(a, p.D, p.H, st) : launch_t<float>(a, p.D, p.H, st);
+}
+
+}  // namespace csa

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum {
   CSA_OK = 0,
@@ -205,6 +205,24 @@ csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void
 csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const void* kv_c,
                                      const void* kv_raw, const int32_t* idx, const float* sinks,
                                      void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of stage 4, query side ("Enabling DeepSeek-V4-Flash Training on AMD
+ * Instinct MI355X GPUs with Primus", section "Attention kernels for the three layer
+ * types": the dQ kernel, with delta = rowsum(o * do) computed inside it):
+ *   dq[b,t,h] = dL/dq[b,t,h] for the forward csa_sparse_mqa_fwd_sink with the same
+ *   params, q, kv_c, kv_raw, idx and sinks (NULL alike), given o (that forward's
+ *   output [B,S,H,D]) and d_o = dL/do [B,S,H,D].  With P = pos0 + t, du = RoPE(d_o, +P)
+ *   and delta[h] = sum_d o[h,d] d_o[h,d]:
+ *     dq[h] = RoPE( softmax_scale * sum_k p[h,k] (du[h] . key_k - delta[h]) key_k , -P )
+ *   over the same keys and softmax p as the forward (sink in the denominator only).
+ *   The selection is held fixed (top-k has no gradient).  dq [B,S,H,D] in the
+ *   activation dtype; the gradients of kv_c, kv_raw and the sinks are not computed
+ *   here.  ws: csa_workspace_bytes(p, CSA_OP_SPARSE_MQA) bytes.  Errors as
+ *   csa_sparse_mqa_fwd_sink, plus CSA_ERR_INVALID_ARG for a NULL o, d_o or dq. */
+csa_status_t csa_sparse_mqa_bwd_dq(const csa_params_t* p, const void* q, const void* kv_c,
+                                   const void* kv_raw, const int32_t* idx, const float* sinks,
+                                   const void* o, const void* d_o, void* dq, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Target distribution of the indexer's distillation loss ("fix(deepseek-v4): correct
  * V4-Flash attention math", Part 1 item 5: KL(attention || indexer) over the selected

@@ -337,8 +337,9 @@ def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None, s
     R, theta, pos0 = cfg.rope_dim, cfg.rope_theta, cfg.pos0
     scale = cfg.D ** -0.5 if getattr(cfg, "softmax_scale", None) is None else cfg.softmax_scale
     if sel is None or kv_c is None:
-        r = layer_rows(cfg, inp, rows)
-        sel, kv_c = r["sel"], r["kv_c"]
+        r = layer_rows(cfg, inp, rows, sel_override=sel)
+        sel = r["sel"] if sel is None else sel
+        kv_c = r["kv_c"] if kv_c is None else kv_c
     out = {}
     for (b, t) in rows:
         lo, hi = window_bounds(t, cfg.window)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 5
+    assert bd.lib.csa_abi_version() == 6
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -256,3 +256,18 @@ def test_kl_target_rejects():
     assert call(p_c1(topk=0)) == bd.CSA_ERR_INVALID_ARG
     assert call(p_c1(H=65)) == bd.CSA_ERR_INVALID_ARG
     assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
+
+
+def test_bwd_dq_rejects():
+    """Argument checks of csa_sparse_mqa_bwd_dq fail before any GPU call."""
+    def call(p, q=A, kv=A, kvr=A, idx=A, o=A, d_o=A, dq=A):
+        return bd.lib.csa_sparse_mqa_bwd_dq(ctypes.byref(p), q, kv, kvr, idx, None, o, d_o, dq, A, 1 << 30, None)
+    assert call(p_c1(), d_o=None) == bd.CSA_ERR_INVALID_ARG and "d_o" in bd.last_error()
+    assert call(p_c1(), dq=None) == bd.CSA_ERR_INVALID_ARG and "dq" in bd.last_error()
+    assert call(p_c1(), o=None) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), q=A + 4) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), kv=None) == bd.CSA_ERR_INVALID_ARG and "idx" in bd.last_error()
+    assert call(p_c1(H=65)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
+    z = ctypes.byref(p_c1(B=0))
+    assert bd.lib.csa_sparse_mqa_bwd_dq(z, None, None, None, None, None, None, None, None, None, 0, None) == bd.CSA_OK
