@@ -50,6 +50,8 @@ def kernel_work(cfg, wl):
         # read and write every raw latent once
         "window_rope": (2 * B * S * D * es, "bytes", "hbm"),
         "attention": (f["attention"], "flops", "mfma"),
+        # attention backward, query side: QK, dP = dU.K^T and dz.K per (query, key), 6*H*D
+        "bwd_dq": (1.5 * f["attention"], "flops", "mfma"),
     }
     if cfg.kind == "csa":
         work["indexer"] = (f["indexer"], "flops", "mfma")
@@ -312,6 +314,9 @@ def main():
                     help="CSA: indexer prologue on (RoPE + Hadamard of q_I and k_I, temperature on w)")
     ap.add_argument("--index-fp8", action="store_true",
                     help="CSA: FP8 (E4M3, per-row scales) indexer operands")
+    ap.add_argument("--bwd-dq", action="store_true",
+                    help="each step also runs the attention backward's query side "
+                         "(csa_sparse_mqa_bwd_dq) on the step's output and a seeded dL/do")
     ap.add_argument("--kl-target", action="store_true",
                     help="CSA: each step also forms the indexer distillation target (csa_kl_target)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -382,7 +387,33 @@ def main():
         bd.kl_target(p, inp["q"], kl["kv_c_out"], kl["idx_out"], kl["target"])
         if k is not None:
             kl["ev"][k][1].record()
-    layer_out = {} if kl is None else {"kv_c_out": kl["kv_c_out"], "idx_out": kl["idx_out"]}
+    dq = None
+    if args.bwd_dq:
+        n = cfg.S // cfg.ratio
+        g = torch.Generator(device=dev).manual_seed(cfg.seed + 23)
+        dq = {"kv_c_out": kl["kv_c_out"] if kl else (None if cfg.kind == "swa" else
+                                                     torch.empty((cfg.B, n, cfg.D), dtype=inp["q"].dtype, device=dev)),
+              "idx_out": kl["idx_out"] if kl else (torch.empty((cfg.B, cfg.S, cfg.topk), dtype=torch.int32, device=dev)
+                                                    if cfg.kind == "csa" else None),
+              "d_o": torch.randn(inp["q"].shape, generator=g, device=dev).to(inp["q"].dtype),
+              "dq": torch.empty_like(inp["q"]),
+              "ws": bd.workspace(p, bd.OP_SPARSE_MQA, dev),
+              "ev": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.steps)]}
+
+    def dq_step(k=None):
+        if dq is None:
+            return
+        if k is not None:
+            dq["ev"][k][0].record()
+        bd.sparse_mqa_bwd_dq(p, inp["q"], dq["kv_c_out"], inp["kv_raw"], dq["idx_out"], o, dq["d_o"],
+                             dq=dq["dq"], ws=dq["ws"], sinks=inp.get("sinks"))
+        if k is not None:
+            dq["ev"][k][1].record()
+    layer_out = {}
+    for src in (kl, dq):
+        if src is not None:
+            layer_out = {k: src[k] for k in ("kv_c_out", "idx_out") if src[k] is not None}
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -396,12 +427,14 @@ def main():
     for _ in range(args.warmup):
         bd.layer_fwd(p, inp, o=o, ws=ws, **layer_out)
         kl_step()
+        dq_step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for k in range(args.steps):
         bd.layer_fwd_traced(p, inp, traces[k], o=o, ws=ws, **layer_out)
         kl_step(k)
+        dq_step(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -416,6 +449,9 @@ def main():
     if kl is not None:
         tot["kl_target"] = sum(a.elapsed_time(b) for a, b in kl["ev"]) / args.steps
         launches["kl_target"] = 1
+    if dq is not None:  # window rotation + dQ kernel, timed together on the step's stream
+        tot["bwd_dq"] = sum(a.elapsed_time(b) for a, b in dq["ev"]) / args.steps
+        launches["bwd_dq"] = 1
     work = kernel_work(cfg, wl)
     kernels = {}
     for k, v in tot.items():
@@ -437,6 +473,8 @@ def main():
     f = wl.layer_flops(cfg)
     if kl is not None:  # the step also forms the distillation target
         f = dict(f, total=f["total"] + work["kl_target"][0])
+    if dq is not None:  # and the attention backward's query side
+        f = dict(f, total=f["total"] + work["bwd_dq"][0])
     tokens = cfg.B * cfg.S
     value = tokens / (ms_step * 1e-3)
     tflops = f["total"] / (ms_step * 1e-3) / 1e12
@@ -445,7 +483,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": cfg.name + ("+kl_target" if kl is not None else ""), "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
+        "config": {"workload": cfg.name + ("+kl_target" if kl is not None else "") + ("+bwd_dq" if dq is not None else ""), "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
                    "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
                    "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue),

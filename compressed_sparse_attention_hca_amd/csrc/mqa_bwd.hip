@@ -58,6 +58,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 // S^T accumulator that lane group g holds (4g..4g+3, then 16+4g..16+4g+3).
 __device__ constexpr int dz_slot_key(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding and its LDS
+// operations are done, then barrier.  Unlike __syncthreads this leaves the N youngest
+// direct-to-LDS loads in flight; the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+template <int N> __device__ inline void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   constexpr int NT = NW * 64;
@@ -77,9 +85,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   constexpr int QROWB = ROWB + 16;
   constexpr int TILEB = NL * LSTRIDE;
   constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
+  // Direct-to-LDS loads per wave per tile, and the pipeline depth: NS stages, tile t+NS-1
+  // in flight while tile t is used (the gather's latency is what this kernel waits on
+  // at one workgroup per CU).  Four stages where the LDS holds them and the wait count
+  // fits the 6-bit vmcnt field, else two.
+  static_assert(NL % NW == 0, "every wave issues the same number of line loads");
+  constexpr int LPT = NL / NW;
+  constexpr int NS = (4 * SB + 12 * 1024 <= 160 * 1024 && 2 * LPT <= 63) ? 4 : 2;
+  constexpr int SB2 = NS == 4 ? SB : 16;
+  // Each stage is its own array: the compiler then sees that the loads in flight into
+  // one stage do not alias the reads of another.
   __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
   __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
-  __shared__ int kv0[KT], kv1[KT];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[SB2];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[SB2];
+  __shared__ int kv0[KT], kv1[KT], kv2[KT], kv3[KT];
   __shared__ int sidx[kMaxTopk];
   __shared__ float2 cs[64];
   __shared__ int overflow;
@@ -98,7 +118,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   const int t = gi % a.S;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane & 15;
   const int g = lane >> 4;
   const int h = 16 * wave + hl;
@@ -110,6 +130,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   const int64_t P = a.pos0 + t;
   const int rlo = D - a.R;
 
+  if (threadIdx.x == 0) overflow = 0;
   if (threadIdx.x < a.R / 2) {
     float c, s;
     rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
@@ -197,9 +218,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   };
   // Source row of key kk; masked keys read this query's own q row (finite data whose
   // weight e is 0).
-  auto key_src = [&](int kk, int* ok) -> const unsigned char* {
+  // `s` is the entry index of key kk when kk < nsel.
+  auto key_src = [&](int kk, int s, int* ok) -> const unsigned char* {
     if (kk < nsel) {
-      const int s = a.mode == MQA_SELECTED ? sidx[kk] : kk;
       if (s >= 0 && s < n_t) {
         *ok = 1;
         return kv_c + ((int64_t)b * a.n_entries + s) * ROWB;
@@ -212,6 +233,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
     return qg;
   };
   auto issue = [&](int tile, unsigned char* sb, int* kv) {
+    // With one key row per line the row, hence its entry index, is wave-uniform: the
+    // tile's indices come from one LDS read (lane j: key tile*KT + j % KT) and are
+    // picked per line with v_readlane, so no line waits on its own LDS read.
+    int sv = 0;
+    if constexpr (RPL == 1) {
+      const int kk = tile * KT + (lane % KT);
+      sv = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
+    }
 #pragma unroll
     for (int L = wave; L < NL; L += NW) {
       int r, byte;
@@ -225,8 +254,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
         r = L / LPR;
         byte = (L % LPR) * 1024 + lane * 16;
       }
-      int ok;
-      const unsigned char* src = key_src(tile * KT + r, &ok);
+      int ok, s;
+      const int kk = tile * KT + r;
+      if constexpr (RPL == 1) s = __builtin_amdgcn_readlane(sv, r);
+      else s = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
+      const unsigned char* src = key_src(kk, s, &ok);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
                                        (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
       if (byte == 0) kv[r] = ok;
@@ -266,20 +298,52 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
       if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
       return f;
     };
+    // One wave per SIMD leaves no other wave to cover LDS latency, so the fragment
+    // reads run PQ k-steps (QK) and PT dim blocks (the transposed product) ahead.
+    constexpr int KS = D / 32, PQ = KS < 3 ? KS : 3;
+    constexpr int DB = D / 16, PT = DB < 6 ? DB : 6;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
-    Frag<T> n0 = ld_k(0, 0), n1 = ld_k(16, 0);
+    Frag<T> ka[PQ], kb[PQ];
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) {
-      const Frag<T> a0 = n0, a1 = n1;
-      if (k + 1 < D / 32) {
-        n0 = ld_k(0, k + 1);
-        n1 = ld_k(16, k + 1);
+    for (int k = 0; k < PQ; ++k) {
+      ka[k] = ld_k(0, k);
+      kb[k] = ld_k(16, k);
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const Frag<T> a0 = ka[k % PQ], a1 = kb[k % PQ];
+      if (k + PQ < KS) {
+        ka[k % PQ] = ld_k(0, k + PQ);
+        kb[k % PQ] = ld_k(16, k + PQ);
       }
       s0 = mfma16x16x32(a0, qf[k], s0);
       s1 = mfma16x16x32(a1, qf[k], s1);
       p0 = mfma16x16x32(a0, uf[k], p0);
       p1 = mfma16x16x32(a1, uf[k], p1);
     }
+    // dQ^T += K^T . dz^T: lane (dim 16db+hl, group g) takes keys dz_slot_key(g, 0..7)
+    // of that dim from two transposing 8-byte reads.
+    auto ld_t = [&](int db) {
+      Frag<T> f;
+      if constexpr (ES == 2) {
+        const CSA_LDS unsigned char* p =
+            lb + tr_base[db & 3] + (SWZ ? 32 * db : eoff(0, 16 * db) - eoff(0, 0));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (CSA_LDS i16x4*)(p + (SWZ ? 16 * 1024 : eoff(16, 0) - eoff(0, 0))));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<i16x8*>(f.v) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          f.v[i] = *(const CSA_LDS T*)(lb + eoff(dz_slot_key(g, i), 16 * db + hl));
+      }
+      return f;
+    };
+    Frag<T> tv[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) tv[i] = ld_t(i);  // independent of dz: issued before the softmax
     float z[8], dp[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -306,56 +370,51 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
     }
     l_run += ls;
 
-    // dQ^T += K^T . dz^T: lane (dim 16db+hl, group g) takes keys dz_slot_key(g, 0..7)
-    // of that dim from two transposing 8-byte reads.
-    auto ld_t = [&](int db) {
-      Frag<T> f;
-      if constexpr (ES == 2) {
-        const CSA_LDS unsigned char* p =
-            lb + tr_base[db & 3] + (SWZ ? 32 * db : eoff(0, 16 * db) - eoff(0, 0));
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (CSA_LDS i16x4*)(p + (SWZ ? 16 * 1024 : eoff(16, 0) - eoff(0, 0))));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        *reinterpret_cast<i16x8*>(f.v) = v;
-      } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          f.v[i] = *(const CSA_LDS T*)(lb + eoff(dz_slot_key(g, i), 16 * db + hl));
-      }
-      return f;
-    };
-    Frag<T> nv = ld_t(0);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const Frag<T> av = nv;
-      if (db + 1 < D / 16) nv = ld_t(db + 1);
+    for (int db = 0; db < DB; ++db) {
+      const Frag<T> av = tv[db % PT];
+      if (db + PT < DB) tv[db % PT] = ld_t(db + PT);
       acc[db] = mfma16x16x32(av, dzf, acc[db]);
     }
   };
 
   const int ntiles = (nk + KT - 1) / KT;
+  // One pipeline step: wait until this wave's loads of tile t have landed (at most
+  // `after` younger tiles, LPT loads each, may still be in flight), barrier (every
+  // wave's part of tile t is in LDS, every wave is done with tile t-1), refill the
+  // stage of tile t-1 with tile t+NS-1, then use tile t.
+  auto step = [&](int t, const unsigned char* cur, const int* kvc, unsigned char* nxt, int* kvn) {
+    const int after = min(ntiles - 1, t + NS - 2) - t;
+    if (after <= 0) vm_wait_barrier<0>();
+    else if (after == 1) vm_wait_barrier<LPT>();
+    else vm_wait_barrier<2 * LPT>();
+    if (t + NS - 1 < ntiles) issue(t + NS - 1, nxt, kvn);
+    compute(cur, kvc);
+  };
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
-    if (threadIdx.x == 0) overflow = 0;
-    if (ntiles > 0) issue(0, st0, kv0);
-    __syncthreads();
-    for (int tile = 0; tile < ntiles; tile += 2) {
-      if (tile + 1 < ntiles) issue(tile + 1, st1, kv1);
-      compute(st0, kv0);
-      __syncthreads();
-      if (tile + 1 < ntiles) {
-        if (tile + 2 < ntiles) issue(tile + 2, st0, kv0);
-        compute(st1, kv1);
-        __syncthreads();
+    for (int i = 0; i < NS - 1 && i < ntiles; ++i) {
+      if (i == 0) issue(0, st0, kv0);
+      else if (i == 1) issue(1, st1, kv1);
+      else issue(2, st2, kv2);
+    }
+    for (int tile = 0; tile < ntiles; tile += NS) {
+      if constexpr (NS == 4) {
+        step(tile, st0, kv0, st3, kv3);
+        if (tile + 1 < ntiles) step(tile + 1, st1, kv1, st0, kv0);
+        if (tile + 2 < ntiles) step(tile + 2, st2, kv2, st1, kv1);
+        if (tile + 3 < ntiles) step(tile + 3, st3, kv3, st2, kv2);
+      } else {
+        step(tile, st0, kv0, st1, kv1);
+        if (tile + 1 < ntiles) step(tile + 1, st1, kv1, st0, kv0);
       }
     }
+    __syncthreads();  // every wave is done with the stages
     if (__any(m_seen > m_ref + 64.0f) && lane == 0) atomicOr(&overflow, 1);
     __syncthreads();
-    if (!overflow) break;
+    if (!overflow || pass == 1) break;
     m_ref = m_seen;
   }
 
