@@ -454,9 +454,357 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// bf16 fast path for D = 512 and up to 64 heads, on the forward's head-group x
+// latent-half mapping: wave w owns heads 32(w/2) .. +31 (hg) and dims 256(w%2) .. +255
+// (dh), so every LDS fragment feeds 32 heads on v_mfma_f32_32x32x16_bf16 and each wave
+// reads only its half of every key row: per 32-key tile a wave reads 16 KB for the two
+// logit-side products and 16 KB for the transposed one, half of the 16-head mapping.
+// Per tile:
+//   partial S^T and dP^T [32 keys, 32 heads] over the wave's 256 dims (32 MFMAs, one
+//     K fragment per k-step feeding both); rows r hold key r ^ 16dh, so rows 0..15 are
+//     the wave's own half of the keys
+//   send the partner wave (same heads, other half) its keys' partials of both, add the
+//     partner's partials of this wave's keys (through LDS)
+//   e = exp2 against the fixed reference, dz = e (dP - delta) for the wave's 16 keys,
+//     rounded to bf16; swap dz with the partner (through LDS)
+//   dQ^T[256 dims, 32 heads] += K^T . dz^T over all 32 keys (16 MFMAs)
+// Delta of a head is summed over the lane halves (v_permlane32_swap) and the partner.
+// Keys stream through four stages as in the generic kernel; the entry indices sit in
+// LDS.  One workgroup per CU (q, du and the accumulator take about 256 registers).
+// ---------------------------------------------------------------------------------
+__device__ inline float halves_sum2(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float halves_max2(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Workgroup barrier for the LDS exchange: this wave's LDS operations are done, the
+// direct-to-LDS copies in flight stay in flight (a workgroup fence would wait for them
+// too, since they write LDS).
+__device__ inline void lds_barrier2() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
+  constexpr int D = 512, ROWB = 1024, KT = 32, NT = 256, LPT = 8;
+  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
+  auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
+  __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st2[KT * ROWB];
+  __shared__ __attribute__((aligned(1024))) unsigned char st3[KT * ROWB];
+  // exchange: partial logits xh (8 KB), partial dP xd (8 KB), dz xp (4 KB), per-head
+  // values xm (1 KB); then the RoPE table, the sink logits and the overflow flag
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[22304];
+  f32x4 (*xh)[2][64] = reinterpret_cast<f32x4 (*)[2][64]>(xbuf);
+  f32x4 (*xd)[2][64] = reinterpret_cast<f32x4 (*)[2][64]>(xbuf + 8192);
+  u32x4 (*xp)[64] = reinterpret_cast<u32x4 (*)[64]>(xbuf + 16384);
+  float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 20480);
+  float2* cs = reinterpret_cast<float2*>(xbuf + 21504);
+  float* sk = reinterpret_cast<float*>(xbuf + 22016);
+  int* ovf = reinterpret_cast<int*>(xbuf + 22272);
+  __shared__ int sidx[kMaxTopk];
+
+  const int total = a.B * a.S;
+  int gi = blockIdx.x;
+  const int nfull = total & ~255;
+  if (gi < nfull) {
+    const int xcd = gi & 7, j = gi >> 3;
+    gi = (((j >> 5) << 3) + xcd) * 32 + (j & 31);
+  }
+  gi = total - 1 - gi;
+  const int b = gi / a.S;
+  const int t = gi % a.S;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave >> 1, dh = wave & 1;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int h = 32 * hg + l32;
+  const int n_t = a.mode == MQA_WINDOW_ONLY ? 0 : visible_entries(t, a.ratio);
+  const int nsel = a.mode == MQA_SELECTED ? min(a.topk, n_t) : n_t;
+  const int nwin = window_count(t, a.window);
+  const int wlo = window_lo(t, a.window);
+  const int nk = nsel + nwin;
+  const int64_t P = a.pos0 + t;
+  const int rlo = D - a.R;
+
+  if (threadIdx.x < a.R / 2) {
+    float c, s;
+    rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
+    cs[threadIdx.x] = make_float2(c, s);
+  }
+  if (threadIdx.x == 0) *ovf = 0;
+  if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = a.sinks[threadIdx.x];
+  if (a.mode == MQA_SELECTED) {
+    const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+    for (int i = threadIdx.x; i < nsel; i += NT) sidx[i] = irow[i];
+  }
+  const int64_t row0 = ((int64_t)b * a.S + t) * a.H * ROWB;
+  const unsigned char* qg = reinterpret_cast<const unsigned char*>(a.q) + row0;
+  const unsigned char* dog = reinterpret_cast<const unsigned char*>(a.d_o) + row0;
+  const unsigned char* og = reinterpret_cast<const unsigned char*>(a.o) + row0;
+  const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
+  const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
+  __syncthreads();  // table, sinks, indices and flag are in LDS
+
+  const int dma_off0 = (lane ^ (2 * (wave & 3))) << 4, dma_off1 = (lane ^ (2 * (wave & 3) + 1)) << 4;
+  // Direct-to-LDS copy of tile `tile`: lane l < 32 resolves key tile*32 + l, wave w
+  // loads rows w, w+4, ... (one 1 KB wave load per row, LPT per wave); returns the
+  // tile's key-validity bits.
+  auto issue = [&](int tile, unsigned char* sb) -> uint32_t {
+    const int kk = tile * KT + l32;
+    const unsigned char* src = qg;  // masked keys read finite data that is never used
+    bool ok = false;
+    if (kk < nsel) {
+      const int sv = a.mode == MQA_SELECTED ? sidx[kk] : kk;
+      if (sv >= 0 && sv < n_t) {
+        ok = true;
+        src = kv_c + ((int64_t)b * a.n_entries + sv) * ROWB;
+      }
+    } else if (kk < nk) {
+      ok = true;
+      src = kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
+    }
+    const uint32_t bits = (uint32_t)__ballot(ok && lane < 32);
+    const uint64_t sp = reinterpret_cast<uint64_t>(src);
+    const uint32_t sp_lo = (uint32_t)sp, sp_hi = (uint32_t)(sp >> 32);
+#pragma unroll
+    for (int m = 0; m < KT / 4; ++m) {
+      const int r = wave + 4 * m;  // swz(r) = 2 wave | (m & 1)
+      const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
+      const unsigned char* gp = reinterpret_cast<const unsigned char*>(row) + (m & 1 ? dma_off1 : dma_off0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp),
+                                       (CSA_LDS void*)(sb + r * ROWB), 16, 0, 0);
+    }
+    return bits;
+  };
+
+  const int ntiles = (nk + KT - 1) / KT;
+  uint32_t km0 = 0u, km1 = 0u, km2 = 0u, km3 = 0u;
+  auto prologue_issue = [&]() {
+    if (ntiles > 0) km0 = issue(0, st0);
+    if (ntiles > 1) km1 = issue(1, st1);
+    if (ntiles > 2) km2 = issue(2, st2);
+  };
+  prologue_issue();  // the first tiles are requested before q, du and o
+
+  // ---- B operands straight from global memory: lane (head h, g), k-step k holds dims
+  // 256dh + 16k + 8g .. +7; q and du rotated at +P in the last R dims; delta partials.
+  bf16x8 qf[16], uf[16];
+  float delta = 0.f;
+  auto rot = [&](bf16x8& v, int d0) {
+    if (d0 + 8 > rlo) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int d = d0 + i;
+        if (d >= rlo) {
+          const float2 r = cs[(d - rlo) >> 1];
+          const float x0 = (float)v[i], x1 = (float)v[i + 1];
+          v[i] = (bf16)(x0 * r.x - x1 * r.y);
+          v[i + 1] = (bf16)(x0 * r.y + x1 * r.x);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int d0 = 256 * dh + 16 * k + 8 * g;
+    const int64_t eo = (int64_t)h * ROWB + 2 * d0;
+    if (h < a.H) {
+      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + eo));
+      uf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dog + eo));
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(og + eo));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) delta = fmaf((float)uf[k][i], (float)ov[i], delta);
+    } else {
+      qf[k] = bf16x8{};
+      uf[k] = bf16x8{};
+    }
+    rot(qf[k], d0);
+    rot(uf[k], d0);
+  }
+  delta = halves_sum2(delta);
+  xm[wave][lane] = delta;
+  lds_barrier2();
+  delta += xm[wave ^ 1][lane];
+  lds_barrier2();  // xm is free again
+
+  // Per-lane LDS offsets, as in the forward's head-group kernel.
+  const int kr = l32 ^ (16 * dh);
+  int qk_base[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qk_base[m] = kr * ROWB + ((32 * dh + ((2 * m + g) ^ swz(kr))) << 4);
+  const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
+  int pv_base[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    pv_base[m] = (4 * g + a4) * ROWB +
+                 ((32 * dh + 2 * ((2 * m + hh) ^ a4) + (((hj >> 1) & 1) ^ g)) << 4) + 8 * (hj & 1);
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const int pv_mine = 16 * ROWB * dh, pv_other = 16 * ROWB * (dh ^ 1);
+
+  float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
+  f32x16 O[8];
+
+  auto compute = [&](const unsigned char* sb, uint32_t kmask, bool first) {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, uf[k], dp, 0, 0, 0);
+      if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      xh[wave][q][lane] = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
+      xd[wave][q][lane] = f32x4{dp[8 + 4 * q], dp[9 + 4 * q], dp[10 + 4 * q], dp[11 + 4 * q]};
+    }
+    lds_barrier2();
+    float z[8], dv[8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f32x4 o4 = xh[wave ^ 1][q][lane], d4 = xd[wave ^ 1][q][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[4 * q + i] = s[4 * q + i] + o4[i];
+        dv[4 * q + i] = dp[4 * q + i] + d4[i];
+      }
+    }
+    if (kmask != 0xffffffffu) {
+      const uint32_t kml = kmask >> (4 * g + 16 * dh);  // bit 8q + i: key 16dh + 8q + 4g + i
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((kml >> (8 * (e >> 2) + (e & 3))) & 1u)) z[e] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mt = fmaxf(mt, z[e]);
+    mt = halves_max2(mt);
+    m_seen = fmaxf(m_seen, mt);
+    if (first) {  // workgroup-uniform: the pair agrees on the reference
+      xm[wave][lane] = mt;
+      lds_barrier2();
+      const float m0 = fmaxf(mt, xm[wave ^ 1][lane]);
+      m_ref = m0 == -INFINITY ? 0.f : m0;
+    }
+    const float nbias = -m_ref * a.scale_log2;
+    bf16x8 dzm;
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(z[e], a.scale_log2, nbias));
+      ls += p;
+      dzm[e] = (bf16)(p * (dv[e] - delta));
+    }
+    l_run += ls;
+    xp[wave][lane] = __builtin_bit_cast(u32x4, dzm);
+    lds_barrier2();
+    const bf16x8 dzo = __builtin_bit_cast(bf16x8, xp[wave ^ 1][lane]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + (ks ? pv_other : pv_mine);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ks ? dzo : dzm, O[db], 0, 0, 0);
+      }
+      if (db & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One pipeline step (see the generic kernel): wait for tile t, barrier, refill the
+  // stage of tile t-1 with tile t+3, use tile t.
+  auto step = [&](int tt, const unsigned char* cur, uint32_t kmc, unsigned char* nxt, uint32_t& kmn, bool first) {
+    const int after = min(ntiles - 1, tt + 2) - tt;
+    if (after <= 0) vm_wait_barrier<0>();
+    else if (after == 1) vm_wait_barrier<LPT>();
+    else vm_wait_barrier<2 * LPT>();
+    if (tt + 3 < ntiles) kmn = issue(tt + 3, nxt);
+    compute(cur, kmc, first);
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+    l_run = 0.f;
+    if (pass > 0) prologue_issue();
+    for (int tile = 0; tile < ntiles; tile += 4) {
+      step(tile, st0, km0, st3, km3, pass == 0 && tile == 0);
+      if (tile + 1 < ntiles) step(tile + 1, st1, km1, st0, km0, false);
+      if (tile + 2 < ntiles) step(tile + 2, st2, km2, st1, km1, false);
+      if (tile + 3 < ntiles) step(tile + 3, st3, km3, st2, km2, false);
+    }
+    __syncthreads();  // every wave is done with the stages and the exchange area
+    xm[wave][lane] = m_seen;
+    __syncthreads();
+    const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
+    const float dev = (mall - m_ref) * a.scale_log2;
+    if (__any(mall != -INFINITY && fabsf(dev) > 64.0f) && lane == 0) atomicOr(ovf, 1);
+    __syncthreads();
+    const int again = *ovf;
+    __syncthreads();
+    if (!again || pass == 1) break;
+    m_ref = mall;  // exact reference for the second pass
+  }
+
+  // ---- dq = RoPE(scale / l * acc, -P), staged by head rows, written coalesced
+  xm[wave][lane] = l_run;
+  __syncthreads();
+  l_run = halves_sum2(l_run + xm[wave ^ 1][lane]);
+  if (a.sinks && h < a.H) l_run += __builtin_amdgcn_exp2f(sk[h] * kLog2e - m_ref * a.scale_log2);
+  const float f = l_run > 0.f ? a.scale / l_run : 0.f;
+  {
+    unsigned char* os = hg == 0 ? st0 : st1;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 256 * dh + 32 * db + 8 * j + 4 * g;
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = O[db][4 * j + i] * f;
+        if (d0 >= rlo) {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float2 r = cs[(d0 + i - rlo) >> 1];
+            const float x0 = x[i], x1 = x[i + 1];
+            x[i] = x0 * r.x + x1 * r.y;
+            x[i + 1] = -x0 * r.y + x1 * r.x;
+          }
+        }
+        bf16 y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = (bf16)x[i];
+        *reinterpret_cast<uint2*>(os + off(l32, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
+      }
+  }
+  __syncthreads();
+  unsigned char* dqg = reinterpret_cast<unsigned char*>(a.dq) + row0;
+  for (int c = threadIdx.x; c < a.H * (ROWB / 16); c += NT) {
+    const int row = c >> 6, col = (c & 63) * 16;
+    *reinterpret_cast<uint4*>(dqg + (int64_t)row * ROWB + col) =
+        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + off(row & 31, col));
+  }
+}
+
 template <typename T, int D>
 void launch_d(const DqArgs& a, int H, hipStream_t st) {
   const dim3 grid(a.B * a.S);
+  if constexpr (D == 512 && sizeof(T) == 2) {
+    if (H > 16) {
+      hipLaunchKernelGGL(mqa_bwd_dq_hd_kernel, grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
   if (H <= 16) hipLaunchKernelGGL((mqa_bwd_dq_kernel<T, D, 1>), grid, dim3(64), 0, st, a);
   else hipLaunchKernelGGL((mqa_bwd_dq_kernel<T, D, 4>), grid, dim3(256), 0, st, a);
 }
