@@ -41,12 +41,15 @@ CASES = {
     "hca_4096": (wl.C2.replace(S=4096, name="hca_4096"), 24, False),
     "swa_1024": (wl.C1.replace(kind="swa", topk=0, S=1024, name="swa_1024"), 24, False),
     "edge": (EDGE, None, False),
+    "hd_h40": (wl.C1.replace(H=40, S=512, name="dq_h40"), None, False),   # head-group kernel, padded heads
     "C3": (wl.C3, 12, False),
 }
 
 
-def dq_check(bd, cfg, n_rows, with_sink):
+def dq_check(bd, cfg, n_rows, with_sink, edit=None, rel=None):
     inp = gen(cfg)
+    if edit is not None:
+        edit(inp)
     p = bd.params(cfg)
     rows = [(b, t) for b in range(cfg.B) for t in range(cfg.S)] if n_rows is None else sample_rows(cfg, n_rows)
     lz = lazy_inputs(inp)
@@ -78,7 +81,7 @@ def dq_check(bd, cfg, n_rows, with_sink):
     do_np = {(b, t): d_o[b, t].float().cpu().double().numpy() for (b, t) in rows}
     want = O.layer_dq_rows(cfg, lz, rows, do_np, sel, kv_ora if kv_ora is not None else {}, sinks=sinks64)
     got = np.stack([dq[b, t].float().cpu().double().numpy() for (b, t) in rows])
-    return assert_close_rel(got, np.stack([want[k] for k in rows]), tol(cfg), f"dq {cfg.name}")
+    return assert_close_rel(got, np.stack([want[k] for k in rows]), rel or tol(cfg), f"dq {cfg.name}")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -111,3 +114,19 @@ def test_dq_deterministic(bd):
     b = bd.sparse_mqa_bwd_dq(p, inp["q"], kv, inp["kv_raw"], idx, o, d_o)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_dq_large_logit_range_recomputes_exactly(bd):
+    """q[..., 0] = 4 and the window latents' dim 0 raised by 100 lift every window logit
+    by about 72 (log2 units) over the selected entries, which fill the first tile of the
+    rows t >= 127 (topk 40): the kernel must run its second pass with the exact
+    reference.  fp32, no RoPE.  dq's dim 0 is a sum of terms of size ~3 that cancel
+    (the common offset), so the bound is 1e-3 of the largest |dq| instead of 1e-5 (one
+    run measured 4.9e-4); a second pass that kept the first pass's sums or reference
+    would be off by O(1)."""
+    cfg = wl.C0.replace(topk=40, rope_dim=0, name="dq_wide_logits")
+
+    def edit(inp):
+        inp["q"][..., 0] = 4.0
+        inp["kv_raw"][..., 0] += 100.0
+    dq_check(bd, cfg, None, False, edit=edit, rel=1e-3)
