@@ -85,6 +85,7 @@ KERNEL_SOURCES = {
     "index_topk": ("index_topk_kernel", ["indexer.hip"]),
     "topk": ("topk_kernel", ["topk.hip"]),
     "attention": ("sparse_mqa", ["sparse_mqa.hip"]),
+    "bwd_dq": ("mqa_bwd_dq", ["mqa_bwd.hip", "mqa_bwd.hpp"]),
 }
 COMMON_SOURCES = ["common.hpp", "launch.hpp"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
