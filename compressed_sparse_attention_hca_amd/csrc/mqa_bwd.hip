@@ -471,7 +471,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dq_kernel(DqArgs a) {
 //   dQ^T[256 dims, 32 heads] += K^T . dz^T over all 32 keys (16 MFMAs)
 // Delta of a head is summed over the lane halves (v_permlane32_swap) and the partner.
 // Keys stream through four stages as in the generic kernel; the entry indices sit in
-// LDS.  One workgroup per CU (q, du and the accumulator take about 256 registers).
+// LDS.  The tiles are software-pipelined: the partial products of tile t+1 are issued
+// while tile t's exchange, softmax and dz run, and one barrier per tile is both tile
+// t's exchange barrier and tile t+1's arrival, so a tile costs two barriers, not three.  One workgroup per CU (q, du and the accumulator take about 256 registers).
 // ---------------------------------------------------------------------------------
 __device__ inline float halves_sum2(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -650,22 +652,25 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
   float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
   f32x16 O[8];
 
-  auto compute = [&](const unsigned char* sb, uint32_t kmask, bool first) {
+  // Partial S^T and dP^T of the tile in `sb` over this wave's 256 dims.
+  auto qk = [&](const unsigned char* sb, f32x16& s, f32x16& dp) {
     const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
-    f32x16 s = {}, dp = {};
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, uf[k], dp, 0, 0, 0);
-      if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      xh[wave][q][lane] = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
-      xd[wave][q][lane] = f32x4{dp[8 + 4 * q], dp[9 + 4 * q], dp[10 + 4 * q], dp[11 + 4 * q]};
-    }
-    lds_barrier2();
+  };
+  // The rest of a tile once its partials are in xh / xd and the exchange barrier is
+  // passed; `nxt` (may be null): the next tile, whose partial products are issued
+  // here so that the MFMA pipe works while this tile's softmax and exchange run.
+  auto rest = [&](const unsigned char* sb, uint32_t kmask, bool first, const f32x16& s, const f32x16& dp,
+                  const unsigned char* nxt, f32x16& sn, f32x16& dpn) {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
+    if (nxt) qk(nxt, sn, dpn);
     float z[8], dv[8];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -720,15 +725,25 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
     }
   };
 
-  // One pipeline step (see the generic kernel): wait for tile t, barrier, refill the
-  // stage of tile t-1 with tile t+3, use tile t.
-  auto step = [&](int tt, const unsigned char* cur, uint32_t kmc, unsigned char* nxt, uint32_t& kmn, bool first) {
-    const int after = min(ntiles - 1, tt + 2) - tt;
-    if (after <= 0) vm_wait_barrier<0>();
-    else if (after == 1) vm_wait_barrier<LPT>();
-    else vm_wait_barrier<2 * LPT>();
-    if (tt + 3 < ntiles) kmn = issue(tt + 3, nxt);
-    compute(cur, kmc, first);
+  auto send = [&](const f32x16& s, const f32x16& dp) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      xh[wave][q][lane] = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
+      xd[wave][q][lane] = f32x4{dp[8 + 4 * q], dp[9 + 4 * q], dp[10 + 4 * q], dp[11 + 4 * q]};
+    }
+  };
+  // Tile t, its partials (s, dp) already formed: send them, then one barrier that is
+  // both the exchange barrier of tile t and the arrival of tile t+1 (at most tile t+2
+  // may still be in flight); refill the stage of tile t-1 with tile t+3; form tile t+1's
+  // partials while finishing tile t.
+  f32x16 sA, dA, sB, dB;
+  auto iter = [&](int tt, const unsigned char* cur, uint32_t kmc, const unsigned char* n1, unsigned char* n3,
+                  uint32_t& km3r, bool first, f32x16& s, f32x16& dp, f32x16& sn, f32x16& dpn) {
+    send(s, dp);
+    if (tt + 2 < ntiles) vm_wait_barrier<LPT>();
+    else vm_wait_barrier<0>();
+    if (tt + 3 < ntiles) km3r = issue(tt + 3, n3);
+    rest(cur, kmc, first, s, dp, tt + 1 < ntiles ? n1 : nullptr, sn, dpn);
   };
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -737,11 +752,17 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
       for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
     l_run = 0.f;
     if (pass > 0) prologue_issue();
+    if (ntiles > 0) {
+      if (ntiles > 2) vm_wait_barrier<2 * LPT>();
+      else if (ntiles > 1) vm_wait_barrier<LPT>();
+      else vm_wait_barrier<0>();
+      qk(st0, sA, dA);
+    }
     for (int tile = 0; tile < ntiles; tile += 4) {
-      step(tile, st0, km0, st3, km3, pass == 0 && tile == 0);
-      if (tile + 1 < ntiles) step(tile + 1, st1, km1, st0, km0, false);
-      if (tile + 2 < ntiles) step(tile + 2, st2, km2, st1, km1, false);
-      if (tile + 3 < ntiles) step(tile + 3, st3, km3, st2, km2, false);
+      iter(tile, st0, km0, st1, st3, km3, pass == 0 && tile == 0, sA, dA, sB, dB);
+      if (tile + 1 < ntiles) iter(tile + 1, st1, km1, st2, st0, km0, false, sB, dB, sA, dA);
+      if (tile + 2 < ntiles) iter(tile + 2, st2, km2, st3, st1, km1, false, sA, dA, sB, dB);
+      if (tile + 3 < ntiles) iter(tile + 3, st3, km3, st0, st2, km2, false, sB, dB, sA, dA);
     }
     __syncthreads();  // every wave is done with the stages and the exchange area
     xm[wave][lane] = m_seen;
