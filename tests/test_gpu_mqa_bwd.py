@@ -42,6 +42,7 @@ CASES = {
     "swa_1024": (wl.C1.replace(kind="swa", topk=0, S=1024, name="swa_1024"), 24, False),
     "edge": (EDGE, None, False),
     "hd_h40": (wl.C1.replace(H=40, S=512, name="dq_h40"), None, False),   # head-group kernel, padded heads
+    "C2": (wl.C2, 12, False),                                            # HCA, S=65536
     "C3": (wl.C3, 12, False),
 }
 
