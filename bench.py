@@ -77,6 +77,12 @@ def roofline_entry(amount, unit, bound, ms, peak_tflops=PEAK_BF16_TFLOPS):
             "frac": round(achieved / PEAK_HBM_GBS, 4)}
 
 
+def dtype_label(index_fp8: bool) -> str:
+    """The arithmetic type of the step: bf16 operands with fp32 accumulation, and with
+    the FP8 indexer the indexer's QK on E4M3 codes."""
+    return "bf16, indexer QK fp8 (e4m3)" if index_fp8 else "bf16"
+
+
 # Library kernel -> (rocprofv3 kernel-name fragment, source files it is built from).
 KERNEL_SOURCES = {
     "compress": ("compress_kernel", ["compress.hip"]),
@@ -236,6 +242,44 @@ def cpu_baseline(cfg, inp, budget_s: float):
             "seconds": round(t_comp + t_rows, 2)}
 
 
+def stack_configs(index_fp8: bool = False):
+    """The 43-layer stack's layer configs; with index_fp8 every CSA layer's indexer QK
+    runs on E4M3 operands."""
+    from compressed_sparse_attention_hca_amd import workloads as wl
+    layers = wl.stack_layers()
+    if index_fp8:
+        layers = [c.replace(index_fp8=True) if c.kind == wl.CSA else c for c in layers]
+    return layers
+
+
+def stack_line(args, layers, ms_step: float, ms_per_kind: dict) -> dict:
+    """The JSON line of the 43-layer stack from its measured step time and the summed
+    per-kind layer times (ms per step)."""
+    from compressed_sparse_attention_hca_amd import workloads as wl
+    flops = sum(wl.layer_flops(c)["total"] for c in layers)
+    B, S = layers[0].B, layers[0].S
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    counts = {kd: sum(1 for c in layers if c.kind == kd) for kd in ms_per_kind}
+    fp8 = any(c.index_fp8 for c in layers)
+    return {
+        "metric": "43-layer V4-Flash attention stack fwd tokens/s (B=4, S=8192, 1 GPU)",
+        "value": round(B * S / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_label(fp8),
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": "v4flash_stack43_bf16_B4_S8192" + ("+index_fp8" if fp8 else ""),
+                   "B": B, "S": S, "layers": len(layers),
+                   "csa": counts.get("csa", 0), "hca": counts.get("hca", 0), "swa": counts.get("swa", 0),
+                   "index_fp8": fp8},
+        "layer_tokens_per_s": round(len(layers) * B * S / (ms_step * 1e-3), 1),
+        "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": flops,
+        "ms_per_kind": {kd: round(v, 3) for kd, v in ms_per_kind.items()},
+        "ms_per_layer_of_kind": {kd: round(v / counts[kd], 3) for kd, v in ms_per_kind.items()},
+    }
+
+
 def run_stack(args, dev) -> dict:
     """The 43-layer training-shape stack (B=4, S=8192): every layer's seeded inputs are
     generated once and stay resident (about 110 GB); a step runs all 43 layers in order
@@ -245,7 +289,7 @@ def run_stack(args, dev) -> dict:
     from compressed_sparse_attention_hca_amd import binding as bd
     from compressed_sparse_attention_hca_amd import workloads as wl
 
-    layers = wl.stack_layers()
+    layers = stack_configs(args.index_fp8)
     log(f"[bench] 43-layer stack: generating inputs on the GPU")
     inps = [wl.make_inputs(c, dev) for c in layers]
     params = [bd.params(c) for c in layers]
@@ -281,28 +325,63 @@ def run_stack(args, dev) -> dict:
     for s in range(args.steps):
         for k, c in enumerate(layers):
             per_kind[c.kind] = per_kind.get(c.kind, 0.0) + ev[s][k].elapsed_time(ev[s][k + 1]) / args.steps
-    flops = sum(wl.layer_flops(c)["total"] for c in layers)
-    B, S = layers[0].B, layers[0].S
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    counts = {kd: sum(1 for c in layers if c.kind == kd) for kd in per_kind}
+    return stack_line(args, layers, ms_step, per_kind)
+
+
+def layer_line(args, cfg, ms_step: float, tot: dict, launches: dict, traffic_path, with_kl: bool,
+               with_dq: bool) -> dict:
+    """The JSON line of one fused layer from its measured step time and the per-kernel
+    times (ms per step) and launch counts."""
+    from compressed_sparse_attention_hca_amd import workloads as wl
+    work = kernel_work(cfg, wl)
+    kernels = {}
+    for k, v in tot.items():
+        amt, unit, bound = work[k]
+        fp8_qk = cfg.index_fp8 and k in ("index_topk", "indexer")
+        e = roofline_entry(amt, unit, bound, v, PEAK_FP8_TFLOPS if fp8_qk else PEAK_BF16_TFLOPS)
+        e.update({"ms_per_step": round(v, 4), "launches_per_step": launches[k],
+                  "avg_launch_ms": round(v / launches[k], 4)})
+        kernels[k] = e
+    dom = max(tot, key=tot.get)
+    traffic = traffic_for(dom, traffic_path)
+    d = kernels[dom]
+    amt, unit, bound = work[dom]
+    roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
+            "unit": d["unit"], "frac": d["frac"], "traffic": traffic,
+            "work_per_step": amt, "work_unit": unit, "launches_per_step": launches[dom],
+            "avg_launch_ms": d["avg_launch_ms"]}
+
+    f = wl.layer_flops(cfg)
+    if with_kl:  # the step also forms the distillation target
+        f = dict(f, total=f["total"] + work["kl_target"][0])
+    if with_dq:  # and the attention backward's query side
+        f = dict(f, total=f["total"] + work["bwd_dq"][0])
+    tokens = cfg.B * cfg.S
+    value = tokens / (ms_step * 1e-3)
+    tflops = f["total"] / (ms_step * 1e-3) / 1e12
     return {
-        "metric": "43-layer V4-Flash attention stack fwd tokens/s (B=4, S=8192, 1 GPU)",
-        "value": round(B * S / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16, indexer QK fp8 (e4m3)" if cfg.index_fp8 else "bf16",
+        "dtype": dtype_label(cfg.index_fp8),
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": "v4flash_stack43_bf16_B4_S8192", "B": B, "S": S, "layers": len(layers),
-                   "csa": counts.get("csa", 0), "hca": counts.get("hca", 0), "swa": counts.get("swa", 0)},
-        "layer_tokens_per_s": round(len(layers) * B * S / (ms_step * 1e-3), 1),
+        "config": {"workload": cfg.name + ("+kl_target" if with_kl else "") + ("+bwd_dq" if with_dq else ""),
+                   "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
+                   "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
+                   "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
+                   "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue),
+                   "index_fp8": bool(cfg.index_fp8)},
         "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "flops_per_step": flops,
-        "ms_per_kind": {kd: round(v, 3) for kd, v in per_kind.items()},
-        "ms_per_layer_of_kind": {kd: round(v / counts[kd], 3) for kd, v in per_kind.items()},
+        "flops_per_step": f["total"],
+        "page_convention_attention_tflops": round(
+            wl.page_convention_attention_flops(cfg) / (tot.get("attention", ms_step) * 1e-3) / 1e12, 2),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
     }
 
 
-def main():
+def make_parser():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
@@ -331,7 +410,11 @@ def main():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB twice (a plain copy "
                          "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = make_parser().parse_args()
 
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     if args.summarize_counters:
@@ -453,50 +536,7 @@ def main():
     if dq is not None:  # window rotation + dQ kernel, timed together on the step's stream
         tot["bwd_dq"] = sum(a.elapsed_time(b) for a, b in dq["ev"]) / args.steps
         launches["bwd_dq"] = 1
-    work = kernel_work(cfg, wl)
-    kernels = {}
-    for k, v in tot.items():
-        amt, unit, bound = work[k]
-        fp8_qk = cfg.index_fp8 and k in ("index_topk", "indexer")
-        e = roofline_entry(amt, unit, bound, v, PEAK_FP8_TFLOPS if fp8_qk else PEAK_BF16_TFLOPS)
-        e.update({"ms_per_step": round(v, 4), "launches_per_step": launches[k],
-                  "avg_launch_ms": round(v / launches[k], 4)})
-        kernels[k] = e
-    dom = max(tot, key=tot.get)
-    traffic = traffic_for(dom, traffic_path)
-    d = kernels[dom]
-    amt, unit, bound = work[dom]
-    roof = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
-            "unit": d["unit"], "frac": d["frac"], "traffic": traffic,
-            "work_per_step": amt, "work_unit": unit, "launches_per_step": launches[dom],
-            "avg_launch_ms": d["avg_launch_ms"]}
-
-    f = wl.layer_flops(cfg)
-    if kl is not None:  # the step also forms the distillation target
-        f = dict(f, total=f["total"] + work["kl_target"][0])
-    if dq is not None:  # and the attention backward's query side
-        f = dict(f, total=f["total"] + work["bwd_dq"][0])
-    tokens = cfg.B * cfg.S
-    value = tokens / (ms_step * 1e-3)
-    tflops = f["total"] / (ms_step * 1e-3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": cfg.name + ("+kl_target" if kl is not None else "") + ("+bwd_dq" if dq is not None else ""), "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
-                   "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
-                   "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
-                   "sink": bool(args.sink), "index_prologue": bool(cfg.index_prologue),
-                   "index_fp8": bool(cfg.index_fp8)},
-        "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "flops_per_step": f["total"],
-        "page_convention_attention_tflops": round(
-            wl.page_convention_attention_flops(cfg) / (tot.get("attention", ms_step) * 1e-3) / 1e12, 2),
-        "kernels": kernels,
-        "roofline": roof,
-        "cpu_baseline": None,
-    }
+    out = layer_line(args, cfg, ms_step, tot, launches, traffic_path, kl is not None, dq is not None)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

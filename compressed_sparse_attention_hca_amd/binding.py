@@ -136,6 +136,35 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _act(p: Params) -> torch.dtype:
+    return torch.bfloat16 if p.dtype == CSA_BF16 else torch.float32
+
+
+def _chk(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype, required: bool = True):
+    """The C ABI sees only pointers, so a tensor of the wrong dtype or size would make a
+    kernel read or write past its end: check both against the params here."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name}: a tensor is required")
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    n = 1
+    for s in shape:
+        n *= int(s)
+    if t.numel() != n:
+        raise ValueError(f"{name}: {t.numel()} elements (shape {tuple(t.shape)}), expected "
+                         f"{n} for shape {tuple(int(s) for s in shape)}")
+
+
+def _key_rows(p: Params):
+    """Shape and dtype of the indexer keys after csa_index_keys for p.flags."""
+    n = p.S // p.ratio
+    if p.flags & FLAG_INDEX_FP8:
+        return (p.B, n, p.idx_dim + 16), torch.uint8
+    return (p.B, n, p.idx_dim), _act(p)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -154,6 +183,13 @@ def compress(p: Params, va, ga, vb, gb, bias, kv_c=None, stream=None) -> torch.T
     n = p.S // p.ratio
     if kv_c is None:
         kv_c = torch.empty((p.B, n, p.D), dtype=va.dtype, device=va.device)
+    act, bsd = _act(p), (p.B, p.S, p.D)
+    for t, nm in ((va, "va"), (ga, "ga")):
+        _chk(t, nm, bsd, act)
+    for t, nm in ((vb, "vb"), (gb, "gb")):
+        _chk(t, nm, bsd, act, required=False)
+    _chk(bias, "bias", ((2 if p.overlap else 1) * p.ratio, p.D), torch.float32)
+    _chk(kv_c, "kv_c", (p.B, n, p.D), act)
     check(lib.csa_compress(ctypes.byref(p), _ptr(va), _ptr(ga), _ptr(vb), _ptr(gb), _ptr(bias),
                            _ptr(kv_c), _stream(stream)))
     return kv_c
@@ -164,9 +200,23 @@ def index_scores(p: Params, q_idx, w_idx, k_idx, t0=0, nrows=None, scores=None, 
     ld = max(p.S // p.ratio, 1)
     if scores is None:
         scores = torch.full((p.B, nrows, ld), float("nan"), dtype=torch.float32, device=q_idx.device)
+    _chk_indexer(p, q_idx, w_idx)
+    kshape, kdt = _key_rows(p) if p.flags & (FLAG_INDEX_FP8 | FLAG_INDEX_PROLOGUE) else \
+        ((p.B, p.S // p.ratio, p.idx_dim), _act(p))
+    _chk(k_idx, "k_idx", kshape, kdt)
+    if scores.dtype != torch.float32 or scores.dim() != 3 or scores.shape[0] != p.B or \
+            scores.shape[1] < nrows or scores.shape[2] < max(p.S // p.ratio, 1):
+        raise ValueError(f"scores: need fp32 [B, >= nrows, >= S/ratio], got {scores.dtype} {tuple(scores.shape)}")
+    if t0 < 0 or nrows < 0 or t0 + nrows > p.S:
+        raise ValueError(f"rows {t0}..{t0 + nrows} outside 0..{p.S}")
     check(lib.csa_index_scores(ctypes.byref(p), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(scores),
                                scores.shape[-1], t0, nrows, _stream(stream)))
     return scores
+
+
+def _chk_indexer(p: Params, q_idx, w_idx):
+    _chk(q_idx, "q_idx", (p.B, p.S, p.idx_heads, p.idx_dim), _act(p))
+    _chk(w_idx, "w_idx", (p.B, p.S, p.idx_heads), torch.float32)
 
 
 def index_keys(p: Params, k_idx, k_out=None, stream=None) -> torch.Tensor:
@@ -178,6 +228,9 @@ def index_keys(p: Params, k_idx, k_out=None, stream=None) -> torch.Tensor:
             k_out = torch.empty((p.B, p.S // p.ratio, p.idx_dim + 16), dtype=torch.uint8, device=k_idx.device)
         else:
             k_out = torch.empty_like(k_idx)
+    _chk(k_idx, "k_idx", (p.B, p.S // p.ratio, p.idx_dim), _act(p))
+    kshape, kdt = _key_rows(p)
+    _chk(k_out, "k_out", kshape, kdt)
     check(lib.csa_index_keys(ctypes.byref(p), _ptr(k_idx), _ptr(k_out), _stream(stream)))
     return k_out
 
@@ -190,9 +243,31 @@ def index_topk(p: Params, q_idx, w_idx, k_idx, idx=None, n_visible=None, ws=None
         n_visible = torch.empty((p.B, p.S), dtype=torch.int32, device=dev)
     if ws is None:
         ws = workspace(p, OP_INDEX_TOPK, dev)
+    _chk_indexer(p, q_idx, w_idx)
+    _chk(k_idx, "k_idx", (p.B, p.S // p.ratio, p.idx_dim), _act(p))
+    _chk(idx, "idx", (p.B, p.S, p.topk), torch.int32)
+    _chk(n_visible, "n_visible", (p.B, p.S), torch.int32)
+    _chk_ws(ws)
     check(lib.csa_index_topk(ctypes.byref(p), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(idx),
                              _ptr(n_visible), _ptr(ws), ws.numel(), _stream(stream)))
     return idx, n_visible
+
+
+def _chk_ws(ws):
+    if ws is not None and ws.dtype != torch.uint8:
+        raise ValueError(f"ws: dtype {ws.dtype}, expected torch.uint8")
+
+
+def _chk_attn(p: Params, q, kv_c, kv_raw, idx, sinks, **outs):
+    act = _act(p)
+    bshd = (p.B, p.S, p.H, p.D)
+    _chk(q, "q", bshd, act)
+    _chk(kv_c, "kv_c", (p.B, p.S // p.ratio, p.D), act, required=False)
+    _chk(kv_raw, "kv_raw", (p.B, p.S, p.D), act)
+    _chk(idx, "idx", (p.B, p.S, p.topk), torch.int32, required=False)
+    _chk(sinks, "sinks", (p.H,), torch.float32, required=False)
+    for nm, t in outs.items():
+        _chk(t, nm, bshd, act)
 
 
 def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream=None, sinks=None):
@@ -201,6 +276,8 @@ def sparse_mqa_fwd(p: Params, q, kv_c, kv_raw, idx=None, o=None, ws=None, stream
         o = torch.empty_like(q)
     if ws is None:
         ws = workspace(p, OP_SPARSE_MQA, q.device)
+    _chk_attn(p, q, kv_c, kv_raw, idx, sinks, o=o)
+    _chk_ws(ws)
     if sinks is None:
         check(lib.csa_sparse_mqa_fwd(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx), _ptr(o),
                                      _ptr(ws), ws.numel(), _stream(stream)))
@@ -218,6 +295,8 @@ def sparse_mqa_bwd_dq(p: Params, q, kv_c, kv_raw, idx, o, d_o, dq=None, ws=None,
         dq = torch.empty_like(q)
     if ws is None:
         ws = workspace(p, OP_SPARSE_MQA, q.device)
+    _chk_attn(p, q, kv_c, kv_raw, idx, sinks, o=o, d_o=d_o, dq=dq)
+    _chk_ws(ws)
     check(lib.csa_sparse_mqa_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx),
                                     _ptr(sinks), _ptr(o), _ptr(d_o), _ptr(dq), _ptr(ws), ws.numel(),
                                     _stream(stream)))
@@ -228,8 +307,31 @@ def kl_target(p: Params, q, kv_c, idx, target=None, stream=None) -> torch.Tensor
     """csa_kl_target: [B, S, topk] fp32 target of the indexer's distillation loss."""
     if target is None:
         target = torch.empty((p.B, p.S, p.topk), dtype=torch.float32, device=q.device)
+    _chk(q, "q", (p.B, p.S, p.H, p.D), _act(p))
+    _chk(kv_c, "kv_c", (p.B, p.S // p.ratio, p.D), _act(p))
+    _chk(idx, "idx", (p.B, p.S, p.topk), torch.int32)
+    _chk(target, "target", (p.B, p.S, p.topk), torch.float32)
     check(lib.csa_kl_target(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(idx), _ptr(target), _stream(stream)))
     return target
+
+
+def _chk_layer(p: Params, inp: dict, o, kv_c_out, idx_out, n_visible_out):
+    act = _act(p)
+    g = inp.get
+    csa = bool(p.overlap)
+    _chk_attn(p, g("q"), None, g("kv_raw"), None, g("sinks"), o=o)
+    bsd = (p.B, p.S, p.D)
+    _chk(g("va"), "va", bsd, act)
+    _chk(g("ga"), "ga", bsd, act)
+    _chk(g("vb"), "vb", bsd, act, required=csa)
+    _chk(g("gb"), "gb", bsd, act, required=csa)
+    _chk(g("bias"), "bias", ((2 if csa else 1) * p.ratio, p.D), torch.float32)
+    if csa:
+        _chk_indexer(p, g("q_idx"), g("w_idx"))
+        _chk(g("k_idx"), "k_idx", (p.B, p.S // p.ratio, p.idx_dim), act)
+        _chk(idx_out, "idx_out", (p.B, p.S, p.topk), torch.int32, required=False)
+        _chk(n_visible_out, "n_visible_out", (p.B, p.S), torch.int32, required=False)
+    _chk(kv_c_out, "kv_c_out", (p.B, p.S // p.ratio, p.D), act, required=False)
 
 
 def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=None) -> Inputs:
@@ -249,6 +351,8 @@ def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None,
     op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
     if ws is None:
         ws = workspace(p, op, q.device)
+    _chk_layer(p, inp, o, kv_c_out, idx_out, n_visible_out)
+    _chk_ws(ws)
     s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
     f = lib.csa_fwd if p.overlap else lib.hca_fwd
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
@@ -289,6 +393,8 @@ def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, s
     op = OP_CSA_FWD if p.overlap else OP_HCA_FWD
     if ws is None:
         ws = workspace(p, op, q.device)
+    _chk_layer(p, inp, o, kv_c_out, idx_out, n_visible_out)
+    _chk_ws(ws)
     s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
     f = lib.csa_fwd_traced if p.overlap else lib.hca_fwd_traced
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream),

@@ -271,3 +271,91 @@ def test_bwd_dq_rejects():
     assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
     z = ctypes.byref(p_c1(B=0))
     assert bd.lib.csa_sparse_mqa_bwd_dq(z, None, None, None, None, None, None, None, None, None, 0, None) == bd.CSA_OK
+
+
+# ---- the binding checks dtype and size against the params before any call --------
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _attn_args(cfg, act):
+    import torch
+    B, S, H, D = cfg.B, cfg.S, cfg.H, cfg.D
+    return dict(q=_t((B, S, H, D), act), kv_c=_t((B, S // cfg.ratio, D), act),
+                kv_raw=_t((B, S, D), act), idx=_t((B, S, cfg.topk), torch.int32))
+
+
+@pytest.mark.parametrize("bad", ["q_dtype", "q_size", "idx_dtype", "idx_size", "kv_raw_size",
+                                 "sinks_dtype", "o_size"])
+def test_binding_rejects_mismatched_attention_tensors(bad):
+    import torch
+    cfg = wl.C0.replace(S=32)
+    p = bd.params(cfg)
+    a = _attn_args(cfg, torch.float32)
+    o = _t(a["q"].shape, torch.float32)
+    sinks = None
+    if bad == "q_dtype":
+        a["q"] = a["q"].to(torch.bfloat16)
+    elif bad == "q_size":
+        a["q"] = _t((1, 32, cfg.H + 1, cfg.D), torch.float32)
+    elif bad == "idx_dtype":
+        a["idx"] = a["idx"].to(torch.int64)
+    elif bad == "idx_size":
+        a["idx"] = _t((1, 32, cfg.topk - 1), torch.int32)
+    elif bad == "kv_raw_size":
+        a["kv_raw"] = _t((1, 31, cfg.D), torch.float32)
+    elif bad == "sinks_dtype":
+        sinks = _t((cfg.H,), torch.float64)
+    elif bad == "o_size":
+        o = _t((1, 32, cfg.H, cfg.D // 2), torch.float32)
+    name = bad.rsplit("_", 1)[0]
+    with pytest.raises(ValueError, match=name):
+        bd.sparse_mqa_fwd(p, a["q"], a["kv_c"], a["kv_raw"], a["idx"], o=o, ws=_t((256,), torch.uint8),
+                          sinks=sinks)
+    with pytest.raises(ValueError, match=name):
+        bd.sparse_mqa_bwd_dq(p, a["q"], a["kv_c"], a["kv_raw"], a["idx"], o, o.clone(), dq=o.clone(),
+                             ws=_t((256,), torch.uint8), sinks=sinks)
+
+
+def test_binding_rejects_mismatched_indexer_and_compress_tensors():
+    import torch
+    cfg = wl.C1.replace(S=64)
+    p = bd.params(cfg)
+    bf = torch.bfloat16
+    B, S, HI, DI, D = cfg.B, cfg.S, cfg.idx_heads, cfg.idx_dim, cfg.D
+    q_idx, w_idx, k_idx = _t((B, S, HI, DI), bf), _t((B, S, HI), torch.float32), _t((B, S // 4, DI), bf)
+    with pytest.raises(ValueError, match="w_idx"):
+        bd.index_topk(p, q_idx, w_idx.to(bf), k_idx, idx=_t((B, S, cfg.topk), torch.int32),
+                      n_visible=_t((B, S), torch.int32), ws=_t((256,), torch.uint8))
+    with pytest.raises(ValueError, match="k_idx"):
+        bd.index_topk(p, q_idx, w_idx, _t((B, S // 4, DI * 2), bf), idx=_t((B, S, cfg.topk), torch.int32),
+                      n_visible=_t((B, S), torch.int32), ws=_t((256,), torch.uint8))
+    with pytest.raises(ValueError, match="n_visible"):
+        bd.index_topk(p, q_idx, w_idx, k_idx, idx=_t((B, S, cfg.topk), torch.int32),
+                      n_visible=_t((B, S + 1), torch.int32), ws=_t((256,), torch.uint8))
+    p8 = bd.params(cfg.replace(index_fp8=True))
+    with pytest.raises(ValueError, match="k_out"):   # fp8 key rows are uint8 [B, n, DI + 16]
+        bd.index_keys(p8, k_idx, k_out=_t((B, S // 4, DI), bf))
+    with pytest.raises(ValueError, match="bias"):
+        bd.compress(p, _t((B, S, D), bf), _t((B, S, D), bf), _t((B, S, D), bf), _t((B, S, D), bf),
+                    _t((4, D), torch.float32), kv_c=_t((B, S // 4, D), bf))
+    with pytest.raises(ValueError, match="target"):
+        bd.kl_target(p, _t((B, S, cfg.H, D), bf), _t((B, S // 4, D), bf), _t((B, S, cfg.topk), torch.int32),
+                     target=_t((B, S, cfg.topk), bf))
+
+
+def test_binding_rejects_mismatched_layer_inputs():
+    import torch
+    cfg = wl.C0.replace(S=32)
+    p = bd.params(cfg)
+    inp = wl.make_inputs(cfg)
+    o = torch.empty_like(inp["q"])
+    bad = dict(inp, gb=inp["gb"][:, :16].contiguous())
+    with pytest.raises(ValueError, match="gb"):
+        bd.layer_fwd(p, bad, o=o, ws=_t((256,), torch.uint8))
+    with pytest.raises(ValueError, match="idx_out"):
+        bd.layer_fwd(p, inp, o=o, ws=_t((256,), torch.uint8), idx_out=_t((1, 32, cfg.topk), torch.int64))
+    # a well-formed call reaches the pointer marshalling, which wants device tensors
+    with pytest.raises(ValueError, match="GPU"):
+        bd.layer_fwd(p, inp, o=o, ws=_t((256,), torch.uint8))
