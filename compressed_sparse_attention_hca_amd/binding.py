@@ -65,6 +65,7 @@ def _load():
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_bwd_dq": [P, V, V, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
+        "csa_fwd_noalloc": [P, ctypes.POINTER(Inputs), V, V],
         "hca_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "csa_debug_layout": [P, V, V, V, V],
         "csa_fwd_traced": [P, ctypes.POINTER(Inputs), V, V, SZ, V, ctypes.POINTER(V),
@@ -94,6 +95,7 @@ lib = _load()
 EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_keys",
            "csa_sparse_mqa_fwd",
            "csa_sparse_mqa_fwd_sink", "csa_sparse_mqa_bwd_dq", "csa_kl_target", "csa_fwd",
+           "csa_fwd_noalloc",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
            "csa_abi_version")
@@ -357,6 +359,22 @@ def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None,
     f = lib.csa_fwd if p.overlap else lib.hca_fwd
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
     return o
+
+
+def csa_fwd_noalloc(p: Params, inp: dict, o=None, stream=None, kv_c_out=None, idx_out=None,
+                    n_visible_out=None):
+    """csa_fwd_noalloc: the fused CSA layer with the library's static workspace (no ws
+    argument; the call allocates nothing)."""
+    q = inp["q"]
+    if o is None:
+        o = torch.empty_like(q)
+    _chk_layer(p, inp, o, kv_c_out, idx_out, n_visible_out)
+    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
+    check(lib.csa_fwd_noalloc(ctypes.byref(p), ctypes.byref(s), _ptr(o), _stream(stream)))
+    return o
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class LayerTrace:

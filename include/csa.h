@@ -28,14 +28,15 @@
  *     only enqueues work on that stream and returns; nothing synchronises.
  *   - The library never allocates or frees memory.  The caller owns every buffer,
  *     including the workspace, whose size comes from csa_workspace_bytes(); its
- *     contents are undefined on return.
+ *     contents are undefined on return.  (csa_fwd_noalloc alone uses a static
+ *     workspace that the library holds; see there.)
  *   - Arguments are validated on the host before any launch.  A bad argument
  *     returns a status and enqueues nothing; csa_last_error() then holds a
  *     thread-local message.  No exception crosses the ABI and nothing aborts.
  *     CSA_ERR_HIP reports a launch failure; errors raised while kernels run surface
  *     at the caller's next synchronisation.
  *   - Calls are re-entrant: the library keeps no global mutable state apart from the
- *     thread-local error string.
+ *     thread-local error string (and the static workspace of csa_fwd_noalloc).
  *
  * Integer layout shared by every kernel (bit-exact, see csa_debug_layout):
  *   n_visible(t) = floor((t + 1) / ratio)   entries whose whole group is seen by t
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef enum {
   CSA_OK = 0,
@@ -245,6 +246,21 @@ csa_status_t csa_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, voi
  * the indexer fields of `in` are ignored). */
 csa_status_t hca_fwd(const csa_params_t* p, const csa_inputs_t* in, void* o, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* csa_fwd without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, kernels and results as csa_fwd; the workspace is a
+ * static device array of CSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends, on the device of `stream`.  A shape whose
+ * workspace (csa_workspace_bytes(p, CSA_OP_CSA_FWD)) exceeds it returns
+ * CSA_ERR_WORKSPACE and enqueues nothing; the CSA layer at B = 1, S = 65536,
+ * D = 512 bf16, top-512 fits.  Nothing is allocated, freed or cleared.  Every call on
+ * one GPU shares that GPU's array, so two calls that overlap in time on one GPU race:
+ * keep them on one stream or order them with events.  The first call on a device also
+ * looks up the array's device address (hipGetSymbolAddress), which may briefly make
+ * that device current on the calling thread. */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+csa_status_t csa_fwd_noalloc(const csa_params_t* p, const csa_inputs_t* in, void* o, void* stream);
 
 /* Kernels of the fused calls, as reported by the traced variants below. */
 typedef enum {

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 6
+    assert bd.lib.csa_abi_version() == 7
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
