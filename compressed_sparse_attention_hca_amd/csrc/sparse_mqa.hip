@@ -418,13 +418,22 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(r.x) + __uint_as_float(r.y);
 }
 
-// Workgroup barrier ordering LDS only: outstanding global loads (the next tile's
-// direct-to-LDS copies) stay in flight.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// Barrier after this wave's LDS accesses have completed; copies in flight stay in
+// flight.  The memory clobber keeps the compiler from moving memory accesses across it,
+// and as inline assembly it also bounds the scheduling regions.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Barrier after every vector-memory load of this wave (the direct-to-LDS copies of the
+// next tile included) and its LDS accesses have completed.  The compiler does not see
+// inside the assembly, so the trailing s_waitcnt vmcnt(0) (free: the counter is already
+// 0) tells it that no load is outstanding; otherwise it keeps waits for loads it thinks
+// are pending, and in hardware those waits drain the next tile's copies.
+__device__ inline void copies_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding of vmcnt(0), expcnt and lgkmcnt not waited
 }
+
+// Scheduling groups (LLVM's AMDGPU sched_group_barrier masks): MFMA, LDS read.
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   typedef bf16 T;
@@ -434,11 +443,13 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
   __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
   __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
-  // exchange area: partial logits xh (8 KB), probabilities xp (4 KB), per-head maxima
-  // and sums xm (1 KB); the RoPE table and the overflow flag borrow it outside the loop
+  // exchange area, 1 KB per wave and block: partial logits xh[q][wave][lane] at
+  // 4096q + 1024 wave + 16 lane (8 KB), probabilities xp[wave][lane] at 8192 + 1024 wave
+  // + 16 lane (4 KB), per-head maxima and sums xm (1 KB); the RoPE table, the overflow
+  // flag and the sink logits borrow it outside the key loop.  A wave's own exchange
+  // slots and its partner's (wave ^ 1) differ by 1024, so two address registers cover
+  // them all.
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[16384];
-  f32x4 (*xh)[2][64] = reinterpret_cast<f32x4 (*)[2][64]>(xbuf);
-  u32x4 (*xp)[64] = reinterpret_cast<u32x4 (*)[64]>(xbuf + 8192);
   float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
   float2* cs = reinterpret_cast<float2*>(xbuf);  // RoPE table outside the loop
   int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
@@ -461,6 +472,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   const int hg = wave >> 1, dh = wave & 1;
   const int l32 = lane & 31;
   const int g = lane >> 5;
+  const int h = 32 * hg + l32;  // this lane's head
   const int n_t = a.mode == MQA_WINDOW_ONLY ? 0 : visible_entries(t, a.ratio);
   const int nsel = a.mode == MQA_SELECTED ? min(a.topk, n_t) : n_t;
   const int nwin = window_count(t, a.window);
@@ -471,9 +483,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
 
   auto rope_table = [&]() {
     if (threadIdx.x < a.R / 2) {
-      float c, s;
-      rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
-      cs[threadIdx.x] = make_float2(c, s);
+      float c, sn;
+      rope_cos_sin(P, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &sn);
+      cs[threadIdx.x] = make_float2(c, sn);
     }
   };
   rope_table();
@@ -484,17 +496,23 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   // Key sources, one tile ahead: lane l < 32 resolves key tile*32 + l.
   const unsigned char* kv_c = reinterpret_cast<const unsigned char*>(a.kv_c);
   const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
-  const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
-  // Every lane loads (from a clamped position, so the load is not predicated) and the
-  // value is only inspected at the next tile's issue: using it earlier would make the
-  // wave wait for the direct-to-LDS copies issued before it.
+  // Entry index of key tile*32 + l32.  Every lane loads, always (from a clamped
+  // position, or from the query's q row when no entry is gathered), so the value
+  // arrives in the same register on every path: a register merge of a load's result
+  // would make the compiler wait for it, and that wait drains the copies in flight.  The
+  // value is only inspected at the next tile's issue.
   const bool gather = a.mode == MQA_SELECTED && nsel > 0;
-  auto load_idx = [&](int tile) -> int {
-    return gather ? irow[min(tile * KT + l32, nsel - 1)] : 0;
-  };
-  const int dma_off0 = (lane ^ (2 * (wave & 3))) << 4, dma_off1 = (lane ^ (2 * (wave & 3) + 1)) << 4;
+  const int32_t* irow = gather ? a.idx + ((int64_t)b * a.S + t) * a.topk : reinterpret_cast<const int32_t*>(qg);
+  const int ilast = gather ? nsel - 1 : 0;
+  auto load_idx = [&](int tile) -> int { return irow[min(tile * KT + l32, ilast)]; };
+  // Row r = wave + 4m of a tile has swz(r) = 2 wave | (m & 1): the lane's 16-byte piece
+  // of the row comes from chunk lane ^ swz(r) and lands at LDS position `lane`.
+  const uint32_t dma_off0 = (uint32_t)(lane ^ (2 * (wave & 3))) << 4;
+  const uint32_t dma_off1 = (uint32_t)(lane ^ (2 * (wave & 3) + 1)) << 4;
   // Direct-to-LDS copy of tile `tile` (index values `sv` from load_idx): wave w loads
-  // rows w, w+4, ..., one 1 KB wave load per row; returns the tile's key-validity bits.
+  // rows w, w+4, ..., one 1 KB wave load per row (scalar row base, 32-bit lane offset);
+  // returns the tile's key-validity bits.  The copies are written in assembly, so the
+  // compiler adds no waits for them; copies_barrier() is the only wait.
   auto issue = [&](int tile, int sv, unsigned char* sb) -> uint32_t {
     const int kk = tile * KT + l32;
     const unsigned char* src = qg;  // masked keys read finite data that is never used
@@ -512,55 +530,66 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     const uint32_t bits = (uint32_t)__ballot(ok && lane < 32);
     const uint64_t sp = reinterpret_cast<uint64_t>(src);
     const uint32_t sp_lo = (uint32_t)sp, sp_hi = (uint32_t)(sp >> 32);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)sb;
 #pragma unroll
     for (int m = 0; m < KT / 4; ++m) {
-      const int r = wave + 4 * m;  // swz(r) = 2 wave | (m & 1)
+      const int r = wave + 4 * m;
       const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
-      const unsigned char* gp = reinterpret_cast<const unsigned char*>(row) + (m & 1 ? dma_off1 : dma_off0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp),
-                                       (CSA_LDS void*)(sb + r * ROWB), 16, 0, 0);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      // The row base was just written to SGPRs by v_readlane (a VALU op); a vector-memory
+      // instruction may read such an SGPR only 5 wait states later, and the compiler
+      // does not pad for an instruction inside inline assembly: s_nop 4 gives the 5 (and
+      // the 1 that the M0 write needs before the copy).
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(m & 1 ? dma_off1 : dma_off0),
+                   "s"(row), "{m0}"(lds) : "memory");
     }
     return bits;
   };
 
+  // Q^T fragments straight from global memory: lane (head 32hg + l32, g), k-step k
+  // holds dims 256dh + 16k + 8g .. +7 (bf16x8 vectors: two values per register).  Lanes
+  // of heads past H load head H-1 (no branch): their logits copy that head's, and their
+  // output rows are never written.
   bf16x8 qf[16];
+  auto load_q = [&]() {
+    const unsigned char* q0 = qg + (int64_t)min(h, a.H - 1) * ROWB + 2 * (256 * dh + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q0 + 32 * k));
+  };
+  // rotate q at +P where its dims fall in the last R
+  auto rotate_q = [&]() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int d0 = 256 * dh + 16 * k + 8 * g;
+      if (d0 + 8 > rlo) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const int d = d0 + i;
+          if (d >= rlo) {
+            const float2 r = cs[(d - rlo) >> 1];
+            const float x0 = (float)qf[k][i], x1 = (float)qf[k][i + 1];
+            qf[k][i] = (bf16)(x0 * r.x - x1 * r.y);
+            qf[k][i + 1] = (bf16)(x0 * r.y + x1 * r.x);
+          }
+        }
+      }
+    }
+  };
+
   // Pass 0's first tile is requested before q, so both latencies overlap.
   const int ntiles = (nk + KT - 1) / KT;
   uint32_t km0 = 0u, km1 = 0u;
   int sv = 0;
   {
-    const int sv0 = ntiles > 0 ? load_idx(0) : 0;
-    // Q^T fragments straight from global memory: lane (head 32hg + l32, g), k-step k
-    // holds dims 256dh + 16k + 8g .. +7 (bf16x8 vectors: two values per register)
-    const int h = 32 * hg + l32;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      qf[k] = h < a.H ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                            qg + (int64_t)h * ROWB + 2 * (256 * dh + 16 * k + 8 * g)))
-                      : bf16x8{};
+    const int sv0 = load_idx(0);
+    load_q();
     if (ntiles > 0) km0 = issue(0, sv0, st0);
-    if (ntiles > 1) sv = load_idx(1);
+    sv = load_idx(1);
     if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = a.sinks[threadIdx.x];
   }
-  __syncthreads();  // the RoPE table and sinks are written; q and key tile 0 have landed
-  // rotate q at +P where its dims fall in the last R
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int d0 = 256 * dh + 16 * k + 8 * g;
-    if (d0 + 8 > rlo) {
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const int d = d0 + i;
-        if (d >= rlo) {
-          const float2 r = cs[(d - rlo) >> 1];
-          const float x0 = (float)qf[k][i], x1 = (float)qf[k][i + 1];
-          qf[k][i] = (bf16)(x0 * r.x - x1 * r.y);
-          qf[k][i + 1] = (bf16)(x0 * r.y + x1 * r.x);
-        }
-      }
-    }
-  }
+  copies_barrier();  // the RoPE table and sinks are written; q and key tile 0 have landed
+  rotate_q();
   lds_barrier();  // the table is read; the exchange buffer may be reused
 
   // Per-lane LDS offsets.  QK: lane row l32 holds key kr = l32 ^ 16dh (this wave's own
@@ -571,18 +600,19 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   int qk_base[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) qk_base[m] = kr * ROWB + ((32 * dh + ((2 * m + g) ^ swz(kr))) << 4);
-  // PV: 16-lane group h = lane/16 covers dims 256dh + 32db + 16(h&1) .. +15; lane j of
-  // the group addresses key row 16ks + 4g + j/4 (and +8), dims + 4(j%4).  With
-  // a4 = j/4 the row's swizzle is 2a4 | g for every ks and for the +8 row, and the
+  // PV: 16-lane group hq = lane/16 covers dims 256dh + 32db + 16(hq&1) .. +15; lane j of
+  // the group addresses key row 16kh + 4g + j/4 (and +8), dims + 4(j%4).  With
+  // a4 = j/4 the row's swizzle is 2a4 | g for every kh and for the +8 row, and the
   // chunk position is 32dh + 8(db>>1) + 2((2(db&1) + hh) ^ a4) + (((j>>1)&1) ^ g):
-  // two bases (db even / odd); 128(db>>1), 16 KB ks and 8 KB for the +8 row are
-  // immediates.
+  // two bases (db even / odd); 128(db>>1), 16 KB for key half kh and 8 KB for the +8
+  // row are immediates.
   const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
   int pv_base[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
     pv_base[m] = (4 * g + a4) * ROWB +
                  ((32 * dh + 2 * ((2 * m + hh) ^ a4) + (((hj >> 1) & 1) ^ g)) << 4) + 8 * (hj & 1);
+  const int xo = 1024 * wave + 16 * lane;  // this wave's exchange slot (its partner's: xo ^ 1024)
   typedef short i16x4 __attribute__((ext_vector_type(4)));
 
   // Softmax with a fixed reference (shift invariance), as in sparse_mqa_kernel.
@@ -595,25 +625,46 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   // and the two swap their bf16 probabilities for PV.  Both use the same per-head
   // reference: the maximum of the pass's first tile, agreed through xm (0 if that tile
   // has no valid key; the end-of-pass check then catches any under- or overflow).
-  const int pv_mine = 16 * ROWB * dh, pv_other = 16 * ROWB * (dh ^ 1);
+  //
+  // The LDS fragment reads of both products run ahead of the MFMAs that consume them
+  // (KA fragments ahead for QK, VA for PV), and sched_group_barrier pins that order, so
+  // an MFMA waits for a read issued KA (VA) MFMAs earlier, not for a full LDS round trip.
+  // The look-ahead is what the 256 registers leave: QK also holds the logits (16).
+  constexpr int KA = 1, VA = 2;
   auto compute = [&](const unsigned char* sb, uint32_t kmask, bool first) {
     const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
+    CSA_LDS unsigned char* xb = (CSA_LDS unsigned char*)xbuf;
+    auto ld_k = [&](int k) {
+      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
+    };
     f32x16 s = {};
+    {
+      bf16x8 kb[KA + 1];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
-      if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < KA; ++k) kb[k] = ld_k(k);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k + KA < 16) kb[(k + KA) % (KA + 1)] = ld_k(k + KA);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[k % (KA + 1)], qf[k], s, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, KA, 0);
+#pragma unroll
+      for (int k = 0; k < 16 - KA; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, KA, 0);
     }
     // send the partner's keys (rows 16..31), receive this wave's
 #pragma unroll
-    for (int q = 0; q < 2; ++q) xh[wave][q][lane] = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
+    for (int q = 0; q < 2; ++q)
+      *(CSA_LDS f32x4*)(xb + xo + 4096 * q) = f32x4{s[8 + 4 * q], s[9 + 4 * q], s[10 + 4 * q], s[11 + 4 * q]};
     lds_barrier();
     // logits in unscaled units; the base-2 scale is folded into the exponent's FMA
     float z[8];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const f32x4 o4 = xh[wave ^ 1][q][lane];
+      const f32x4 o4 = *(const CSA_LDS f32x4*)(xb + (xo ^ 1024) + 4096 * q);
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[4 * q + i] = s[4 * q + i] + o4[i];
     }
@@ -644,21 +695,35 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
       pm[e] = (bf16)p;
     }
     l_run += ls;
-    xp[wave][lane] = __builtin_bit_cast(u32x4, pm);
+    *(CSA_LDS u32x4*)(xb + xo + 8192) = __builtin_bit_cast(u32x4, pm);
     lds_barrier();
-    const bf16x8 po = __builtin_bit_cast(bf16x8, xp[wave ^ 1][lane]);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + (ks ? pv_other : pv_mine);
+    const bf16x8 po = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(xb + (xo ^ 1024) + 8192));
+    // O^T += V^T . P^T: MFMA i = 2 db + kh reads V^T of this wave's keys (kh = 0, with
+    // pm) or the partner's (kh = 1, with po), dims block db, with two transposing reads
+    // (keys 16(kh ^ dh) + 4g + j/4 and +8)
+    {
+      auto ld_v = [&](int i) {
+        const int db = i >> 1, kh = i & 1;
+        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + 16 * ROWB * (kh ^ dh);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ks ? po : pm, O[db], 0, 0, 0);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vb[VA + 1];
+#pragma unroll
+      for (int i = 0; i < VA; ++i) vb[i] = ld_v(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + VA < 16) vb[(i + VA) % (VA + 1)] = ld_v(i + VA);
+        O[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % (VA + 1)], (i & 1) ? po : pm, O[i >> 1], 0, 0, 0);
       }
-      // keep the transposing reads at most one block ahead of their MFMAs
-      if (db & 1) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VA, 0);
+#pragma unroll
+      for (int i = 0; i < 16 - VA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, VA, 0);
     }
   };
 
@@ -670,46 +735,46 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     l_run = 0.f;
     if (pass > 0) {
       if (ntiles > 0) km0 = issue(0, load_idx(0), st0);
-      if (ntiles > 1) sv = load_idx(1);
-      __syncthreads();
+      sv = load_idx(1);
+      copies_barrier();
     }
     for (int tile = 0; tile < ntiles; tile += 2) {
       if (tile + 1 < ntiles) km1 = issue(tile + 1, sv, st1);
-      if (tile + 2 < ntiles) sv = load_idx(tile + 2);
+      sv = load_idx(tile + 2);
       compute(st0, km0, pass == 0 && tile == 0);
-      __syncthreads();  // tile+1 landed in st1; every wave is done with st0 and the exchange area
+      copies_barrier();  // tile+1 landed in st1; every wave is done with st0 and the exchange area
       if (tile + 1 < ntiles) {
         if (tile + 2 < ntiles) km0 = issue(tile + 2, sv, st0);
-        if (tile + 3 < ntiles) sv = load_idx(tile + 3);
+        sv = load_idx(tile + 3);
         compute(st1, km1, false);
-        __syncthreads();
+        copies_barrier();
       }
     }
     // the pair's maximum; run again with it as the reference if some probability could
     // have overflowed, or (reference taken as 0 after an all-masked first tile) underflowed
     xm[wave][lane] = m_seen;
     if (threadIdx.x == 0) *ovf = 0;
-    __syncthreads();
+    lds_barrier();
     const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
     const float dev = (mall - m_ref) * a.scale_log2;
     if (__any(mall != -INFINITY && fabsf(dev) > 64.0f) && lane == 0) atomicOr(ovf, 1);
-    __syncthreads();
+    lds_barrier();
     const int again = *ovf;
-    __syncthreads();
+    lds_barrier();
     if (!again) break;
     m_ref = mall;  // exact reference for the second pass
   }
 
   // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced
   xm[wave][lane] = l_run;
-  __syncthreads();
+  lds_barrier();
   l_run = halves_sum(l_run + xm[wave ^ 1][lane]);
-  if (a.sinks && 32 * hg + l32 < a.H)  // the sink joins the denominator, same reference
-    l_run += __builtin_amdgcn_exp2f(sk[32 * hg + l32] * kLog2e - m_ref * a.scale_log2);
+  if (a.sinks && h < a.H)  // the sink joins the denominator, same reference
+    l_run += __builtin_amdgcn_exp2f(sk[h] * kLog2e - m_ref * a.scale_log2);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  __syncthreads();
+  lds_barrier();
   rope_table();
-  __syncthreads();
+  lds_barrier();
   {
     unsigned char* os = hg == 0 ? st0 : st1;
 #pragma unroll
@@ -735,7 +800,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
         *reinterpret_cast<uint2*>(os + off(l32, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
       }
   }
-  __syncthreads();
+  lds_barrier();
   unsigned char* og = reinterpret_cast<unsigned char*>(a.o) + ((int64_t)b * a.S + t) * a.H * ROWB;
   for (int c = threadIdx.x; c < a.H * (ROWB / 16); c += NT) {
     const int row = c >> 6, col = (c & 63) * 16;
