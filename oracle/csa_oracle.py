@@ -45,7 +45,7 @@ import numpy as np
 
 __all__ = [
     "rope_angles", "rope", "gated_pool", "rms_norm", "compress", "visible_entries",
-    "window_bounds", "indexer_scores_row", "indexer_scores", "topk_row", "topk",
+    "window_bounds", "indexer_scores_row", "indexer_scores_block", "indexer_scores", "topk_row", "topk",
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
     "hadamard", "round_to", "index_prologue", "index_temperature", "e4m3", "quant_e4m3_rows",
     "kl_target_row", "kl_target", "attend_row_bwd_dq", "layer_dq_rows",
@@ -150,6 +150,21 @@ def indexer_scores_row(q_i_t, w_t, k_i, n_vis: int) -> np.ndarray:
         return np.zeros(0)
     dots = q_i_t @ k_i[:n_vis].T  # [H_I, n_vis]
     return w_t @ np.maximum(dots, 0.0)
+
+
+def indexer_scores_block(q_i, w, k_i, n_vis) -> list:
+    """indexer_scores_row for a block of queries at once (one matrix product for the
+    block; the same definition, for speed at long sequence lengths).
+    q_i [R, H_I, D_I], w [R, H_I], k_i [n, D_I], n_vis: R visible-entry counts.
+    Returns R rows, row r of length n_vis[r]."""
+    R, HI, DI = q_i.shape
+    nmax = int(max(n_vis)) if R else 0
+    if nmax == 0:
+        return [np.zeros(0) for _ in range(R)]
+    dots = (q_i.reshape(R * HI, DI) @ k_i[:nmax].T).reshape(R, HI, nmax)
+    np.maximum(dots, 0.0, out=dots)  # ReLU (in place: the block can be large)
+    sc = np.matmul(w[:, None, :], dots)[:, 0, :]  # sum_h w[r,h] ReLU(q . k)
+    return [sc[r, : int(n_vis[r])].copy() for r in range(R)]
 
 
 def hadamard(n: int) -> np.ndarray:

@@ -47,7 +47,11 @@ CASES = {
 }
 
 
-def dq_check(bd, cfg, n_rows, with_sink, edit=None, rel=None):
+def dq_check(bd, cfg, n_rows, with_sink, edit=None, rel=None, mutate_sel=None, split_dim0=None):
+    """mutate_sel(idx, sel): edit the selection handed to the kernels ([B,S,K] int32
+    numpy) and return the entries the oracle attends to (dict of rows).  split_dim0:
+    compare dims 1.. at `rel` and dim 0 at this bound (both relative to the largest
+    |dq_ora| over dims 1..)."""
     inp = gen(cfg)
     if edit is not None:
         edit(inp)
@@ -73,6 +77,8 @@ def dq_check(bd, cfg, n_rows, with_sink, edit=None, rel=None):
             idx = np.full((cfg.B, cfg.S, cfg.topk), -1, dtype=np.int32)
             for k in rows:
                 idx[k[0], k[1], :len(sel[k])] = sel[k]
+            if mutate_sel is not None:
+                sel = mutate_sel(idx, sel)
             idx_d = torch.from_numpy(idx).to(DEV)
     o = bd.sparse_mqa_fwd(p, inp["q"], kv, inp["kv_raw"], idx_d, sinks=sinks_d)
     dq = bd.sparse_mqa_bwd_dq(p, inp["q"], kv, inp["kv_raw"], idx_d, o, d_o, sinks=sinks_d)
@@ -82,7 +88,13 @@ def dq_check(bd, cfg, n_rows, with_sink, edit=None, rel=None):
     do_np = {(b, t): d_o[b, t].float().cpu().double().numpy() for (b, t) in rows}
     want = O.layer_dq_rows(cfg, lz, rows, do_np, sel, kv_ora if kv_ora is not None else {}, sinks=sinks64)
     got = np.stack([dq[b, t].float().cpu().double().numpy() for (b, t) in rows])
-    return assert_close_rel(got, np.stack([want[k] for k in rows]), rel or tol(cfg), f"dq {cfg.name}")
+    want = np.stack([want[k] for k in rows])
+    if split_dim0 is not None:
+        scale = float(np.max(np.abs(want[..., 1:])))
+        err0 = float(np.max(np.abs(got[..., 0] - want[..., 0])))
+        assert err0 <= split_dim0 * scale, f"dq dim 0: {err0:.3e} > {split_dim0} * {scale:.3e}"
+        return assert_close_rel(got[..., 1:], want[..., 1:], rel or tol(cfg), f"dq {cfg.name} dims 1..")
+    return assert_close_rel(got, want, rel or tol(cfg), f"dq {cfg.name}")
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -131,3 +143,45 @@ def test_dq_large_logit_range_recomputes_exactly(bd):
         inp["q"][..., 0] = 4.0
         inp["kv_raw"][..., 0] += 100.0
     dq_check(bd, cfg, None, False, edit=edit, rel=1e-3)
+
+
+def test_dq_bf16_second_pass(bd):
+    """The head-group kernel (bf16, D=512, 64 heads) on a logit range that forces the
+    second pass: q[..., 0] = 64 and the window latents' dim 0 raised by 24 lift every
+    window logit by 64 * 24 * 512**-0.5 = 68 (98 log2 units) over the selected
+    entries, which fill the first tile of the rows t >= 127, while the softmax over the
+    window stays spread (a few units of spread from dim 0 and the other dims).  RoPE is
+    off, so keys are exact bf16 values.  Dims 1.. are held to the bf16 bound.  Dim 0
+    is the common component 24 of every window key: dq's dim 0 is 24 times a sum of dz
+    that cancels exactly, and dz is rounded to bf16 (2^-9 relative) before that
+    product, so it is held to 24 * 2^-8 of the largest |dq|."""
+    cfg = wl.C1.replace(S=512, rope_dim=0, name="dq_wide_logits_bf16")
+
+    def edit(inp):
+        inp["q"][..., 0] = 64.0
+        inp["kv_raw"][..., 0] += 24.0
+    dq_check(bd, cfg, None, False, edit=edit, split_dim0=24 * 2.0 ** -8)
+
+
+def test_dq_invalid_selection_entries_are_masked(bd):
+    """Selection entries outside 0..n_t-1 inside the selection (-1, n_t, n_t + 1000,
+    -7) are masked out of the backward as of the forward.  The first 40 entries of every
+    row are made invalid, so the first 32-key tile of each query holds no valid entry
+    (the reference then starts at 0 and the end-of-pass check decides on a second
+    pass), and every seventh row's whole selection is invalid (window keys only)."""
+    cfg = wl.C1.replace(S=1024, name="dq_masked")
+    junk = [-1, None, "far", -7]
+
+    def mutate(idx, sel):
+        out = {}
+        for (b, t), s_ in sel.items():
+            n_t = O.visible_entries(t, cfg.ratio)
+            m = len(s_)
+            k = m if t % 7 == 0 else min(40, m)
+            for j in range(k):
+                v = junk[j % 4]
+                idx[b, t, j] = n_t if v is None else (n_t + 1000 if v == "far" else v)
+            r = idx[b, t, :m]
+            out[(b, t)] = r[(r >= 0) & (r < n_t)].astype(np.int64)
+        return out
+    dq_check(bd, cfg, None, False, mutate_sel=mutate)

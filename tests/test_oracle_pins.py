@@ -168,6 +168,31 @@ def test_indexer_hand_example():
     assert np.allclose(O.indexer_scores_row(q, w, k, 2), want[:2], atol=0)
 
 
+def test_indexer_block_matches_rows(rng):
+    """The block form gives, row by row, the pinned per-row scores (hand example
+    included), for ragged visible counts."""
+    q = np.array([[[1.0, 2.0], [-1.0, 0.5]]])
+    w = np.array([[0.5, 2.0]])
+    k = np.array([[1.0, 1.0], [2.0, -1.0], [-3.0, 1.0]])
+    assert np.array_equal(O.indexer_scores_block(q, w, k, [3])[0], np.array([1.5, 0.0, 7.0]))
+    R, HI, DI, n = 9, 5, 12, 40
+    q, w, k = rng.normal(size=(R, HI, DI)), rng.uniform(size=(R, HI)), rng.normal(size=(n, DI))
+    nv = [0, 1, 7, 40, 13, 0, 39, 2, 40]
+    got = O.indexer_scores_block(q, w, k, nv)
+    for r in range(R):
+        want = O.indexer_scores_row(q[r], w[r], k, nv[r])
+        assert got[r].shape == (nv[r],)
+        assert np.allclose(got[r], want, rtol=1e-13, atol=1e-13)
+    # scalar loops (a third transcription of the definition)
+    r = 3
+    for s_ in range(0, 40, 7):
+        acc = 0.0
+        for h in range(HI):
+            d = sum(q[r, h, j] * k[s_, j] for j in range(DI))
+            acc += w[r, h] * max(d, 0.0)
+        assert abs(got[r][s_] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
 def test_visibility_and_window_layout():
     assert [O.visible_entries(t, 4) for t in range(10)] == [0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
     assert O.visible_entries(127, 128) == 1 and O.visible_entries(126, 128) == 0
@@ -634,6 +659,31 @@ def test_kl_target_is_the_attention_restricted_to_the_selection():
     kt = O.kl_target(cfg, inp, rows, r["sel"], r["kv_c"])
     for k in rows:
         assert np.allclose(kt[k], np.mean(r["P"][k], axis=0), atol=1e-14)
+
+
+def test_kl_target_reading_with_a_window():
+    """With a window the layer's softmax also covers the window keys, and two readings
+    of "the attention over the selected entries" part ways: (A) each head's
+    probabilities restricted to the selection and renormalised per head, then the mean
+    over heads (the same as a softmax over the selected entries alone); (B) the head
+    sum of the restricted probabilities, L1-normalised.  The target is (A): the page's
+    target branch gathers only the selected entries ([B, S, K, head_dim], item 11) and
+    sums heads over softmaxes formed from those gathered logits.  Here the two differ
+    by more than 1e-2, so a target built as (B) fails this pin."""
+    cfg = tiny("csa", S=40, window=6, topk=4, H=4)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in (11, 23, 39)]
+    r = O.layer_rows(cfg, inp, rows, want_p=True)
+    kt = O.kl_target(cfg, inp, rows, r["sel"], r["kv_c"])
+    sep = 0.0
+    for k in rows:
+        m = len(r["sel"][k])
+        ps = r["P"][k][:, :m]  # the selected entries come first in the layer's key list
+        a = np.mean(ps / ps.sum(axis=1, keepdims=True), axis=0)
+        b_ = ps.sum(axis=0) / ps.sum()
+        assert np.allclose(kt[k], a, atol=1e-14)
+        sep = max(sep, float(np.max(np.abs(a - b_))))
+    assert sep > 1e-2, sep
 
 
 def test_kl_target_matches_brute_force():
