@@ -1,4 +1,4 @@
-"""fp64 numpy oracle of the compressed attention layer forward.
+"""fp64 numpy oracle of the compressed attention layer: forward and attention backward.
 
 TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU-baseline
 leg of the benchmark; never by the product path.
@@ -49,6 +49,7 @@ __all__ = [
     "rotate_queries", "rotate_window", "attend_row", "layer_forward", "layer_rows",
     "hadamard", "round_to", "index_prologue", "index_temperature", "e4m3", "quant_e4m3_rows",
     "kl_target_row", "kl_target", "attend_row_bwd_dq", "layer_dq_rows",
+    "attend_row_lse", "attend_row_bwd", "rms_norm_bwd", "layer_bwd_rows",
 ]
 
 
@@ -370,6 +371,114 @@ def layer_dq_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None, s
     return out
 
 
+def attend_row_lse(qr_t, keys, scale: float, sink=None) -> np.ndarray:
+    """Natural log of each head's softmax denominator, the statistic a training forward
+    keeps for its backward: lse[h] = log( sum_k exp(z[h,k]) + exp(sink[h]) ) with
+    z = (qr . key) * scale as in attend_row (the sink term only with a sink).  Then
+    P[h,k] = exp(z[h,k] - lse[h]).  A head with no key and no sink gets -inf."""
+    z = (qr_t @ keys.T) * scale
+    H = qr_t.shape[0]
+    cols = [z]
+    if sink is not None:
+        cols.append(np.asarray(sink, dtype=np.float64).reshape(H, 1))
+    allz = np.concatenate(cols, axis=1)
+    if allz.shape[1] == 0:
+        return np.full(H, -np.inf)
+    m = np.max(allz, axis=1, keepdims=True)
+    return m[:, 0] + np.log(np.sum(np.exp(allz - m), axis=1))
+
+
+def attend_row_bwd(qr_t, keys, scale: float, du, sink=None) -> dict:
+    """Backward of one query's attention with the query, every key and the sink as
+    variables ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with
+    Primus", section "Attention kernels for the three layer types": dQ with delta,
+    and interm, the contraction over heads that gives each key's gradient;
+    "fix(deepseek-v4): correct V4-Flash attention math", Part 1 item 6f: the sink is a
+    logit of the softmax).  K = V, so a key gets a logit term and a value term:
+        dP[h,k] = du[h] . key_k,   delta[h] = sum_k P dP,   dz = P (dP - delta)
+        dqr[h]  = scale sum_k dz[h,k] key_k
+        dkey_k  = scale sum_h dz[h,k] qr[h]  +  sum_h P[h,k] du[h]
+    The sink is a logit with a zero value, so its dP is 0 and its dz is
+        dsink[h] = -Ps[h] delta[h],   Ps[h] = exp(sink[h] - lse[h]).
+    qr_t [H, D] rotated query, keys [nk, D], du [H, D] the gradient of u.  Returns
+    dqr [H, D], dkeys [nk, D], dsink [H] (zeros without a sink), lse [H], delta [H]."""
+    _, P = attend_row(qr_t, keys, scale, sink)
+    dP = du @ keys.T
+    delta = np.sum(P * dP, axis=1)
+    dz = P * (dP - delta[:, None])
+    lse = attend_row_lse(qr_t, keys, scale, sink)
+    if sink is None:
+        dsink = np.zeros(qr_t.shape[0])
+    else:
+        dsink = -np.exp(np.asarray(sink, dtype=np.float64) - lse) * delta
+    return {"dqr": scale * (dz @ keys), "dkeys": scale * (dz.T @ qr_t) + P.T @ du,
+            "dsink": dsink, "lse": lse, "delta": delta}
+
+
+def rms_norm_bwd(x, dy, eps: float) -> np.ndarray:
+    """Gradient through rms_norm: with r = (mean(x^2) + eps)**-0.5 and y = x r,
+    dx = r (dy - y mean(dy * y)) over the last axis."""
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def layer_bwd_rows(cfg, inp: dict, rows, do: dict, sel: dict = None, kv_c=None, sinks=None) -> dict:
+    """Gradients of L = sum over the query rows `rows` of sum(do[(b,t)] * o[b,t]) with
+    the selection held fixed (top-k has no gradient):
+      dq {(b,t): [H,D]}, lse {(b,t): [H]},
+      dkv_c {b: [n, D]}   with respect to the rotated entries the attention reads
+                          (the selected entries of each row gather their key gradient),
+      dkv_raw {b: [S, D]} with respect to the raw window latents: the key gradients of
+                          token t' over every row whose window holds it, rotated back
+                          by -(pos0 + t') (the transpose of its rotation) and, with
+                          norm_window, taken through the RMSNorm,
+      dsinks [H] or None.
+    Keys, selection and window as in layer_rows (`sel` and `kv_c` may come from a
+    layer_rows result)."""
+    R, theta, pos0, eps = cfg.rope_dim, cfg.rope_theta, cfg.pos0, cfg.rms_eps
+    scale = cfg.D ** -0.5 if getattr(cfg, "softmax_scale", None) is None else cfg.softmax_scale
+    norm_window = bool(getattr(cfg, "norm_window", False))
+    if cfg.kind != "swa" and (sel is None or kv_c is None):
+        r = layer_rows(cfg, inp, rows, sel_override=sel)
+        sel = r["sel"] if sel is None else sel
+        kv_c = r["kv_c"] if kv_c is None else kv_c
+    n = cfg.S // cfg.ratio if cfg.kind != "swa" else 0
+    out = {"dq": {}, "lse": {}, "dkv_c": {}, "dkv_raw": {},
+           "dsinks": None if sinks is None else np.zeros(cfg.H)}
+    gwin = {}
+    for b in sorted({b for b, _ in rows}):
+        out["dkv_c"][b] = np.zeros((n, cfg.D))
+        gwin[b] = np.zeros((cfg.S, cfg.D))
+    for (b, t) in rows:
+        lo, hi = window_bounds(t, cfg.window)
+        win = rotate_window(_as64(inp["kv_raw"][b][lo:hi + 1]), R, theta, eps, pos0 + lo, norm_window)
+        if cfg.kind == "swa":
+            s_t = np.zeros(0, dtype=np.int64)
+            ent = np.zeros((0, cfg.D))
+        else:
+            s_t = np.asarray(sel[(b, t)], dtype=np.int64)
+            ent = np.asarray(kv_c[b], dtype=np.float64)[s_t]
+        keys = np.concatenate([ent, win], axis=0)
+        qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
+        du = rope(np.asarray(do[(b, t)], dtype=np.float64), pos0 + t, R, theta)
+        g = attend_row_bwd(qr, keys, scale, du, sinks)
+        out["dq"][(b, t)] = rope(g["dqr"], -(pos0 + t), R, theta)
+        out["lse"][(b, t)] = g["lse"]
+        if len(s_t):
+            np.add.at(out["dkv_c"][b], s_t, g["dkeys"][:len(s_t)])
+        gwin[b][lo:hi + 1] += g["dkeys"][len(s_t):]
+        if sinks is not None:
+            out["dsinks"] += g["dsink"]
+    for b, gw in gwin.items():
+        pos = pos0 + np.arange(cfg.S, dtype=np.int64)
+        d = rope(gw, -pos, R, theta)
+        if norm_window:
+            d = rms_norm_bwd(_as64(inp["kv_raw"][b]), d, eps)
+        out["dkv_raw"][b] = d
+    return out
+
+
 def _as64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
@@ -386,8 +495,8 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
     prologue when both are set.
 
     Returns a dict: o {(b,t): [H,D]}, sel {(b,t): indices}, scores {(b,t): row},
-    n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, and P when
-    want_p.  Steps, per [PR930] Part 1 and [BLOG] "Three attention types":
+    n_visible {(b,t): int}, win {(b,t): (lo, hi)}, kv_c {b: [n, D]}, lse {(b,t): [H]}
+    (attend_row_lse), and P when want_p.  Steps, per [PR930] Part 1 and [BLOG] "Three attention types":
       1 pool + norm + rotate entries at pos0 + s*r   (CSA, HCA)
       2 rotate queries at pos0 + t and window tokens at pos0 + t'
       3 indexer scores over visible entries          (CSA)
@@ -399,7 +508,7 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
     R, theta, eps, pos0 = cfg.rope_dim, cfg.rope_theta, cfg.rms_eps, cfg.pos0
     scale = cfg.D ** -0.5 if getattr(cfg, "softmax_scale", None) is None else cfg.softmax_scale
     norm_window = bool(getattr(cfg, "norm_window", False))
-    out = {"o": {}, "sel": {}, "scores": {}, "n_visible": {}, "win": {}, "kv_c": {}, "P": {}}
+    out = {"o": {}, "sel": {}, "scores": {}, "n_visible": {}, "win": {}, "kv_c": {}, "P": {}, "lse": {}}
     batches = sorted({b for b, _ in rows})
     for b in batches:
         if kind in ("csa", "hca"):
@@ -457,6 +566,7 @@ def layer_rows(cfg, inp: dict, rows, sel_override: dict = None, kv_c=None, want_
             qr = rope(_as64(inp["q"][b, t]), pos0 + t, R, theta)
             u, P = attend_row(qr, keys, scale, sinks)
             out["o"][(b, t)] = rope(u, -(pos0 + t), R, theta)
+            out["lse"][(b, t)] = attend_row_lse(qr, keys, scale, sinks)
             out["sel"][(b, t)] = sel
             out["n_visible"][(b, t)] = n_vis
             out["win"][(b, t)] = (lo, hi)

@@ -752,3 +752,154 @@ def test_dq_closed_forms(rng):
     assert np.allclose(dq, 0, atol=1e-15) and np.allclose(delta, du @ k1[0], atol=1e-15)
     dq2, _ = O.attend_row_bwd_dq(q, np.repeat(k1, 4, axis=0), 0.5, du)
     assert np.allclose(dq2, 0, atol=1e-14)
+
+
+# ----------------------------------------------------- key-side backward -----------
+# "Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
+# "Attention kernels for the three layer types": interm, the contraction over heads
+# that gives each key's gradient; "fix(deepseek-v4): correct V4-Flash attention
+# math", Part 1 item 6f: the sink is an fp32 logit of the softmax.
+
+def _loss(cfg, inp, rows, sel, kv_c, do, sinks):
+    r = O.layer_rows(cfg, inp, rows, sel_override=sel, kv_c=kv_c, sinks=sinks)
+    return sum(float(np.sum(r["o"][k] * do[k])) for k in rows)
+
+
+@pytest.mark.parametrize("kind,with_sink,norm_window", [
+    ("csa", False, False), ("csa", True, False), ("hca", True, False), ("swa", False, True),
+    ("csa", True, True)])
+def test_key_grads_match_finite_differences(kind, with_sink, norm_window, rng):
+    """Central differences of L = sum over every row of sum(o * do), through the
+    forward oracle, in sampled coordinates of the rotated entries kv_c, of the raw
+    window latents kv_raw (each feeds the windows of up to W queries) and in every
+    sink.  The selection is held fixed, as the backward holds it."""
+    cfg = tiny(kind, S=24, pos0=5, H=2, D=8, rope_dim=4, window=5, norm_window=norm_window)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(cfg.S)]
+    base = O.layer_rows(cfg, inp, rows)
+    sel, kv_c = base["sel"], base["kv_c"]
+    do = {k: rng.normal(size=(cfg.H, cfg.D)) for k in rows}
+    sinks = rng.normal(size=cfg.H) if with_sink else None
+    g = O.layer_bwd_rows(cfg, inp, rows, do, sel, kv_c, sinks=sinks)
+    eps = 1e-6
+
+    def fd(edit):
+        return (_loss(*edit(+eps)) - _loss(*edit(-eps))) / (2 * eps)
+
+    if kind != "swa":
+        n = kv_c[0].shape[0]
+        for _ in range(12):
+            s, d = int(rng.integers(0, n)), int(rng.integers(0, cfg.D))
+
+            def edit(e, s=s, d=d):
+                kv = {0: kv_c[0].copy()}
+                kv[0][s, d] += e
+                return cfg, inp, rows, sel, kv, do, sinks
+            assert abs(fd(edit) - g["dkv_c"][0][s, d]) < 1e-7, (s, d)
+    for _ in range(12):
+        t, d = int(rng.integers(0, cfg.S)), int(rng.integers(0, cfg.D))
+
+        def edit(e, t=t, d=d):
+            kr = inp["kv_raw"].copy()
+            kr[0, t, d] += e
+            return cfg, dict(inp, kv_raw=kr), rows, sel, kv_c, do, sinks
+        assert abs(fd(edit) - g["dkv_raw"][0][t, d]) < 1e-7, (t, d)
+    if with_sink:
+        for h in range(cfg.H):
+            def edit(e, h=h):
+                sk = sinks.copy()
+                sk[h] += e
+                return cfg, inp, rows, sel, kv_c, do, sk
+            assert abs(fd(edit) - g["dsinks"][h]) < 1e-7, h
+    # the query side agrees with the dQ oracle
+    dq = O.layer_dq_rows(cfg, inp, rows, do, sel, kv_c, sinks=sinks)
+    for k in rows:
+        assert np.allclose(g["dq"][k], dq[k], atol=1e-12)
+
+
+def _torch_rope(x, pos, R, theta):
+    """Interleaved RoPE on the last R dims, written with torch ops (pairs 2i, 2i+1)."""
+    if R == 0:
+        return x
+    D = x.shape[-1]
+    i = torch.arange(R // 2, dtype=torch.float64)
+    ang = torch.as_tensor(pos, dtype=torch.float64)[..., None] * theta ** (-2.0 * i / R)
+    c, s = torch.cos(ang), torch.sin(ang)
+    x0, x1 = x[..., D - R::2], x[..., D - R + 1::2]
+    rot = torch.stack([x0 * c - x1 * s, x0 * s + x1 * c], dim=-1).reshape(*x.shape[:-1], R)
+    return torch.cat([x[..., :D - R], rot], dim=-1)
+
+
+@pytest.mark.parametrize("norm_window", [False, True])
+def test_layer_grads_match_torch_autograd(norm_window, rng):
+    """torch autograd through the layer's attention written with torch ops in fp64
+    (RoPE of queries and window tokens, optional window RMSNorm, entries gathered by the
+    fixed selection, one softmax with a sink, de-rotation), for every input the
+    backward differentiates: q, kv_c, kv_raw and the sinks."""
+    cfg = tiny("csa", S=28, pos0=11, H=3, D=8, rope_dim=4, window=6, topk=3, norm_window=norm_window)
+    inp = to_np(wl.make_inputs(cfg))
+    rows = [(0, t) for t in range(cfg.S)]
+    base = O.layer_rows(cfg, inp, rows)
+    sel, kv_c = base["sel"], base["kv_c"]
+    do = {k: rng.normal(size=(cfg.H, cfg.D)) for k in rows}
+    sinks = rng.normal(size=cfg.H)
+    g = O.layer_bwd_rows(cfg, inp, rows, do, sel, kv_c, sinks=sinks)
+
+    q = torch.tensor(inp["q"][0], requires_grad=True)
+    kc = torch.tensor(kv_c[0], requires_grad=True)
+    kr = torch.tensor(inp["kv_raw"][0], requires_grad=True)
+    sk = torch.tensor(sinks, requires_grad=True)
+    R, th, scale = cfg.rope_dim, cfg.rope_theta, cfg.D ** -0.5
+    loss = torch.zeros((), dtype=torch.float64)
+    for (_, t) in rows:
+        lo = max(0, t - cfg.window + 1)
+        w = kr[lo:t + 1]
+        if norm_window:
+            w = w / torch.sqrt((w * w).mean(-1, keepdim=True) + cfg.rms_eps)
+        w = _torch_rope(w, cfg.pos0 + torch.arange(lo, t + 1), R, th)
+        keys = torch.cat([kc[torch.as_tensor(sel[(0, t)], dtype=torch.long)], w], 0)
+        qr = _torch_rope(q[t], torch.full((cfg.H,), cfg.pos0 + t), R, th)
+        z = torch.cat([(qr @ keys.T) * scale, sk[:, None]], 1)
+        p = torch.softmax(z, dim=1)[:, :-1]
+        o = _torch_rope(p @ keys, torch.full((cfg.H,), -(cfg.pos0 + t)), R, th)
+        loss = loss + (o * torch.tensor(do[(0, t)])).sum()
+    loss.backward()
+    assert np.allclose(np.stack([g["dq"][k] for k in rows]), q.grad.numpy(), atol=1e-11)
+    assert np.allclose(g["dkv_c"][0], kc.grad.numpy(), atol=1e-11)
+    assert np.allclose(g["dkv_raw"][0], kr.grad.numpy(), atol=1e-11)
+    assert np.allclose(g["dsinks"], sk.grad.numpy(), atol=1e-11)
+
+
+def test_key_grads_closed_forms(rng):
+    """Without a sink, moving every key by one vector c moves u by c and leaves the
+    softmax unchanged, so sum_k dkey_k = sum_h du[h]; with one key and a sink,
+    L = Pk (du . key) and dL/dsink = -Pk Ps (du . key); the lse of all-zero keys is
+    log(nk), or log(nk + e^s) with a sink."""
+    H, D, nk, scale = 3, 6, 7, 0.4
+    qr, keys, du = rng.normal(size=(H, D)), rng.normal(size=(nk, D)), rng.normal(size=(H, D))
+    g = O.attend_row_bwd(qr, keys, scale, du)
+    assert np.allclose(g["dkeys"].sum(0), du.sum(0), atol=1e-13)
+    assert np.allclose(g["dsink"], 0.0)
+    key = rng.normal(size=(1, D))
+    s = rng.normal(size=H)
+    g1 = O.attend_row_bwd(qr, key, scale, du, sink=s)
+    z = (qr @ key[0]) * scale
+    pk, ps = np.exp(z) / (np.exp(z) + np.exp(s)), np.exp(s) / (np.exp(z) + np.exp(s))
+    assert np.allclose(g1["dsink"], -pk * ps * (du @ key[0]), atol=1e-14)
+    assert np.allclose(O.attend_row_lse(qr, np.zeros((nk, D)), scale), np.log(nk), atol=1e-14)
+    assert np.allclose(O.attend_row_lse(qr, np.zeros((nk, D)), scale, s), np.log(nk + np.exp(s)), atol=1e-14)
+    assert np.all(O.attend_row_lse(qr, np.zeros((0, D)), scale) == -np.inf)
+
+
+def test_lse_reproduces_the_forward_probabilities(rng):
+    """exp(z - lse) is the forward's softmax (attend_row's P) and, with a sink, the
+    keys' probabilities sum to 1 - exp(sink - lse)."""
+    H, D, nk, scale = 4, 8, 9, 0.3
+    qr, keys = rng.normal(size=(H, D)), rng.normal(size=(nk, D)) * 3
+    s = rng.normal(size=H)
+    for sink in (None, s):
+        _, P = O.attend_row(qr, keys, scale, sink)
+        lse = O.attend_row_lse(qr, keys, scale, sink)
+        assert np.allclose(np.exp((qr @ keys.T) * scale - lse[:, None]), P, atol=1e-14)
+        rest = 0.0 if sink is None else np.exp(sink - lse)
+        assert np.allclose(P.sum(1) + rest, 1.0, atol=1e-14)
