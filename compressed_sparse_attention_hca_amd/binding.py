@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_WORKSPACE, CSA_ERR_UNSUPPORTED, CSA_ERR_HIP = range(5)
 CSA_F32, CSA_BF16 = 0, 1
-OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_CSA_FWD, OP_HCA_FWD = range(5)
+OP_COMPRESS, OP_INDEX_TOPK, OP_SPARSE_MQA, OP_CSA_FWD, OP_HCA_FWD, OP_SPARSE_MQA_BWD = range(6)
 FLAG_NORM_WINDOW = 1
 FLAG_INDEX_PROLOGUE = 2
 FLAG_INDEX_FP8 = 4
@@ -63,7 +63,9 @@ def _load():
         "csa_kl_target": [P, V, V, V, V, V],
         "csa_sparse_mqa_fwd": [P, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_fwd_sink": [P, V, V, V, V, V, V, V, SZ, V],
+        "csa_sparse_mqa_fwd_lse": [P, V, V, V, V, V, V, V, V, SZ, V],
         "csa_sparse_mqa_bwd_dq": [P, V, V, V, V, V, V, V, V, V, SZ, V],
+        "csa_sparse_mqa_bwd_dkv": [P, V, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
         "csa_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
         "csa_fwd_noalloc": [P, ctypes.POINTER(Inputs), V, V],
         "hca_fwd": [P, ctypes.POINTER(Inputs), V, V, SZ, V],
@@ -94,7 +96,8 @@ lib = _load()
 
 EXPORTS = ("csa_compress", "csa_index_scores", "csa_index_topk", "csa_index_keys",
            "csa_sparse_mqa_fwd",
-           "csa_sparse_mqa_fwd_sink", "csa_sparse_mqa_bwd_dq", "csa_kl_target", "csa_fwd",
+           "csa_sparse_mqa_fwd_sink", "csa_sparse_mqa_fwd_lse", "csa_sparse_mqa_bwd_dq",
+           "csa_sparse_mqa_bwd_dkv", "csa_kl_target", "csa_fwd",
            "csa_fwd_noalloc",
            "hca_fwd", "csa_fwd_traced", "hca_fwd_traced", "csa_trace_events",
            "csa_workspace_bytes", "csa_debug_layout", "csa_status_str", "csa_last_error",
@@ -303,6 +306,50 @@ def sparse_mqa_bwd_dq(p: Params, q, kv_c, kv_raw, idx, o, d_o, dq=None, ws=None,
                                     _ptr(sinks), _ptr(o), _ptr(d_o), _ptr(dq), _ptr(ws), ws.numel(),
                                     _stream(stream)))
     return dq
+
+
+def sparse_mqa_fwd_lse(p: Params, q, kv_c, kv_raw, idx=None, sinks=None, o=None, lse=None, ws=None,
+                       stream=None):
+    """csa_sparse_mqa_fwd_lse: the forward's output o and lse [B,S,H] fp32, the natural
+    log of each head's softmax denominator (what the backward reads)."""
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((p.B, p.S, p.H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(p, OP_SPARSE_MQA, q.device)
+    _chk_attn(p, q, kv_c, kv_raw, idx, sinks, o=o)
+    _chk(lse, "lse", (p.B, p.S, p.H), torch.float32)
+    _chk_ws(ws)
+    check(lib.csa_sparse_mqa_fwd_lse(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx),
+                                     _ptr(sinks), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return o, lse
+
+
+def sparse_mqa_bwd_dkv(p: Params, q, kv_c, kv_raw, idx, o, lse, d_o, sinks=None, dkv_c=None, dkv_raw=None,
+                       dsinks=None, ws=None, stream=None):
+    """csa_sparse_mqa_bwd_dkv: dL/dkv_c [B,S/ratio,D] (None without kv_c), dL/dkv_raw
+    [B,S,D] and dL/dsinks [H] (None without sinks), all fp32, for sparse_mqa_fwd_lse
+    with the same arguments, given its o and lse and dL/do."""
+    dev = q.device
+    if dkv_c is None and kv_c is not None:
+        dkv_c = torch.empty((p.B, p.S // p.ratio, p.D), dtype=torch.float32, device=dev)
+    if dkv_raw is None:
+        dkv_raw = torch.empty((p.B, p.S, p.D), dtype=torch.float32, device=dev)
+    if dsinks is None and sinks is not None:
+        dsinks = torch.empty((p.H,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(p, OP_SPARSE_MQA_BWD, dev)
+    _chk_attn(p, q, kv_c, kv_raw, idx, sinks, o=o, d_o=d_o)
+    _chk(lse, "lse", (p.B, p.S, p.H), torch.float32)
+    _chk(dkv_c, "dkv_c", (p.B, p.S // p.ratio, p.D), torch.float32, required=kv_c is not None)
+    _chk(dkv_raw, "dkv_raw", (p.B, p.S, p.D), torch.float32)
+    _chk(dsinks, "dsinks", (p.H,), torch.float32, required=sinks is not None)
+    _chk_ws(ws)
+    check(lib.csa_sparse_mqa_bwd_dkv(ctypes.byref(p), _ptr(q), _ptr(kv_c), _ptr(kv_raw), _ptr(idx), _ptr(sinks),
+                                     _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dkv_c), _ptr(dkv_raw), _ptr(dsinks),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+    return dkv_c, dkv_raw, dsinks
 
 
 def kl_target(p: Params, q, kv_c, idx, target=None, stream=None) -> torch.Tensor:

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
 SOURCES = ["abi.cpp", "validate.cpp", "compress.hip", "indexer.hip", "topk.hip", "sparse_mqa.hip",
-           "kl_target.hip", "mqa_bwd.hip", "noalloc.hip"]
+           "kl_target.hip", "mqa_bwd.hip", "mqa_bwd_dkv.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -5,6 +5,7 @@
 #include "csa.h"
 #include "launch.hpp"
 #include "mqa_bwd.hpp"
+#include "mqa_bwd_dkv.hpp"
 #include "validate.hpp"
 
 using namespace csa;
@@ -152,11 +153,12 @@ size_t csa_workspace_bytes(const csa_params_t* p, int32_t op) {
     case CSA_OP_SPARSE_MQA: need = uint32_t(Need::MQA); break;
     case CSA_OP_CSA_FWD: need = Need::COMPRESS | Need::INDEX | Need::MQA; break;
     case CSA_OP_HCA_FWD: need = Need::COMPRESS | Need::MQA; break;
+    case CSA_OP_SPARSE_MQA_BWD: need = uint32_t(Need::MQA); break;
     default: set_error("unknown op %d", op); return 0;
   }
   // the attention workspace (rotated window latents) does not depend on the entries,
   // so it is sized for the window-only case too
-  if (validate_params(p, need, op == CSA_OP_SPARSE_MQA) != CSA_OK) return 0;
+  if (validate_params(p, need, op == CSA_OP_SPARSE_MQA || op == CSA_OP_SPARSE_MQA_BWD) != CSA_OK) return 0;
   return plan_workspace(*p, op).total;
 }
 
@@ -221,6 +223,11 @@ csa_status_t csa_index_topk(const csa_params_t* p, const void* q_idx, const floa
                         plan, as_stream(stream));
 }
 
+static csa_status_t sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
+                                   const void* kv_raw, const int32_t* idx, const float* sinks,
+                                   void* o, float* lse, bool want_lse, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
                                 const void* kv_raw, const int32_t* idx, void* o, void* ws,
                                 size_t ws_bytes, void* stream) {
@@ -230,6 +237,19 @@ csa_status_t csa_sparse_mqa_fwd(const csa_params_t* p, const void* q, const void
 csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const void* kv_c,
                                      const void* kv_raw, const int32_t* idx, const float* sinks,
                                      void* o, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_mqa_fwd(p, q, kv_c, kv_raw, idx, sinks, o, nullptr, false, ws, ws_bytes, stream);
+}
+
+csa_status_t csa_sparse_mqa_fwd_lse(const csa_params_t* p, const void* q, const void* kv_c,
+                                    const void* kv_raw, const int32_t* idx, const float* sinks,
+                                    void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_mqa_fwd(p, q, kv_c, kv_raw, idx, sinks, o, lse, true, ws, ws_bytes, stream);
+}
+
+static csa_status_t sparse_mqa_fwd(const csa_params_t* p, const void* q, const void* kv_c,
+                                   const void* kv_raw, const int32_t* idx, const float* sinks,
+                                   void* o, float* lse, bool want_lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
   const bool window_only = kv_c == nullptr;
   CSA_TRY(validate_params(p, uint32_t(Need::MQA) | (idx ? uint32_t(Need::SELECT) : 0u), window_only));
   if (window_only && idx) {
@@ -240,6 +260,7 @@ csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const
   CSA_TRY(check_ptr(q, "q"));
   CSA_TRY(check_ptr(kv_raw, "kv_raw"));
   CSA_TRY(check_ptr(o, "o"));
+  if (want_lse) CSA_TRY(check_ptr(lse, "lse"));
   CSA_TRY(check_optional(kv_c, "kv_c"));
   CSA_TRY(check_optional(idx, "idx"));
   CSA_TRY(check_optional(sinks, "sinks"));
@@ -250,7 +271,7 @@ csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const
   void* kv_w = w + plan.kv_w;
   CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
   const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
-  CSA_HIP(launch_sparse_mqa(*p, mode, q, kv_c, kv_w, idx, sinks, o, st), "attention launch");
+  CSA_HIP(launch_sparse_mqa(*p, mode, q, kv_c, kv_w, idx, sinks, o, lse, st), "attention launch");
   return CSA_OK;
 }
 
@@ -281,6 +302,67 @@ csa_status_t csa_sparse_mqa_bwd_dq(const csa_params_t* p, const void* q, const v
   CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
   const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
   CSA_HIP(launch_mqa_bwd_dq(*p, mode, q, kv_c, kv_w, idx, sinks, o, d_o, dq, st), "dq launch");
+  return CSA_OK;
+}
+
+csa_status_t csa_sparse_mqa_bwd_dkv(const csa_params_t* p, const void* q, const void* kv_c,
+                                    const void* kv_raw, const int32_t* idx, const float* sinks,
+                                    const void* o, const float* lse, const void* d_o, float* dkv_c,
+                                    float* dkv_raw, float* dsinks, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const bool window_only = kv_c == nullptr;
+  CSA_TRY(validate_params(p, uint32_t(Need::MQA) | (idx ? uint32_t(Need::SELECT) : 0u), window_only));
+  if (window_only && idx) {
+    set_error("idx given without kv_c");
+    return CSA_ERR_INVALID_ARG;
+  }
+  if (p->dtype == CSA_F32 && p->D > 256) {
+    set_error("the key-side backward holds fp32 operands for D <= 256, not D=%d", p->D);
+    return CSA_ERR_UNSUPPORTED;
+  }
+  if (!dkv_c != window_only) {
+    set_error(window_only ? "dkv_c given without kv_c" : "dkv_c is NULL");
+    return CSA_ERR_INVALID_ARG;
+  }
+  if (!dsinks != !sinks) {
+    set_error(sinks ? "dsinks is NULL" : "dsinks given without sinks");
+    return CSA_ERR_INVALID_ARG;
+  }
+  if (dsinks) CSA_TRY(check_ptr(dsinks, "dsinks"));
+  const hipStream_t st = as_stream(stream);
+  if (empty(p)) {  // nothing contributes: the sink gradient is zero
+    if (dsinks) CSA_HIP(launch_zero_f32(dsinks, (size_t)p->H, st), "zero launch");
+    return CSA_OK;
+  }
+  CSA_TRY(check_ptr(q, "q"));
+  CSA_TRY(check_ptr(kv_raw, "kv_raw"));
+  CSA_TRY(check_ptr(o, "o"));
+  CSA_TRY(check_ptr(lse, "lse"));
+  CSA_TRY(check_ptr(d_o, "d_o"));
+  CSA_TRY(check_ptr(dkv_raw, "dkv_raw"));
+  CSA_TRY(check_optional(kv_c, "kv_c"));
+  CSA_TRY(check_optional(dkv_c, "dkv_c"));
+  CSA_TRY(check_optional(idx, "idx"));
+  CSA_TRY(check_optional(sinks, "sinks"));
+  WsPlan plan;
+  CSA_TRY(check_ws(p, CSA_OP_SPARSE_MQA_BWD, ws, ws_bytes, &plan));
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  void* kv_w = w + plan.kv_w;
+  CSA_HIP(launch_window_rope(*p, kv_raw, kv_w, st), "window rope launch");
+  DkvWs dw;
+  dw.interm = w + plan.interm;
+  dw.ds_row = reinterpret_cast<float*>(w + plan.ds_row);
+  dw.sink_part = reinterpret_cast<float*>(w + plan.sink_part);
+  dw.cnt = reinterpret_cast<int32_t*>(w + plan.cnt);
+  dw.tot = reinterpret_cast<int32_t*>(w + plan.tot);
+  dw.base = reinterpret_cast<int32_t*>(w + plan.base);
+  dw.segbase = reinterpret_cast<int32_t*>(w + plan.segbase);
+  dw.list = reinterpret_cast<int32_t*>(w + plan.list);
+  dw.partial = reinterpret_cast<float*>(w + plan.partial);
+  const MqaMode mode = window_only ? MQA_WINDOW_ONLY : (idx ? MQA_SELECTED : MQA_DENSE);
+  CSA_HIP(launch_mqa_bwd_dkv(*p, mode, q, kv_c, kv_w, kv_raw, idx, sinks, o, lse, d_o, dkv_c, dkv_raw,
+                             dsinks, dw, st),
+          "key-side backward launch");
   return CSA_OK;
 }
 
@@ -342,7 +424,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
     int32_t* nvis = in->n_visible_out ? in->n_visible_out : reinterpret_cast<int32_t*>(w + plan.nvis);
     CSA_TRY(run_index_topk(p, in->q_idx, in->w_idx, in->k_idx, idx, nvis, w, plan, st, tr));
   }
-  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, in->sinks, o, st),
+  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, in->sinks, o, nullptr, st),
           "attention launch");
   CSA_HIP(tr->mark(CSA_KERNEL_ATTENTION, st), "event record");
   return CSA_OK;

@@ -30,10 +30,11 @@ hipError_t launch_index_topk(const csa_params_t& p, const void* q_idx, const flo
 hipError_t launch_topk(const csa_params_t& p, const float* scores, int64_t ld, int32_t t0,
                        int32_t nrows, int32_t* idx, int32_t* n_visible, hipStream_t st);
 
-// sinks [H] fp32 or nullptr: per-head softmax-sink logits.
+// sinks [H] fp32 or nullptr: per-head softmax-sink logits.  lse [B,S,H] fp32 or
+// nullptr: the natural log of each head's softmax denominator (sink included).
 hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
                              const void* kv_w, const int32_t* idx, const float* sinks, void* o,
-                             hipStream_t st);
+                             float* lse, hipStream_t st);
 
 // Target of the indexer's distillation loss over the selected entries ([B,S,topk] fp32).
 hipError_t launch_kl_target(const csa_params_t& p, const void* q, const void* kv_c, const int32_t* idx,

@@ -40,6 +40,7 @@ struct MqaArgs {
   const int32_t* idx;
   const float* sinks;  // [H] softmax-sink logits, or nullptr
   void* o;
+  float* lse;          // [B,S,H] log of each head's softmax denominator, or nullptr
   int32_t B, S, H, R, ratio, window, topk, n_entries, mode;
   float scale_log2;  // softmax_scale * log2(e)
   double theta;
@@ -51,6 +52,17 @@ __device__ __host__ constexpr int slot_key(int g, int i) { return i < 4 ? 4 * g 
 
 constexpr int MQA_MAX_TOPK = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Natural log of a head's softmax denominator, the statistic a training forward keeps
+// for its backward: ln(2^m2 * l + e^sink), from the keys' mass l against the log2
+// reference m2 and the sink logit (if any).  No key and no sink: -inf.
+__device__ inline float head_lse(float m2, float l, const float* sinks, int h) {
+  const float a2 = l > 0.f ? m2 + log2f(l) : -INFINITY;
+  const float b2 = sinks ? sinks[h] * kLog2e : -INFINITY;
+  const float hi = fmaxf(a2, b2), lo = fminf(a2, b2);
+  const float r = lo == -INFINITY ? hi : hi + log2f(1.0f + exp2f(lo - hi));
+  return r * 0.69314718055994531f;
+}
 
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
@@ -343,6 +355,11 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
   // ---- normalise, de-rotate at -P, stage through LDS, write o[b,t] coalesced
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  if (a.lse && g == 0) {
+    const int h = 16 * wave + hl;
+    if (h < a.H)
+      a.lse[((int64_t)b * a.S + t) * a.H + h] = head_lse(m_ref == -INFINITY ? 0.f : m_ref, l_run, a.sinks, h);
+  }
   if (a.sinks) {  // the sink joins the denominator against the same reference
     const int h = 16 * wave + hl;
     if (h < a.H) l_run += __builtin_amdgcn_exp2f(a.sinks[h] * kLog2e - m_ref);
@@ -769,6 +786,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   xm[wave][lane] = l_run;
   lds_barrier();
   l_run = halves_sum(l_run + xm[wave ^ 1][lane]);
+  if (a.lse && dh == 0 && g == 0 && h < a.H)
+    a.lse[((int64_t)b * a.S + t) * a.H + h] = head_lse(m_ref * a.scale_log2, l_run, a.sinks, h);
   if (a.sinks && h < a.H)  // the sink joins the denominator, same reference
     l_run += __builtin_amdgcn_exp2f(sk[h] * kLog2e - m_ref * a.scale_log2);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
@@ -836,7 +855,7 @@ static hipError_t launch_t(const MqaArgs& a, int D, int H, hipStream_t st) {
 
 hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
                              const void* kv_w, const int32_t* idx, const float* sinks, void* o,
-                             hipStream_t st) {
+                             float* lse, hipStream_t st) {
   MqaArgs a{};
   a.q = q;
   a.kv_c = kv_c;
@@ -844,6 +863,7 @@ hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q,
   a.idx = idx;
   a.sinks = sinks;
   a.o = o;
+  a.lse = lse;
   a.B = p.B;
   a.S = p.S;
   a.H = p.H;

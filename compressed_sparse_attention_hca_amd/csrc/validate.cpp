@@ -100,6 +100,31 @@ csa_status_t validate_params(const csa_params_t* p, uint32_t need, bool window_o
   return CSA_OK;
 }
 
+DkvShape dkv_shape(const csa_params_t& p, int mode) {
+  DkvShape s;
+  const int64_t B = p.B > 0 ? p.B : 0, S = p.S > 0 ? p.S : 0, all = B * S;
+  const int64_t n = (mode != 2 && p.ratio >= 1) ? S / p.ratio : 0;
+  s.kmax = mode == 0 ? p.topk : (mode == 1 ? (int32_t)n : 0);
+  s.kw = s.kmax + (p.window > 0 ? p.window : 0);
+  const size_t row_bytes = (size_t)s.kw * (size_t)(p.D > 0 ? p.D : 0) * elem_size(p);
+  int64_t rows = all < kDkvMaxChunkRows ? all : kDkvMaxChunkRows;
+  if (row_bytes) {
+    const int64_t fit = (int64_t)(kDkvIntermBudget / row_bytes);
+    if (rows > (fit > 0 ? fit : 1)) rows = fit > 0 ? fit : 1;
+  }
+  if (rows < all && rows >= kDkvRowBlock) rows -= rows % kDkvRowBlock;
+  s.rows = rows;
+  s.nblk = (rows + kDkvRowBlock - 1) / kDkvRowBlock;
+  if (s.kmax > 0 && S > 0) {
+    int64_t spans = (rows + S - 1) / S + 1;  // sequences a chunk can touch
+    if (spans > B) spans = B;
+    s.nkeys = spans * n;
+  }
+  s.pairs = rows * s.kmax;
+  s.segs = s.pairs / kDkvSeg + s.nkeys + 1;
+  return s;
+}
+
 WsPlan plan_workspace(const csa_params_t& p, int32_t op) {
   WsPlan w;
   const size_t es = elem_size(p);
@@ -113,8 +138,34 @@ WsPlan plan_workspace(const csa_params_t& p, int32_t op) {
   };
   const bool idx = op == CSA_OP_INDEX_TOPK || op == CSA_OP_CSA_FWD;
   if (op == CSA_OP_CSA_FWD || op == CSA_OP_HCA_FWD) w.kv_c = take(B * n * (size_t)p.D * es);
-  if (op == CSA_OP_SPARSE_MQA || op == CSA_OP_CSA_FWD || op == CSA_OP_HCA_FWD)
+  if (op == CSA_OP_SPARSE_MQA || op == CSA_OP_CSA_FWD || op == CSA_OP_HCA_FWD || op == CSA_OP_SPARSE_MQA_BWD)
     w.kv_w = take(B * S * (size_t)p.D * es);
+  if (op == CSA_OP_SPARSE_MQA_BWD) {  // sized for every mode these params allow
+    size_t interm = 0, nblk = 0, nkeys = 0, pairs = 0, segs = 0;
+    const bool entries = p.ratio >= 1 && S % (size_t)p.ratio == 0;
+    for (int mode = 0; mode < 3; ++mode) {
+      if (mode == 0 && !(entries && p.topk >= 1 && p.topk <= kMaxTopk)) continue;
+      if (mode == 1 && !entries) continue;
+      const DkvShape d = dkv_shape(p, mode);
+      const size_t ib = (size_t)d.rows * (size_t)d.kw * (size_t)p.D * es;
+      interm = ib > interm ? ib : interm;
+      if (d.kmax > 0) {
+        nblk = (size_t)d.nblk > nblk ? (size_t)d.nblk : nblk;
+        nkeys = (size_t)d.nkeys > nkeys ? (size_t)d.nkeys : nkeys;
+        pairs = (size_t)d.pairs > pairs ? (size_t)d.pairs : pairs;
+        segs = (size_t)d.segs > segs ? (size_t)d.segs : segs;
+      }
+    }
+    w.interm = take(interm);
+    w.ds_row = take(B * S * (size_t)p.H * 4);
+    w.sink_part = take((size_t)kDkvSinkGroups * (size_t)p.H * 4);
+    w.cnt = take(nblk * nkeys * 4);
+    w.tot = take(nkeys * 4);
+    w.base = take((nkeys + 1) * 4);
+    w.segbase = take((nkeys + 1) * 4);
+    w.list = take(pairs * 4);
+    w.partial = take(segs * (size_t)p.D * 4);
+  }
   if (op == CSA_OP_CSA_FWD) {
     w.idx = take(B * S * (size_t)p.topk * 4);
     w.nvis = take(B * S * 4);

@@ -37,9 +37,27 @@ csa_status_t check_ptr(const void* ptr, const char* name);
 size_t elem_size(const csa_params_t& p);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Key-side attention backward: the query rows are taken in chunks whose per-pair
+// intermediate ([rows, kw, D] in the activation type) stays within a budget.
+constexpr int32_t kDkvRowBlock = 64;           // rows per counting block
+constexpr int32_t kDkvSeg = 256;               // pairs per summed segment
+constexpr int64_t kDkvMaxChunkRows = 8192;     // rows per chunk at most
+constexpr size_t kDkvIntermBudget = size_t(4) << 30;
+constexpr int32_t kDkvSinkGroups = 256;        // partial sums of the sink gradient
+// mode: 0 selected entries (idx), 1 every visible entry, 2 window only.
+struct DkvShape {
+  int32_t kmax = 0, kw = 0;  // entry slots, all slots per row
+  int64_t rows = 0;          // rows per chunk
+  int64_t nblk = 0, nkeys = 0, pairs = 0, segs = 0;  // per-chunk bounds
+};
+DkvShape dkv_shape(const csa_params_t& p, int mode);
+
 // Workspace layout of each op.
 struct WsPlan {
   size_t kv_c = 0, kv_w = 0, idx = 0, nvis = 0, scores = 0, k_rot = 0;  // offsets
+  // key-side backward (CSA_OP_SPARSE_MQA_BWD)
+  size_t interm = 0, ds_row = 0, sink_part = 0, cnt = 0, tot = 0, base = 0, segbase = 0, list = 0,
+         partial = 0;
   size_t total = 0;
   int64_t ld = 0;         // scores row stride (floats)
   int32_t chunk_rows = 0; // query rows per indexer/top-k chunk (0: fused, no scores)

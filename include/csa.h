@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 7
+#define CSA_ABI_VERSION 8
 
 typedef enum {
   CSA_OK = 0,
@@ -70,7 +70,8 @@ typedef enum {
   CSA_OP_INDEX_TOPK = 1,
   CSA_OP_SPARSE_MQA = 2,
   CSA_OP_CSA_FWD = 3,
-  CSA_OP_HCA_FWD = 4
+  CSA_OP_HCA_FWD = 4,
+  CSA_OP_SPARSE_MQA_BWD = 5 /* csa_sparse_mqa_bwd_dkv */
 } csa_op_t;
 
 /* flags */
@@ -207,6 +208,20 @@ csa_status_t csa_sparse_mqa_fwd_sink(const csa_params_t* p, const void* q, const
                                      const void* kv_raw, const int32_t* idx, const float* sinks,
                                      void* o, void* ws, size_t ws_bytes, void* stream);
 
+/* Stage 4 as csa_sparse_mqa_fwd_sink, also keeping what its backward needs
+ * ("Enabling DeepSeek-V4-Flash Training on AMD Instinct MI355X GPUs with Primus",
+ * section "Attention kernels for the three layer types": the backward kernels recompute
+ * the softmax of the forward):
+ *   lse [B,S,H] fp32 output: lse[b,t,h] = log( sum_k exp(z[h,k]) + exp(sinks[h]) ), the
+ *   natural log of head h's softmax denominator over the logits z = (RoPE(q, pos0+t) .
+ *   key) * softmax_scale the forward forms (the sink term only with sinks), so that
+ *   p[h,k] = exp(z[h,k] - lse[h]); -inf for a head with no valid key and no sink.
+ * Other arguments, results and errors as csa_sparse_mqa_fwd_sink, plus
+ * CSA_ERR_INVALID_ARG for a NULL lse. */
+csa_status_t csa_sparse_mqa_fwd_lse(const csa_params_t* p, const void* q, const void* kv_c,
+                                    const void* kv_raw, const int32_t* idx, const float* sinks,
+                                    void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Backward of stage 4, query side ("Enabling DeepSeek-V4-Flash Training on AMD
  * Instinct MI355X GPUs with Primus", section "Attention kernels for the three layer
  * types": the dQ kernel, with delta = rowsum(o * do) computed inside it):
@@ -224,6 +239,37 @@ csa_status_t csa_sparse_mqa_bwd_dq(const csa_params_t* p, const void* q, const v
                                    const void* kv_raw, const int32_t* idx, const float* sinks,
                                    const void* o, const void* d_o, void* dq, void* ws,
                                    size_t ws_bytes, void* stream);
+
+/* Backward of stage 4, key side ("Enabling DeepSeek-V4-Flash Training on AMD Instinct
+ * MI355X GPUs with Primus", section "Attention kernels for the three layer types":
+ * interm, the contraction over heads that gives each key's gradient, and the scatter of
+ * those gradients back to the entries; "fix(deepseek-v4): correct V4-Flash attention
+ * math", Part 1 item 6f: the sink is an fp32 logit of the softmax).  For the forward
+ * csa_sparse_mqa_fwd_lse with the same params, q, kv_c, kv_raw, idx and sinks, given
+ * its o and lse and d_o = dL/do [B,S,H,D], with the selection held fixed:
+ *   dkv_c [B,S/ratio,D] fp32 = dL/dkv_c (the rotated entries; a selected entry
+ *     collects the key gradient of every query that selected it):
+ *       dkey_k = sum_h ( softmax_scale p[h,k] (du[h].key_k - delta[h]) RoPE(q[h], P)
+ *                        + p[h,k] du[h] ),  du = RoPE(d_o, P), delta[h] = o[h].d_o[h],
+ *     p = exp(z - lse), P = pos0 + t; NULL exactly when kv_c is NULL;
+ *   dkv_raw [B,S,D] fp32 = dL/dkv_raw: the key gradients of window token t' over every
+ *     query whose window holds it, rotated by -(pos0 + t') and, with
+ *     CSA_FLAG_NORM_WINDOW, taken through the RMSNorm;
+ *   dsinks [H] fp32 = dL/dsinks[h] = -sum_{b,t} exp(sinks[h] - lse[b,t,h]) delta[b,t,h];
+ *     non-NULL exactly when sinks is.
+ * The outputs are overwritten (zero where nothing contributes).  Sums are fp32 in an
+ * order that does not depend on timing, so two calls give identical results; the
+ * per-pair gradients pass through the workspace in the activation dtype.  fp32
+ * activations need D <= 256 (CSA_ERR_UNSUPPORTED at 512).  ws:
+ * csa_workspace_bytes(p, CSA_OP_SPARSE_MQA_BWD) bytes (at most about 4.2 GiB plus the
+ * rotated window latents and per-query terms).  Errors as csa_sparse_mqa_fwd_sink,
+ * plus CSA_ERR_INVALID_ARG for a NULL o, lse, d_o or dkv_raw, or a dkv_c or dsinks
+ * that does not match kv_c or sinks. */
+csa_status_t csa_sparse_mqa_bwd_dkv(const csa_params_t* p, const void* q, const void* kv_c,
+                                    const void* kv_raw, const int32_t* idx, const float* sinks,
+                                    const void* o, const float* lse, const void* d_o, float* dkv_c,
+                                    float* dkv_raw, float* dsinks, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* Target distribution of the indexer's distillation loss ("fix(deepseek-v4): correct
  * V4-Flash attention math", Part 1 item 5: KL(attention || indexer) over the selected

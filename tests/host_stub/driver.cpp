@@ -177,6 +177,51 @@ static void bad_pointers() {
   EXPECT_ST(csa_sparse_mqa_bwd_dq(&p, L.in.q, L.in.q, L.in.kv_raw, idx, nullptr, L.o, nullptr, L.o, aws, awsb,
                                   nullptr), CSA_ERR_INVALID_ARG);  // d_o NULL
   EXPECT_ST(csa_kl_target(&p, L.in.q, nullptr, idx, (float*)L.o, nullptr), CSA_ERR_INVALID_ARG);
+  EXPECT_ST(csa_sparse_mqa_fwd_lse(&p, L.in.q, L.in.q, L.in.kv_raw, idx, nullptr, L.o, nullptr, aws, awsb, nullptr),
+            CSA_ERR_INVALID_ARG);  // lse NULL
+  {  // key-side backward: required and matching pointers, dtype limit, workspace size
+    const size_t dwsb = csa_workspace_bytes(&p, CSA_OP_SPARSE_MQA_BWD);
+    void* dws = buf(dwsb);
+    float* f = (float*)buf((size_t)p.B * p.S * p.D * 4);
+    float* lse = (float*)buf((size_t)p.B * p.S * p.H * 4);
+    const float* sk = (const float*)buf((size_t)p.H * 4);
+    float* dsk = (float*)buf((size_t)p.H * 4);
+    const void* kv = L.in.q;
+    struct Bad { const char* what; int want; int st; };
+    g_calls.clear();
+    const Bad bads[] = {
+        {"lse NULL", CSA_ERR_INVALID_ARG, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o,
+                                                                  nullptr, L.o, f, f, nullptr, dws, dwsb, nullptr)},
+        {"d_o NULL", CSA_ERR_INVALID_ARG, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o,
+                                                                  lse, nullptr, f, f, nullptr, dws, dwsb, nullptr)},
+        {"dkv_raw NULL", CSA_ERR_INVALID_ARG, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o,
+                                                                      lse, L.o, f, nullptr, nullptr, dws, dwsb, nullptr)},
+        {"dkv_c NULL", CSA_ERR_INVALID_ARG, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o,
+                                                                    lse, L.o, nullptr, f, nullptr, dws, dwsb, nullptr)},
+        {"dkv_c without kv_c", CSA_ERR_INVALID_ARG,
+         csa_sparse_mqa_bwd_dkv(&p, L.in.q, nullptr, L.in.kv_raw, nullptr, nullptr, L.o, lse, L.o, f, f, nullptr,
+                                dws, dwsb, nullptr)},
+        {"dsinks NULL", CSA_ERR_INVALID_ARG, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, sk, L.o,
+                                                                     lse, L.o, f, f, nullptr, dws, dwsb, nullptr)},
+        {"dsinks without sinks", CSA_ERR_INVALID_ARG,
+         csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o, lse, L.o, f, f, dsk, dws, dwsb,
+                                nullptr)},
+        {"lse misaligned", CSA_ERR_INVALID_ARG,
+         csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o, lse + 1, L.o, f, f, nullptr, dws,
+                                dwsb, nullptr)},
+        {"ws short", CSA_ERR_WORKSPACE, csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o, lse,
+                                                                L.o, f, f, nullptr, dws, dwsb - 1, nullptr)},
+        {"idx without kv_c", CSA_ERR_INVALID_ARG,
+         csa_sparse_mqa_bwd_dkv(&p, L.in.q, nullptr, L.in.kv_raw, idx, nullptr, L.o, lse, L.o, nullptr, f, nullptr,
+                                dws, dwsb, nullptr)},
+    };
+    for (const Bad& b : bads) EXPECT(b.st == b.want, "bwd_dkv %s -> %d, expected %d", b.what, b.st, b.want);
+    csa_params_t p512 = p;
+    p512.D = 512;
+    EXPECT_ST(csa_sparse_mqa_bwd_dkv(&p512, L.in.q, kv, L.in.kv_raw, idx, nullptr, L.o, lse, L.o, f, f, nullptr,
+                                     dws, dwsb, nullptr), CSA_ERR_UNSUPPORTED);  // fp32 at D = 512
+    EXPECT(g_calls.empty(), "bwd_dkv launched after a bad argument");
+  }
   // index_scores row range and ld
   float* sc = (float*)buf((size_t)p.B * p.S * 16 * 4);
   EXPECT_ST(csa_index_scores(&p, L.in.q_idx, L.in.w_idx, L.in.k_idx, sc, 16, 60, 8, nullptr), CSA_ERR_INVALID_ARG);
@@ -296,6 +341,22 @@ static void valid_calls() {
   EXPECT_ST(csa_sparse_mqa_bwd_dq(&p, L.in.q, kv_c, L.in.kv_raw, idx, sinks, L.o, L.o, dq, aws, awsb, nullptr),
             CSA_OK);
   EXPECT_ST(csa_kl_target(&p, L.in.q, kv_c, idx, (float*)buf((size_t)p.B * p.S * p.topk * 4), nullptr), CSA_OK);
+  float* lse = (float*)buf((size_t)p.B * p.S * p.H * 4);
+  EXPECT_ST(csa_sparse_mqa_fwd_lse(&p, L.in.q, kv_c, L.in.kv_raw, idx, sinks, L.o, lse, aws, awsb, nullptr), CSA_OK);
+  {  // key-side backward in its three modes, with and without sinks
+    const size_t dwsb = csa_workspace_bytes(&p, CSA_OP_SPARSE_MQA_BWD);
+    EXPECT(dwsb > awsb, "key-side workspace %zu", dwsb);
+    void* dws = buf(dwsb);
+    float* dkv_c = (float*)buf((size_t)p.B * (p.S / p.ratio) * p.D * 4);
+    float* dkv_raw = (float*)buf((size_t)p.B * p.S * p.D * 4);
+    float* dsk = (float*)buf((size_t)p.H * 4);
+    EXPECT_ST(csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv_c, L.in.kv_raw, idx, sinks, L.o, lse, L.o, dkv_c, dkv_raw, dsk,
+                                     dws, dwsb, nullptr), CSA_OK);
+    EXPECT_ST(csa_sparse_mqa_bwd_dkv(&p, L.in.q, kv_c, L.in.kv_raw, nullptr, nullptr, L.o, lse, L.o, dkv_c, dkv_raw,
+                                     nullptr, dws, dwsb, nullptr), CSA_OK);
+    EXPECT_ST(csa_sparse_mqa_bwd_dkv(&p, L.in.q, nullptr, L.in.kv_raw, nullptr, sinks, L.o, lse, L.o, nullptr,
+                                     dkv_raw, dsk, dws, dwsb, nullptr), CSA_OK);
+  }
   csa_params_t pk = p;
   pk.flags = CSA_FLAG_INDEX_FP8;
   pk.idx_dim = 64;
@@ -304,7 +365,8 @@ static void valid_calls() {
   EXPECT_ST(csa_debug_layout(&p, (int32_t*)buf(16 * 4), (int32_t*)buf(64 * 4), (int32_t*)buf(64 * 4), nullptr),
             CSA_OK);
   const char* want = "compress,index_topk,index_topk,index_scores,window_rope,mqa_selected,window_rope,mqa_dense,"
-                     "window_rope,mqa_window,window_rope,bwd_dq,kl_target,index_keys,debug_layout";
+                     "window_rope,mqa_window,window_rope,bwd_dq,kl_target,window_rope,mqa_selected,"
+                     "window_rope,bwd_dkv,window_rope,bwd_dkv,window_rope,bwd_dkv,index_keys,debug_layout";
   EXPECT(joined() == want, "stage calls %s", joined().c_str());
   EXPECT(csa_abi_version() == CSA_ABI_VERSION, "abi version");
   EXPECT(strcmp(csa_status_str((csa_status_t)42), "CSA_ERR_UNKNOWN") == 0, "unknown status string");

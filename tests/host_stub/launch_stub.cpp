@@ -10,6 +10,8 @@
 
 #include "launch.hpp"
 #include "mqa_bwd.hpp"
+#include "mqa_bwd_dkv.hpp"
+#include "validate.hpp"
 
 std::vector<std::string> g_calls;
 hipError_t g_fail = hipSuccess;  // returned by every launcher when set
@@ -106,13 +108,14 @@ hipError_t launch_topk(const csa_params_t& p, const float* scores, int64_t ld, i
 
 hipError_t launch_sparse_mqa(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
                              const void* kv_w, const int32_t* idx, const float* sinks, void* o,
-                             hipStream_t) {
+                             float* lse, hipStream_t) {
   touch_in(q, bs(p) * p.H * p.D * es(p));
   if (mode != MQA_WINDOW_ONLY) touch_in(kv_c, (size_t)p.B * n_ent(p) * p.D * es(p));
   touch_in(kv_w, bs(p) * p.D * es(p));
   if (mode == MQA_SELECTED) touch_in(idx, bs(p) * p.topk * 4);
   if (sinks) touch_in(sinks, (size_t)p.H * 4);
   touch_out(o, bs(p) * p.H * p.D * es(p));
+  if (lse) touch_out(lse, bs(p) * p.H * 4);
   return done(mode == MQA_SELECTED ? "mqa_selected" : mode == MQA_DENSE ? "mqa_dense" : "mqa_window");
 }
 
@@ -145,6 +148,55 @@ hipError_t launch_mqa_bwd_dq(const csa_params_t& p, MqaMode mode, const void* q,
   touch_in(d_o, bs(p) * p.H * p.D * es(p));
   touch_out(dq, bs(p) * p.H * p.D * es(p));
   return done("bwd_dq");
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t) {
+  touch_out(p, n * 4);
+  return done("zero");
+}
+
+// Writes what the real launcher writes, chunk by chunk: the outputs, and in each chunk
+// the intermediate rows and the counting-sort and segment regions at their per-chunk
+// extents, so a plan smaller than any chunk needs shows up under the sanitizer.
+hipError_t launch_mqa_bwd_dkv(const csa_params_t& p, MqaMode mode, const void* q, const void* kv_c,
+                              const void* kv_w, const void* kv_raw, const int32_t* idx, const float* sinks,
+                              const void* o, const float* lse, const void* d_o, float* dkv_c, float* dkv_raw,
+                              float* dsinks, const DkvWs& w, hipStream_t) {
+  const size_t act = bs(p) * p.H * p.D * es(p);
+  const size_t n = mode == MQA_WINDOW_ONLY ? 0 : n_ent(p);
+  touch_in(q, act);
+  touch_in(o, act);
+  touch_in(d_o, act);
+  touch_in(lse, bs(p) * p.H * 4);
+  touch_in(kv_w, bs(p) * p.D * es(p));
+  touch_in(kv_raw, bs(p) * p.D * es(p));
+  if (mode != MQA_WINDOW_ONLY) touch_in(kv_c, (size_t)p.B * n * p.D * es(p));
+  if (mode == MQA_SELECTED) touch_in(idx, bs(p) * p.topk * 4);
+  if (sinks) touch_in(sinks, (size_t)p.H * 4);
+  if (dkv_c) touch_out(dkv_c, (size_t)p.B * n * p.D * 4);
+  touch_out(dkv_raw, bs(p) * p.D * 4);
+  const DkvShape sh = dkv_shape(p, mode == MQA_SELECTED ? 0 : (mode == MQA_DENSE ? 1 : 2));
+  const int64_t rows = (int64_t)bs(p);
+  for (int64_t r0 = 0; r0 < rows; r0 += sh.rows) {
+    const int64_t nr = rows - r0 < sh.rows ? rows - r0 : sh.rows;
+    touch_out(w.interm, (size_t)nr * sh.kw * p.D * es(p));
+    if (sh.kmax > 0) {
+      const int64_t nkeys = ((r0 + nr - 1) / p.S - r0 / p.S + 1) * (int64_t)n;
+      const int64_t nblk = (nr + kDkvRowBlock - 1) / kDkvRowBlock;
+      touch_out(w.cnt, (size_t)(nblk * nkeys) * 4);
+      touch_out(w.tot, (size_t)nkeys * 4);
+      touch_out(w.base, (size_t)(nkeys + 1) * 4);
+      touch_out(w.segbase, (size_t)(nkeys + 1) * 4);
+      touch_out(w.list, (size_t)(nr * sh.kmax) * 4);
+      touch_out(w.partial, (size_t)(nr * sh.kmax / kDkvSeg + nkeys + 1) * p.D * 4);
+    }
+  }
+  if (sinks) {
+    touch_out(w.ds_row, bs(p) * p.H * 4);
+    touch_out(w.sink_part, (size_t)kDkvSinkGroups * p.H * 4);
+    touch_out(dsinks, (size_t)p.H * 4);
+  }
+  return done("bwd_dkv");
 }
 
 }  // namespace csa

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert bd.lib.csa_abi_version() == 7
+    assert bd.lib.csa_abi_version() == 8
     for code, name in bd._status_names.items():
         assert bd.lib.csa_status_str(code).decode() == name
 
@@ -271,6 +271,52 @@ def test_bwd_dq_rejects():
     assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
     z = ctypes.byref(p_c1(B=0))
     assert bd.lib.csa_sparse_mqa_bwd_dq(z, None, None, None, None, None, None, None, None, None, 0, None) == bd.CSA_OK
+
+
+def test_bwd_dkv_rejects():
+    """Argument checks of csa_sparse_mqa_bwd_dkv (and of the forward that keeps lse)
+    fail before any GPU call."""
+    W = 1 << 40
+
+    def call(p, q=A, kv=A, kvr=A, idx=A, sinks=None, o=A, lse=A, d_o=A, dkv_c=A, dkv_raw=A, dsinks=None, wsb=W):
+        return bd.lib.csa_sparse_mqa_bwd_dkv(ctypes.byref(p), q, kv, kvr, idx, sinks, o, lse, d_o, dkv_c, dkv_raw,
+                                             dsinks, A, wsb, None)
+    assert call(p_c1(), lse=None) == bd.CSA_ERR_INVALID_ARG and "lse" in bd.last_error()
+    assert call(p_c1(), d_o=None) == bd.CSA_ERR_INVALID_ARG and "d_o" in bd.last_error()
+    assert call(p_c1(), dkv_raw=None) == bd.CSA_ERR_INVALID_ARG and "dkv_raw" in bd.last_error()
+    assert call(p_c1(), dkv_c=None) == bd.CSA_ERR_INVALID_ARG and "dkv_c" in bd.last_error()
+    assert call(p_c1(), kv=None, idx=None) == bd.CSA_ERR_INVALID_ARG and "dkv_c" in bd.last_error()
+    assert call(p_c1(), sinks=A) == bd.CSA_ERR_INVALID_ARG and "dsinks" in bd.last_error()
+    assert call(p_c1(), dsinks=A) == bd.CSA_ERR_INVALID_ARG and "dsinks" in bd.last_error()
+    assert call(p_c1(), lse=A + 4) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(), kv=None) == bd.CSA_ERR_INVALID_ARG and "idx" in bd.last_error()
+    assert call(p_c1(), wsb=0) == bd.CSA_ERR_WORKSPACE
+    assert call(p_c1(H=65)) == bd.CSA_ERR_INVALID_ARG
+    assert call(p_c1(D=192)) == bd.CSA_ERR_UNSUPPORTED
+    assert call(p_c1(dtype=bd.CSA_F32)) == bd.CSA_ERR_UNSUPPORTED and "D <= 256" in bd.last_error()
+    z = ctypes.byref(p_c1(B=0))  # empty batch without sinks: nothing to launch
+    assert bd.lib.csa_sparse_mqa_bwd_dkv(z, *([None] * 11), None, 0, None) == bd.CSA_OK
+    assert bd.lib.csa_sparse_mqa_fwd_lse(ctypes.byref(p_c1()), A, A, A, A, None, A, None, A, W, None) \
+        == bd.CSA_ERR_INVALID_ARG and "lse" in bd.last_error()
+
+
+def test_bwd_dkv_workspace():
+    """The key-side workspace holds the rotated window latents, the per-query sink terms
+    and a chunk of per-pair key gradients of at most 4 GiB plus the chunk's inverse
+    index; the chunk covers the whole problem when it fits."""
+    c1 = bd.params(wl.C1)
+    ws1 = bd.workspace_bytes(c1, bd.OP_SPARSE_MQA_BWD)
+    win = 4096 * 512 * 2
+    assert ws1 >= win + 4096 * (512 + 128) * 512 * 2      # every row's pairs of the selected mode
+    assert ws1 <= win + (4 << 30) + (256 << 20)
+    c3 = bd.params(wl.C3)
+    ws3 = bd.workspace_bytes(c3, bd.OP_SPARSE_MQA_BWD)
+    assert (4 << 30) - (1 << 20) <= ws3 - 65536 * 512 * 2 <= (4 << 30) + (256 << 20)
+    c0 = bd.params(wl.C0)
+    assert 0 < bd.workspace_bytes(c0, bd.OP_SPARSE_MQA_BWD) < 64 << 20
+    swa = bd.params(wl.C1.replace(kind="swa", topk=0))
+    assert bd.workspace_bytes(swa, bd.OP_SPARSE_MQA_BWD) >= win + 4096 * 128 * 512 * 2
+    assert bd.workspace_bytes(p_c1(D=192), bd.OP_SPARSE_MQA_BWD) == 0
 
 
 # ---- the binding checks dtype and size against the params before any call --------
