@@ -39,6 +39,8 @@
 #include "mqa_bwd_dkv.hpp"
 #include "validate.hpp"
 
+#include <type_traits>
+
 namespace csa {
 namespace {
 
@@ -76,6 +78,16 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // h' = 2 head + {0: ds, 1: p} on K).  The A operand of the second product, qu, holds at
 // k-slot h' = 32j + 8g + e the value (e even: q~, e odd: du) of head 16j + 4g + e/2 at
 // the lane's dim; the exchange rows hold ds and p of one key in the same h' order.
+//
+// Pipeline (one workgroup per CU, one wave per SIMD): per tile t, the softmax of t
+// writes its exchange buffer (two, alternating), then one barrier is both the exchange
+// barrier of t and the arrival of tile t+1; after it the key gradients of t and the
+// logits and dP of t+1 are issued interleaved, so the MFMA pipe has work while the
+// LDS reads of either wait.  After that barrier tile t+NS is requested into tile t's
+// stage (its logits were formed in the step before), so NS-1 tiles stay in flight
+// beyond the one being waited for.  The gradient rows of t are stored right after the
+// next barrier: the arrival wait counts stores and loads together (gfx9 vmcnt), and
+// stores issued a whole tile earlier have completed by then.
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
   constexpr int NT = NW * 64;
@@ -95,20 +107,25 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
   constexpr int TILEB = NL * LSTRIDE;
   constexpr int SB = TILEB > (HP / 2) * QROWB ? TILEB : (HP / 2) * QROWB;
   constexpr int XS = 2 * HP * ES + 16;  // exchange row (one key) stride, padded
+  constexpr int XB = KT * XS;
   constexpr int DW = D / NW;            // dims of the key gradient per wave
   constexpr int DBW = DW / 16;
+  constexpr int KS = D / 32;            // k-steps of the logit products
   static_assert(NL % NW == 0, "every wave issues the same number of line loads");
+  static_assert(DBW * NW * 2 == 4 * KS, "four key-gradient MFMAs per logit k-step");
   constexpr int LPT = NL / NW;
-  constexpr int NS = (4 * SB + KT * XS + 10 * 1024 <= 160 * 1024 && 2 * LPT <= 63) ? 4 : 2;
+  constexpr int NS = (4 * SB + 2 * XB + 10 * 1024 <= 160 * 1024 && 3 * LPT <= 63) ? 4 : 2;
   constexpr int SB2 = NS == 4 ? SB : 16;
   __shared__ __attribute__((aligned(16))) unsigned char st0[SB];
   __shared__ __attribute__((aligned(16))) unsigned char st1[SB];
   __shared__ __attribute__((aligned(16))) unsigned char st2[SB2];
   __shared__ __attribute__((aligned(16))) unsigned char st3[SB2];
-  __shared__ __attribute__((aligned(16))) unsigned char xs[KT * XS];
+  __shared__ __attribute__((aligned(16))) unsigned char xs0[XB];
+  __shared__ __attribute__((aligned(16))) unsigned char xs1[XB];
   __shared__ int kv0[KT], kv1[KT], kv2[KT], kv3[KT];
   __shared__ int sidx[kMaxTopk];
   __shared__ float2 cs[64];
+  __shared__ float sdelta[HP];
 
   // workgroup -> row of the chunk: 32 consecutive rows per XCD visit, latest first
   const int total = a.nrows;
@@ -151,16 +168,54 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
   const unsigned char* dog = reinterpret_cast<const unsigned char*>(a.d_o) + row0;
   const unsigned char* og = reinterpret_cast<const unsigned char*>(a.o) + row0;
 
-  auto stage_rows = [&](const unsigned char* src) {
-    for (int c = threadIdx.x; c < HP * NCH; c += NT) {
+  // rows of heads 0..HP/2-1 in stage lo, the rest in stage hi (heads >= H zero)
+  constexpr int SCH = HP * NCH / NT;  // 16-byte chunks per thread
+  auto stage_rows = [&](const unsigned char* src, unsigned char* lo, unsigned char* hi) {
+    uint4 v[SCH];
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int c = threadIdx.x + i * NT;
       const int row = c / NCH, col = (c % NCH) * 16;
-      const uint4 v = row < a.H ? *reinterpret_cast<const uint4*>(src + (int64_t)row * ROWB + col)
-                                : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>((row < HP / 2 ? st0 : st1) + (row % (HP / 2)) * QROWB + col) = v;
+      v[i] = row < a.H ? *reinterpret_cast<const uint4*>(src + (int64_t)row * ROWB + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int row = c / NCH, col = (c % NCH) * 16;
+      *reinterpret_cast<uint4*>((row < HP / 2 ? lo : hi) + (row % (HP / 2)) * QROWB + col) = v[i];
     }
   };
-  auto head_row = [&](int hh) -> unsigned char* {
-    return (hh < HP / 2 ? st0 : st1) + (hh % (HP / 2)) * QROWB;
+  // do rows staged as stage_rows does, with delta[row] = o[row] . do[row] from the o
+  // chunks loaded beside them (NCH lanes hold one row: a segmented lane sum)
+  static_assert(NCH <= 64 && 64 % NCH == 0, "a row's chunks sit in one wave");
+  auto stage_rows_delta = [&](const unsigned char* src, const unsigned char* osrc, unsigned char* lo,
+                              unsigned char* hi) {
+    uint4 v[SCH], w[SCH];
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int row = c / NCH, col = (c % NCH) * 16;
+      const bool in = row < a.H;
+      v[i] = in ? *reinterpret_cast<const uint4*>(src + (int64_t)row * ROWB + col) : make_uint4(0, 0, 0, 0);
+      w[i] = in ? *reinterpret_cast<const uint4*>(osrc + (int64_t)row * ROWB + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int row = c / NCH, col = (c % NCH) * 16;
+      *reinterpret_cast<uint4*>((row < HP / 2 ? lo : hi) + (row % (HP / 2)) * QROWB + col) = v[i];
+      const T* dv = reinterpret_cast<const T*>(&v[i]);
+      const T* ov = reinterpret_cast<const T*>(&w[i]);
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16 / ES; ++e) x = fmaf(to_f32(dv[e]), to_f32(ov[e]), x);
+#pragma unroll
+      for (int m = NCH / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+      if (c % NCH == 0) sdelta[row] = x;
+    }
+  };
+  auto row_in = [&](unsigned char* lo, unsigned char* hi, int hh) -> unsigned char* {
+    return (hh < HP / 2 ? lo : hi) + (hh % (HP / 2)) * QROWB;
   };
   auto rotate_frag = [&](Frag<T>& f, int d0) {
     if (d0 + 8 > rlo) {
@@ -180,10 +235,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
     *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(f.v);
     if constexpr (ES == 4) *reinterpret_cast<uint4*>(p + 16) = *reinterpret_cast<const uint4*>(f.v + 4);
   };
-  // k-slots e = kind (0: q~, 1: du) .. of the key-gradient operand, from the staged and
-  // rotated rows: head 16j + 4g + e/2 at dim wave*DW + 16db + hl
+  // k-slots e = kind (0: q~, 1: du) .. of the key-gradient operand, from rotated rows:
+  // head 16j + 4g + e/2 at dim wave*DW + 16db + hl
   Frag<T> qu[DBW][NW];
-  auto read_qu = [&](int kind) {
+  auto read_qu = [&](int kind, unsigned char* lo, unsigned char* hi) {
 #pragma unroll
     for (int db = 0; db < DBW; ++db)
 #pragma unroll
@@ -191,43 +246,57 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
 #pragma unroll
         for (int e = kind; e < 8; e += 2) {
           const int hh = 16 * j + 4 * g + (e >> 1);
-          qu[db][j].v[e] = reinterpret_cast<const T*>(head_row(hh))[wave * DW + 16 * db + hl];
+          qu[db][j].v[e] = reinterpret_cast<const T*>(row_in(lo, hi, hh))[wave * DW + 16 * db + hl];
         }
   };
 
   // ---- operands: q~ and du as register fragments (lane: head h, dims 32k + 8g ..),
-  // written back rotated so the key-gradient operand can be read from the same rows
-  Frag<T> qf[D / 32], uf[D / 32];
-  stage_rows(qg);
-  __syncthreads();
+  // written back rotated so the key-gradient operand can be read from the same rows;
+  // delta = o . do from the unrotated rows.  With four stages q and do are staged
+  // together (st0/st1 and st2/st3), else one after the other.
+  Frag<T> qf[KS], uf[KS];
+  unsigned char* ulo = NS == 4 ? st2 : st0;
+  unsigned char* uhi = NS == 4 ? st3 : st1;
+  auto build_q = [&]() {
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    qf[k] = load_frag(reinterpret_cast<const T*>(head_row(h)) + 32 * k + 8 * g);
-    rotate_frag(qf[k], 32 * k + 8 * g);
-    store_frag(head_row(h) + (32 * k + 8 * g) * ES, qf[k]);
-  }
-  __syncthreads();
-  read_qu(0);
-  __syncthreads();
-  stage_rows(dog);
-  __syncthreads();
-  float delta = 0.f;
-#pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d0 = 32 * k + 8 * g;
-    uf[k] = load_frag(reinterpret_cast<const T*>(head_row(h)) + d0);
-    if (h < a.H) {
-      const Frag<T> of = load_frag(reinterpret_cast<const T*>(og + (int64_t)h * ROWB) + d0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) delta = fmaf(to_f32(uf[k].v[i]), to_f32(of.v[i]), delta);
+    for (int k = 0; k < KS; ++k) {
+      qf[k] = load_frag(reinterpret_cast<const T*>(row_in(st0, st1, h)) + 32 * k + 8 * g);
+      rotate_frag(qf[k], 32 * k + 8 * g);
+      store_frag(row_in(st0, st1, h) + (32 * k + 8 * g) * ES, qf[k]);
     }
-    rotate_frag(uf[k], d0);
-    store_frag(head_row(h) + d0 * ES, uf[k]);
+  };
+  auto build_u = [&]() {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int d0 = 32 * k + 8 * g;
+      uf[k] = load_frag(reinterpret_cast<const T*>(row_in(ulo, uhi, h)) + d0);
+      rotate_frag(uf[k], d0);
+      store_frag(row_in(ulo, uhi, h) + d0 * ES, uf[k]);
+    }
+  };
+  if constexpr (NS == 4) {
+    stage_rows(qg, st0, st1);
+    stage_rows_delta(dog, og, st2, st3);
+    __syncthreads();
+    build_q();
+    build_u();
+    __syncthreads();
+    read_qu(0, st0, st1);
+    read_qu(1, st2, st3);
+  } else {
+    stage_rows(qg, st0, st1);
+    __syncthreads();
+    build_q();
+    __syncthreads();
+    read_qu(0, st0, st1);
+    __syncthreads();
+    stage_rows_delta(dog, og, st0, st1);
+    __syncthreads();
+    build_u();
+    __syncthreads();
+    read_qu(1, st0, st1);
   }
-  delta += __shfl_xor(delta, 16, 64);
-  delta += __shfl_xor(delta, 32, 64);
-  __syncthreads();
-  read_qu(1);
+  const float delta = sdelta[h];
   // log2 of the head's denominator; +inf (p = 0) for padded heads and for heads whose
   // forward had no mass (lse = -inf: no valid key and no sink)
   float lse2 = INFINITY;
@@ -262,32 +331,68 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
     return qg;
   };
   auto issue = [&](int tile, unsigned char* sb, int* kv) {
-    int sv = 0;
-    if constexpr (RPL == 1) {
-      const int kk = tile * KT + (lane % KT);
-      sv = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
-    }
-#pragma unroll
-    for (int L = wave; L < NL; L += NW) {
-      int rr, byte;
-      if constexpr (RPL > 1) {
-        rr = L * RPL + lane / NCH;
-        byte = (lane % NCH) * 16;
-      } else if constexpr (SWZ) {
-        rr = L;
-        byte = (lane ^ swz(rr)) * 16;
-      } else {
-        rr = L / LPR;
-        byte = (L % LPR) * 1024 + lane * 16;
+    if constexpr (ROWB == 1024) {
+      // one 1 KB line per key row: lane l < 32 resolves key tile*32 + l (branch-free),
+      // each line takes its row base by v_readlane and copies with a fixed per-lane
+      // swizzled offset
+      const int kk = tile * KT + (lane & 31);
+      const unsigned char* src = qg;  // masked keys read finite data that is never used
+      bool ok = false;
+      if (kk < nsel) {
+        const int sv = a.mode == MQA_SELECTED ? sidx[kk] : kk;
+        ok = sv >= 0 && sv < n_t;
+        src = ok ? kv_c + ((int64_t)b * a.n_entries + sv) * ROWB : qg;
+      } else if (kk < nk) {
+        ok = true;
+        src = kv_w + ((int64_t)b * a.S + wlo + (kk - nsel)) * ROWB;
       }
-      int ok, s;
-      const int kk = tile * KT + rr;
-      if constexpr (RPL == 1) s = __builtin_amdgcn_readlane(sv, rr);
-      else s = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
-      const unsigned char* src = key_src(kk, s, &ok);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + byte),
-                                       (CSA_LDS void*)(sb + L * LSTRIDE), 16, 0, 0);
-      if (byte == 0) kv[rr] = ok;
+      if (wave == 0 && lane < KT) kv[lane] = ok;
+      const uint64_t sp = reinterpret_cast<uint64_t>(src);
+      const uint32_t sp_lo = (uint32_t)sp, sp_hi = (uint32_t)(sp >> 32);
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)sb;
+#pragma unroll
+      for (int m = 0; m < LPT; ++m) {
+        const int rr = wave + NW * m;
+        const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, rr) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, rr);
+        const uint32_t off = (uint32_t)((SWZ ? (lane ^ swz(rr)) : lane) << 4);
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)rr * LSTRIDE);
+        // The row base was just written to SGPRs by v_readlane (a VALU op), and M0
+        // just set: a vector-memory instruction may read such SGPRs only 5 wait states
+        // later, and the compiler does not pad for an instruction inside inline
+        // assembly.  As assembly the copy is also invisible to the compiler's wait-count
+        // tracking, which would otherwise drain every copy in flight before each LDS
+        // write it cannot tell apart from the stages; this kernel's own waits
+        // (vm_wait_barrier) order the copies.
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(row), "{m0}"(lds) : "memory");
+      }
+    } else {
+      int sv = 0;
+      if constexpr (RPL == 1) {
+        const int kk = tile * KT + (lane % KT);
+        sv = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
+      }
+#pragma unroll
+      for (int L = wave; L < NL; L += NW) {
+        int rr, byte;
+        if constexpr (RPL > 1) {
+          rr = L * RPL + lane / NCH;
+          byte = (lane % NCH) * 16;
+        } else {
+          rr = L / LPR;
+          byte = (L % LPR) * 1024 + lane * 16;
+        }
+        int ok, s;
+        const int kk = tile * KT + rr;
+        if constexpr (RPL == 1) s = __builtin_amdgcn_readlane(sv, rr);
+        else s = a.mode == MQA_SELECTED ? (kk < nsel ? sidx[kk] : -1) : kk;
+        const unsigned char* src = key_src(kk, s, &ok) + byte;
+        // as above: invisible to the compiler's wait counting, padded for M0
+        const uint32_t lds =
+            __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(sb + L * LSTRIDE));
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+        if (byte == 0) kv[rr] = ok;
+      }
     }
   };
 
@@ -303,119 +408,174 @@ __global__ __launch_bounds__(NW * 64, 1) void mqa_bwd_dkv_kernel(DkvArgs a) {
   unsigned char* const interm = reinterpret_cast<unsigned char*>(a.interm);
   const int64_t prow = (int64_t)(r - a.r0) * a.kw;  // first slot row of this query
 
-  auto compute = [&](const unsigned char* sb, const int* kv, int tile) {
+  typedef f32x4 Acc[4];  // logits (keys 4g+i, 16+4g+i) and dP of one tile, this wave's heads
+  auto ld_k = [&](const CSA_LDS unsigned char* lb, int row16, int k) {
+    Frag<T> f;
+    const CSA_LDS unsigned char* p =
+        lb + qk_base[k & 1] + (SWZ ? row16 * 1024 + 64 * k : eoff(row16, 32 * k) - eoff(0, 0));
+    *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
+    if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
+    return f;
+  };
+  auto qk_only = [&](const unsigned char* sb, Acc& acc) {
     const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
-    auto ld_k = [&](int row16, int k) {
-      Frag<T> f;
-      const CSA_LDS unsigned char* p =
-          lb + qk_base[k & 1] + (SWZ ? row16 * 1024 + 64 * k : eoff(row16, 32 * k) - eoff(0, 0));
-      *reinterpret_cast<u32x4*>(f.v) = *(const CSA_LDS u32x4*)p;
-      if constexpr (ES == 4) *reinterpret_cast<u32x4*>(f.v + 4) = *(const CSA_LDS u32x4*)(p + 16);
-      return f;
-    };
-    // logits and dP, transposed: rows are keys (4g+i, 16+4g+i), columns this wave's heads
-    constexpr int KS = D / 32, PQ = KS < 3 ? KS : 3;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
-    Frag<T> ka[PQ], kb[PQ];
 #pragma unroll
-    for (int k = 0; k < PQ; ++k) {
-      ka[k] = ld_k(0, k);
-      kb[k] = ld_k(16, k);
-    }
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      const Frag<T> a0 = ka[k % PQ], a1 = kb[k % PQ];
-      if (k + PQ < KS) {
-        ka[k % PQ] = ld_k(0, k + PQ);
-        kb[k % PQ] = ld_k(16, k + PQ);
-      }
-      s0 = mfma16x16x32(a0, qf[k], s0);
-      s1 = mfma16x16x32(a1, qf[k], s1);
-      p0 = mfma16x16x32(a0, uf[k], p0);
-      p1 = mfma16x16x32(a1, uf[k], p1);
+      const Frag<T> a0 = ld_k(lb, 0, k), a1 = ld_k(lb, 16, k);
+      acc[0] = mfma16x16x32(a0, qf[k], acc[0]);
+      acc[1] = mfma16x16x32(a1, qf[k], acc[1]);
+      acc[2] = mfma16x16x32(a0, uf[k], acc[2]);
+      acc[3] = mfma16x16x32(a1, uf[k], acc[3]);
     }
-    // p = exp(z - lse), ds = scale p (dP - delta), both rounded to T, to the exchange
-    // rows at h' = 2h (ds) and 2h + 1 (p)
+  };
+  // p = exp(z - lse), ds = scale p (dP - delta), both rounded to T, into the exchange
+  // rows at h' = 2h (ds) and 2h + 1 (p)
+  auto softmax = [&](const Acc& acc, const int* kv, unsigned char* xb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
-      const float z = i < 4 ? s0[i] : s1[i - 4];
-      const float dp = i < 4 ? p0[i] : p1[i - 4];
+      const float z = i < 4 ? acc[0][i] : acc[1][i - 4];
+      const float dp = i < 4 ? acc[2][i] : acc[3][i - 4];
       const float pr = kv[key] ? __builtin_amdgcn_exp2f(z * a.scale_log2 - lse2) : 0.f;
-      T pair[2] = {from_f32<T>(a.scale * pr * (dp - delta)), from_f32<T>(pr)};
-      unsigned char* xp = xs + key * XS + 2 * h * ES;
-      if constexpr (ES == 2) *reinterpret_cast<uint32_t*>(xp) = *reinterpret_cast<const uint32_t*>(pair);
-      else *reinterpret_cast<uint2*>(xp) = *reinterpret_cast<const uint2*>(pair);
+      const float2 pd = make_float2(a.scale * pr * (dp - delta), pr);
+      unsigned char* xp = xb + key * XS + 2 * h * ES;
+      if constexpr (ES == 2) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<uint32_t*>(xp) =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{pd.x, pd.y}, bf16x2_t));
+      } else {
+        *reinterpret_cast<float2*>(xp) = pd;
+      }
     }
-    lds_barrier();  // every head's ds and p of this tile are in the exchange rows
-    // dkey^T[dims, keys] = qu . X over the 2*HP values, keys 16kb + hl of the tile, one
-    // dim block at a time (its two accumulators are stored before the next block)
+  };
+  // key gradients of a tile, rounded to T: lane (dims 4g..4g+3 of block db, key 16kb + hl)
+  typedef typename std::conditional<ES == 2, uint2, uint4>::type Pack;
+  // deferred stores need the tile's rows in registers; where that is too many (one
+  // wave holding every dim) each dim block is stored as soon as it is formed
+  constexpr bool DEFER = DBW * 2 * (int)sizeof(Pack) / 4 <= 32;
+  Pack pend[DEFER ? DBW : 1][2];
+  auto pack = [&](const f32x4& c) -> Pack {
+    if constexpr (ES == 2) {
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+      return __builtin_bit_cast(Pack, __builtin_convertvector(c, bf16x4_t));
+    } else {
+      return __builtin_bit_cast(Pack, c);
+    }
+  };
+  auto row_dst = [&](int tile, int kb) -> unsigned char* {
+    const int kk = tile * KT + 16 * kb + hl;
+    if (kk >= nk) return nullptr;
+    const int slot = kk < nsel ? kk : a.kmax + (kk - nsel);
+    return interm + ((prow + slot) * D + wave * DW + 4 * g) * ES;
+  };
+  // the gradient rows of tile `tile` (in pend) to their slot rows (nothing to do when
+  // they were stored as formed)
+  auto store_tile = [&](int tile) {
+    if constexpr (DEFER) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        unsigned char* dst = row_dst(tile, kb);
+        if (dst) {
+#pragma unroll
+          for (int db = 0; db < DBW; ++db) *reinterpret_cast<Pack*>(dst + 16 * db * ES) = pend[db][kb];
+        }
+      }
+    }
+  };
+  // key gradients of the tile whose exchange rows are in xb (into pend), interleaved
+  // with the logits and dP of the tile in nsb (into nacc): per logit k-step, four
+  // MFMAs of each
+  auto grad_and_qk = [&](const unsigned char* xb, const unsigned char* nsb, Acc& nacc, int tile) {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)nsb;
+    unsigned char* dst0 = DEFER ? nullptr : row_dst(tile, 0);
+    unsigned char* dst1 = DEFER ? nullptr : row_dst(tile, 1);
     Frag<T> xf[NW][2];
 #pragma unroll
     for (int j = 0; j < NW; ++j)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const unsigned char* p = xs + (16 * kb + hl) * XS + (32 * j + 8 * g) * ES;
+        const unsigned char* p = xb + (16 * kb + hl) * XS + (32 * j + 8 * g) * ES;
         *reinterpret_cast<uint4*>(xf[j][kb].v) = *reinterpret_cast<const uint4*>(p);
         if constexpr (ES == 4) *reinterpret_cast<uint4*>(xf[j][kb].v + 4) = *reinterpret_cast<const uint4*>(p + 16);
       }
-    // lane (dims 4g..4g+3 of block db, key 16kb + hl) -> the key's slot row
-    unsigned char* dst[2];
-    bool live[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kk = tile * KT + 16 * kb + hl;
-      live[kb] = kk < nk;
-      const int slot = kk < nsel ? kk : a.kmax + (kk - nsel);
-      dst[kb] = interm + ((prow + slot) * D + wave * DW + 4 * g) * ES;
-    }
+    for (int i = 0; i < 4; ++i) nacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 c4[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int k = 0; k < KS; ++k) {
+      const Frag<T> a0 = ld_k(lb, 0, k), a1 = ld_k(lb, 16, k);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        acc[0] = mfma16x16x32(qu[db][j], xf[j][0], acc[0]);
-        acc[1] = mfma16x16x32(qu[db][j], xf[j][1], acc[1]);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (live[kb]) {
-          T y[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = from_f32<T>(acc[kb][i]);
-          unsigned char* d = dst[kb] + 16 * db * ES;
-          if constexpr (ES == 2) *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(y);
-          else *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(y);
+      for (int m = 0; m < 2; ++m) {  // two (db, j) pairs of the key gradient per k-step
+        const int f = 2 * k + m;
+        const int db = f / NW, j = f % NW;
+        c4[0] = mfma16x16x32(qu[db][j], xf[j][0], c4[0]);
+        c4[1] = mfma16x16x32(qu[db][j], xf[j][1], c4[1]);
+        if (j == NW - 1) {
+          if constexpr (DEFER) {
+            pend[db][0] = pack(c4[0]);
+            pend[db][1] = pack(c4[1]);
+          } else {
+            if (dst0) *reinterpret_cast<Pack*>(dst0 + 16 * db * ES) = pack(c4[0]);
+            if (dst1) *reinterpret_cast<Pack*>(dst1 + 16 * db * ES) = pack(c4[1]);
+          }
+          c4[0] = c4[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
+      nacc[0] = mfma16x16x32(a0, qf[k], nacc[0]);
+      nacc[1] = mfma16x16x32(a1, qf[k], nacc[1]);
+      nacc[2] = mfma16x16x32(a0, uf[k], nacc[2]);
+      nacc[3] = mfma16x16x32(a1, uf[k], nacc[3]);
     }
   };
 
   const int ntiles = (nk + KT - 1) / KT;
-  auto step = [&](int tl, const unsigned char* cur, const int* kvc, unsigned char* nxt, int* kvn) {
-    const int after = min(ntiles - 1, tl + NS - 2) - tl;
-    if (after <= 0) vm_wait_barrier<0>();
-    else if (after == 1) vm_wait_barrier<LPT>();
-    else vm_wait_barrier<2 * LPT>();
-    if (tl + NS - 1 < ntiles) issue(tl + NS - 1, nxt, kvn);
-    compute(cur, kvc, tl);
+  // all stages filled up front; tile t+NS then goes to tile t's stage once tile t's
+  // logits (formed in the step before) are done with it
+  if (ntiles > 0) issue(0, st0, kv0);
+  if (ntiles > 1) issue(1, st1, kv1);
+  if (NS == 4 && ntiles > 2) issue(2, st2, kv2);
+  if (NS == 4 && ntiles > 3) issue(3, st3, kv3);
+  // barrier once this wave's copies of every tile up to tile `need` have landed; the
+  // copies of later tiles (up to tile `last`, the last requested) stay in flight.
+  // Stores issued in between count too, so the wait may also cover some of them.
+  auto wait_tile = [&](int need, int last) {
+    const int ahead = min(ntiles - 1, last) - need;
+    if (ahead <= 0) vm_wait_barrier<0>();
+    else if (ahead == 1) vm_wait_barrier<LPT>();
+    else if (ahead == 2) vm_wait_barrier<2 * LPT>();
+    else vm_wait_barrier<3 * LPT>();
   };
-  for (int i = 0; i < NS - 1 && i < ntiles; ++i) {
-    if (i == 0) issue(0, st0, kv0);
-    else if (i == 1) issue(1, st1, kv1);
-    else issue(2, st2, kv2);
+  Acc accA, accB;
+  if (ntiles > 0) {
+    wait_tile(0, NS - 1);
+    qk_only(st0, accA);
   }
+  // tile tl: its logits are in cur; after the barrier its gradients and the next tile's
+  // logits (into nxt, from nsb) are formed, the previous tile's gradient rows stored,
+  // and tile tl+NS requested into tile tl's stage (isb)
+  auto iter = [&](int tl, int* kvc, unsigned char* xb, const Acc& cur, Acc& nxt, const unsigned char* nsb,
+                  unsigned char* isb) {
+    softmax(cur, kvc, xb);
+    wait_tile(tl + 1, tl + NS - 1);  // also: every exchange row of tile tl is written
+    if (tl > 0) store_tile(tl - 1);
+    if (tl + NS < ntiles) issue(tl + NS, isb, kvc);
+    grad_and_qk(xb, nsb, nxt, tl);  // at the last tile the logits of a stale stage are not used
+  };
   for (int tile = 0; tile < ntiles; tile += NS) {
     if constexpr (NS == 4) {
-      step(tile, st0, kv0, st3, kv3);
-      if (tile + 1 < ntiles) step(tile + 1, st1, kv1, st0, kv0);
-      if (tile + 2 < ntiles) step(tile + 2, st2, kv2, st1, kv1);
-      if (tile + 3 < ntiles) step(tile + 3, st3, kv3, st2, kv2);
+      iter(tile, kv0, xs0, accA, accB, st1, st0);
+      if (tile + 1 < ntiles) iter(tile + 1, kv1, xs1, accB, accA, st2, st1);
+      if (tile + 2 < ntiles) iter(tile + 2, kv2, xs0, accA, accB, st3, st2);
+      if (tile + 3 < ntiles) iter(tile + 3, kv3, xs1, accB, accA, st0, st3);
     } else {
-      step(tile, st0, kv0, st1, kv1);
-      if (tile + 1 < ntiles) step(tile + 1, st1, kv1, st0, kv0);
+      iter(tile, kv0, xs0, accA, accB, st1, st0);
+      if (tile + 1 < ntiles) iter(tile + 1, kv1, xs1, accB, accA, st0, st1);
     }
   }
+  if (ntiles > 0) store_tile(ntiles - 1);
 }
 
 // ---------------------------------------------------------------------------------
@@ -744,8 +904,19 @@ hipError_t run_chunks(const csa_params_t& p, MqaMode mode, DkvArgs a, const DkvW
     const int nr = (int)(rows - r0 < sh.rows ? rows - r0 : sh.rows);
     a.r0 = r0;
     a.nrows = nr;
-    if (p.H <= 16) hipLaunchKernelGGL((mqa_bwd_dkv_kernel<T, D, 1>), dim3(nr), dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((mqa_bwd_dkv_kernel<T, D, 4>), dim3(nr), dim3(256), 0, st, a);
+    // waves of 16 heads; one wave holding all 512 dims of the key-gradient operand would
+    // run out of registers, so up to 32 heads take two waves there
+    bool done = false;
+    if constexpr (D <= 256) {
+      if (p.H <= 16) {
+        hipLaunchKernelGGL((mqa_bwd_dkv_kernel<T, D, 1>), dim3(nr), dim3(64), 0, st, a);
+        done = true;
+      }
+    }
+    if (!done) {
+      if (p.H <= 32) hipLaunchKernelGGL((mqa_bwd_dkv_kernel<T, D, 2>), dim3(nr), dim3(128), 0, st, a);
+      else hipLaunchKernelGGL((mqa_bwd_dkv_kernel<T, D, 4>), dim3(nr), dim3(256), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (sh.kmax > 0) {
