@@ -52,6 +52,10 @@ def kernel_work(cfg, wl):
         "attention": (f["attention"], "flops", "mfma"),
         # attention backward, query side: QK, dP = dU.K^T and dz.K per (query, key), 6*H*D
         "bwd_dq": (1.5 * f["attention"], "flops", "mfma"),
+        # key side: QK and dP again, then the two contractions over heads that form each
+        # key's gradient, 8*H*D per (query, key) (the inverse-index sums are HBM work on
+        # top, counted in the same timed group)
+        "bwd_dkv": (2.0 * f["attention"], "flops", "mfma"),
     }
     if cfg.kind == "csa":
         work["indexer"] = (f["indexer"], "flops", "mfma")
@@ -92,6 +96,7 @@ KERNEL_SOURCES = {
     "topk": ("topk_kernel", ["topk.hip"]),
     "attention": ("sparse_mqa", ["sparse_mqa.hip"]),
     "bwd_dq": ("mqa_bwd_dq", ["mqa_bwd.hip", "mqa_bwd.hpp"]),
+    "bwd_dkv": ("mqa_bwd_dkv", ["mqa_bwd_dkv.hip", "mqa_bwd_dkv.hpp", "validate.hpp"]),
 }
 COMMON_SOURCES = ["common.hpp", "launch.hpp"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -329,7 +334,7 @@ def run_stack(args, dev) -> dict:
 
 
 def layer_line(args, cfg, ms_step: float, tot: dict, launches: dict, traffic_path, with_kl: bool,
-               with_dq: bool) -> dict:
+               with_dq: bool, with_dkv: bool = False) -> dict:
     """The JSON line of one fused layer from its measured step time and the per-kernel
     times (ms per step) and launch counts."""
     from compressed_sparse_attention_hca_amd import workloads as wl
@@ -356,6 +361,8 @@ def layer_line(args, cfg, ms_step: float, tot: dict, launches: dict, traffic_pat
         f = dict(f, total=f["total"] + work["kl_target"][0])
     if with_dq:  # and the attention backward's query side
         f = dict(f, total=f["total"] + work["bwd_dq"][0])
+    if with_dkv:  # and its key side
+        f = dict(f, total=f["total"] + work["bwd_dkv"][0])
     tokens = cfg.B * cfg.S
     value = tokens / (ms_step * 1e-3)
     tflops = f["total"] / (ms_step * 1e-3) / 1e12
@@ -365,7 +372,8 @@ def layer_line(args, cfg, ms_step: float, tot: dict, launches: dict, traffic_pat
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype_label(cfg.index_fp8),
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": cfg.name + ("+kl_target" if with_kl else "") + ("+bwd_dq" if with_dq else ""),
+        "config": {"workload": cfg.name + ("+kl_target" if with_kl else "") +
+                   ("+bwd" if with_dkv else ("+bwd_dq" if with_dq else "")),
                    "kind": cfg.kind, "B": cfg.B, "S": cfg.S, "H": cfg.H,
                    "D": cfg.D, "rope_dim": cfg.rope_dim, "ratio": cfg.ratio, "window": cfg.window,
                    "topk": cfg.topk, "idx_heads": cfg.idx_heads, "idx_dim": cfg.idx_dim,
@@ -397,6 +405,9 @@ def make_parser():
     ap.add_argument("--bwd-dq", action="store_true",
                     help="each step also runs the attention backward's query side "
                          "(csa_sparse_mqa_bwd_dq) on the step's output and a seeded dL/do")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also run the whole attention backward in each step: the forward keeps "
+                         "lse, then csa_sparse_mqa_bwd_dq and csa_sparse_mqa_bwd_dkv on a seeded dL/do")
     ap.add_argument("--kl-target", action="store_true",
                     help="CSA: each step also forms the indexer distillation target (csa_kl_target)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -472,6 +483,8 @@ def main():
         if k is not None:
             kl["ev"][k][1].record()
     dq = None
+    if args.bwd:
+        args.bwd_dq = True
     if args.bwd_dq:
         n = cfg.S // cfg.ratio
         g = torch.Generator(device=dev).manual_seed(cfg.seed + 23)
@@ -485,6 +498,18 @@ def main():
               "ev": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                      for _ in range(args.steps)]}
 
+    dkv = None
+    if args.bwd:
+        n = cfg.S // cfg.ratio
+        sk = inp.get("sinks")
+        dkv = {"lse": torch.empty((cfg.B, cfg.S, cfg.H), dtype=torch.float32, device=dev),
+               "dkv_c": None if cfg.kind == "swa" else torch.empty((cfg.B, n, cfg.D), dtype=torch.float32, device=dev),
+               "dkv_raw": torch.empty((cfg.B, cfg.S, cfg.D), dtype=torch.float32, device=dev),
+               "dsinks": None if sk is None else torch.empty((cfg.H,), dtype=torch.float32, device=dev),
+               "ws": bd.workspace(p, bd.OP_SPARSE_MQA_BWD, dev),
+               "ev": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.steps)]}
+
     def dq_step(k=None):
         if dq is None:
             return
@@ -494,10 +519,21 @@ def main():
                              dq=dq["dq"], ws=dq["ws"], sinks=inp.get("sinks"))
         if k is not None:
             dq["ev"][k][1].record()
+        if dkv is None:
+            return
+        if k is not None:
+            dkv["ev"][k][0].record()
+        bd.sparse_mqa_bwd_dkv(p, inp["q"], dq["kv_c_out"], inp["kv_raw"], dq["idx_out"], o, dkv["lse"], dq["d_o"],
+                              sinks=inp.get("sinks"), dkv_c=dkv["dkv_c"], dkv_raw=dkv["dkv_raw"],
+                              dsinks=dkv["dsinks"], ws=dkv["ws"])
+        if k is not None:
+            dkv["ev"][k][1].record()
     layer_out = {}
     for src in (kl, dq):
         if src is not None:
             layer_out = {k: src[k] for k in ("kv_c_out", "idx_out") if src[k] is not None}
+    if dkv is not None:
+        layer_out["lse_out"] = dkv["lse"]
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -536,7 +572,11 @@ def main():
     if dq is not None:  # window rotation + dQ kernel, timed together on the step's stream
         tot["bwd_dq"] = sum(a.elapsed_time(b) for a, b in dq["ev"]) / args.steps
         launches["bwd_dq"] = 1
-    out = layer_line(args, cfg, ms_step, tot, launches, traffic_path, kl is not None, dq is not None)
+    if dkv is not None:  # window rotation, per-pair kernel and the sums, timed together
+        tot["bwd_dkv"] = sum(a.elapsed_time(b) for a, b in dkv["ev"]) / args.steps
+        launches["bwd_dkv"] = 1
+    out = layer_line(args, cfg, ms_step, tot, launches, traffic_path, kl is not None, dq is not None,
+                     dkv is not None)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)

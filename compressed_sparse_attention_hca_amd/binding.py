@@ -36,7 +36,7 @@ class Params(ctypes.Structure):
 class Inputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("q", "kv_raw", "va", "ga", "vb", "gb", "bias", "q_idx", "w_idx", "k_idx",
-                 "kv_c_out", "idx_out", "n_visible_out", "sinks")]
+                 "kv_c_out", "idx_out", "n_visible_out", "sinks", "lse_out")]
 
 
 class CsaError(RuntimeError):
@@ -383,17 +383,19 @@ def _chk_layer(p: Params, inp: dict, o, kv_c_out, idx_out, n_visible_out):
     _chk(kv_c_out, "kv_c_out", (p.B, p.S // p.ratio, p.D), act, required=False)
 
 
-def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=None) -> Inputs:
+def make_inputs_struct(inp: dict, kv_c_out=None, idx_out=None, n_visible_out=None, lse_out=None) -> Inputs:
     g = inp.get
     return Inputs(q=_ptr(g("q")), kv_raw=_ptr(g("kv_raw")), va=_ptr(g("va")), ga=_ptr(g("ga")),
                   vb=_ptr(g("vb")), gb=_ptr(g("gb")), bias=_ptr(g("bias")), q_idx=_ptr(g("q_idx")),
                   w_idx=_ptr(g("w_idx")), k_idx=_ptr(g("k_idx")), kv_c_out=_ptr(kv_c_out),
-                  idx_out=_ptr(idx_out), n_visible_out=_ptr(n_visible_out), sinks=_ptr(g("sinks")))
+                  idx_out=_ptr(idx_out), n_visible_out=_ptr(n_visible_out), sinks=_ptr(g("sinks")),
+                  lse_out=_ptr(lse_out))
 
 
 def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None, idx_out=None,
-              n_visible_out=None):
-    """csa_fwd when p.overlap == 1, else hca_fwd."""
+              n_visible_out=None, lse_out=None):
+    """csa_fwd when p.overlap == 1, else hca_fwd.  lse_out: optional [B,S,H] fp32, the
+    attention's log-denominators for the key-side backward."""
     q = inp["q"]
     if o is None:
         o = torch.empty_like(q)
@@ -401,8 +403,9 @@ def layer_fwd(p: Params, inp: dict, o=None, ws=None, stream=None, kv_c_out=None,
     if ws is None:
         ws = workspace(p, op, q.device)
     _chk_layer(p, inp, o, kv_c_out, idx_out, n_visible_out)
+    _chk(lse_out, "lse_out", (p.B, p.S, p.H), torch.float32, required=False)
     _chk_ws(ws)
-    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
+    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out, lse_out)
     f = lib.csa_fwd if p.overlap else lib.hca_fwd
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream)))
     return o
@@ -451,7 +454,7 @@ class LayerTrace:
 
 
 def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, stream=None,
-                     kv_c_out=None, idx_out=None, n_visible_out=None):
+                     kv_c_out=None, idx_out=None, n_visible_out=None, lse_out=None):
     q = inp["q"]
     if o is None:
         o = torch.empty_like(q)
@@ -459,8 +462,9 @@ def layer_fwd_traced(p: Params, inp: dict, trace: LayerTrace, o=None, ws=None, s
     if ws is None:
         ws = workspace(p, op, q.device)
     _chk_layer(p, inp, o, kv_c_out, idx_out, n_visible_out)
+    _chk(lse_out, "lse_out", (p.B, p.S, p.H), torch.float32, required=False)
     _chk_ws(ws)
-    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out)
+    s = make_inputs_struct(inp, kv_c_out, idx_out, n_visible_out, lse_out)
     f = lib.csa_fwd_traced if p.overlap else lib.hca_fwd_traced
     check(f(ctypes.byref(p), ctypes.byref(s), _ptr(o), _ptr(ws), ws.numel(), _stream(stream),
             trace.handles, trace.kinds, trace.n))

@@ -400,6 +400,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
   CSA_TRY(check_optional(in->idx_out, "idx_out"));
   CSA_TRY(check_optional(in->n_visible_out, "n_visible_out"));
   CSA_TRY(check_optional(in->sinks, "sinks"));
+  CSA_TRY(check_optional(in->lse_out, "lse_out"));
   WsPlan plan;
   CSA_TRY(check_ws(p, csa_layer ? CSA_OP_CSA_FWD : CSA_OP_HCA_FWD, ws, ws_bytes, &plan));
   unsigned char* w = static_cast<unsigned char*>(ws);
@@ -424,7 +425,7 @@ static csa_status_t fused(const csa_params_t* p, const csa_inputs_t* in, void* o
     int32_t* nvis = in->n_visible_out ? in->n_visible_out : reinterpret_cast<int32_t*>(w + plan.nvis);
     CSA_TRY(run_index_topk(p, in->q_idx, in->w_idx, in->k_idx, idx, nvis, w, plan, st, tr));
   }
-  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, in->sinks, o, nullptr, st),
+  CSA_HIP(launch_sparse_mqa(*p, csa_layer ? MQA_SELECTED : MQA_DENSE, in->q, kv_c, kv_w, idx, in->sinks, o, in->lse_out, st),
           "attention launch");
   CSA_HIP(tr->mark(CSA_KERNEL_ATTENTION, st), "event record");
   return CSA_OK;

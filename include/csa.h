@@ -123,7 +123,9 @@ typedef struct {
  * The *_out pointers are optional (NULL = keep in workspace only): kv_c_out
  * [B,S/ratio,D], idx_out [B,S,topk], n_visible_out [B,S].
  * sinks [H] fp32 is optional (NULL = no sink): one softmax-sink logit per head, shared
- * by every batch and token, see csa_sparse_mqa_fwd_sink. */
+ * by every batch and token, see csa_sparse_mqa_fwd_sink.  lse_out [B,S,H] fp32 is
+ * optional (NULL = not kept): the attention's log-denominators, as
+ * csa_sparse_mqa_fwd_lse writes them, for csa_sparse_mqa_bwd_dkv. */
 typedef struct {
   const void* q;
   const void* kv_raw;
@@ -139,6 +141,7 @@ typedef struct {
   int32_t* idx_out;
   int32_t* n_visible_out;
   const float* sinks;
+  float* lse_out;
 } csa_inputs_t;
 
 /* Stages 1-2: gated pooling, RMSNorm and RoPE at pos0 + s*ratio.

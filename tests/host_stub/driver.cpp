@@ -153,6 +153,13 @@ static void bad_pointers() {
   }
   (void)base;
   EXPECT_ST(csa_fwd(&p, nullptr, L.o, ws, wsb, nullptr), CSA_ERR_INVALID_ARG);
+  {
+    csa_inputs_t in = L.in;
+    in.lse_out = (float*)((char*)buf(64) + 4);  // misaligned optional output
+    g_calls.clear();
+    EXPECT_ST(csa_fwd(&p, &in, L.o, ws, wsb, nullptr), CSA_ERR_INVALID_ARG);
+    EXPECT(g_calls.empty(), "launch after a misaligned lse_out");
+  }
   EXPECT_ST(csa_fwd(&p, &L.in, nullptr, ws, wsb, nullptr), CSA_ERR_INVALID_ARG);
   EXPECT_ST(csa_fwd(&p, &L.in, L.o, ws, wsb - 1, nullptr), CSA_ERR_WORKSPACE);
   EXPECT_ST(csa_fwd(&p, &L.in, L.o, nullptr, wsb, nullptr), CSA_ERR_INVALID_ARG);
@@ -275,6 +282,7 @@ static void run_fused(csa_params_t p, bool csa, const char* want) {
     in.kv_c_out = buf((size_t)p.B * (p.S / p.ratio) * p.D * es(p));
     in.idx_out = (int32_t*)buf((size_t)p.B * p.S * p.topk * 4);
     in.n_visible_out = (int32_t*)buf((size_t)p.B * p.S * 4);
+    in.lse_out = (float*)buf((size_t)p.B * p.S * p.H * 4);
     EXPECT_ST(csa_fwd(&p, &in, L.o, ws, wsb, nullptr), CSA_OK);
   }
   // a failing launch is reported, not ignored

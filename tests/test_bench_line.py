@@ -81,3 +81,21 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_layer_line_with_the_attention_backward():
+    """--bwd: the step runs the forward, dQ and the key side; the workload says so and
+    the step's FLOPs include both backward parts."""
+    args = _args("--bwd", "--workload", "C1")
+    cfg = wl.C1
+    tot = {"compress": 0.01, "window_rope": 0.01, "index_topk": 0.5, "attention": 0.4,
+           "bwd_dq": 0.85, "bwd_dkv": 2.1}
+    launches = {k: 1 for k in tot}
+    line = bench.layer_line(args, cfg, 3.9, tot, launches, None, False, True, True)
+    json.dumps(line)
+    assert line["config"]["workload"] == cfg.name + "+bwd"
+    work = bench.kernel_work(cfg, wl)
+    f = wl.layer_flops(cfg)["total"] + work["bwd_dq"][0] + work["bwd_dkv"][0]
+    assert line["flops_per_step"] == f
+    assert line["roofline"]["kernel"] == "bwd_dkv"
+    assert work["bwd_dkv"][0] == 2.0 * wl.layer_flops(cfg)["attention"]

@@ -237,3 +237,21 @@ def test_dkv_empty_batch_zeroes_the_sink_gradient(bd):
     bd.sparse_mqa_bwd_dkv(p, z, kv, kvr, idx, z, lse, z, sinks=sinks, dsinks=dsinks)
     torch.cuda.synchronize()
     assert torch.equal(dsinks, torch.zeros_like(dsinks))
+
+
+def test_fused_layer_keeps_the_same_lse(bd):
+    """csa_fwd with lse_out keeps the log-denominators csa_sparse_mqa_fwd_lse writes for
+    the same entries and selection, bit for bit, and the same output."""
+    cfg = wl.C1.replace(S=1024, name="dkv_fused_lse")
+    inp = gen(cfg)
+    inp["sinks"] = torch.linspace(-1.0, 1.0, cfg.H, device=DEV)
+    p = bd.params(cfg)
+    n = cfg.S // cfg.ratio
+    kv = torch.empty((cfg.B, n, cfg.D), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((cfg.B, cfg.S, cfg.topk), dtype=torch.int32, device=DEV)
+    lse = torch.empty((cfg.B, cfg.S, cfg.H), dtype=torch.float32, device=DEV)
+    o = bd.layer_fwd(p, inp, kv_c_out=kv, idx_out=idx, lse_out=lse)
+    o2, lse2 = bd.sparse_mqa_fwd_lse(p, inp["q"], kv, inp["kv_raw"], idx, sinks=inp["sinks"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    assert torch.equal(lse, lse2)
