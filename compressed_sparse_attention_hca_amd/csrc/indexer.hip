@@ -480,8 +480,11 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void index_scores_kernel(IndexArgs 
 // ring (global_load_lds), two tiles ahead of the one being multiplied.  Rows are
 // padded by 16 bytes, so the fragment reads are free of bank conflicts and their
 // addresses are one base plus immediate offsets; the DMA simply also fills the pads.
-// Each wave issues the MFMAs of its next 32-entry block next to the epilogue of the
-// previous one (branch-free), so the scoring VALU work overlaps the matrix core.
+// Each wave issues the MFMAs of its next 32-entry block next to the ReLU-weighted head
+// sums of the previous one, so the scoring VALU work overlaps the matrix core, and
+// admits a tile's two blocks in one step: the low lane half scores one block and the
+// high half the other, so the key and admission bookkeeping (branch-free) runs once
+// per 64 entries.
 // ---------------------------------------------------------------------------------
 constexpr int FT_WAVES = 8;
 constexpr int FT_TILE = 64;    // entries per LDS stage (two 32-entry MFMA blocks)
@@ -710,6 +713,8 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   constexpr int KS = DI / 16;
   constexpr int HB = 2;
   constexpr int CAP = SH::CAP;
+  // two blocks admitted per step (see admit_pair) except with fp32 query fragments
+  constexpr bool PAIR = sizeof(T) == 2 || F8;
   // three distinct arrays, so the compiler can tell a stage being read from the
   // stages that DMA writes are still in flight to
   __shared__ __attribute__((aligned(1024))) unsigned char st0[SH::STAGE];
@@ -865,27 +870,54 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   uint32_t kept_lo = 0xffffffffu, kmn_l = 0xffffffffu, kmax_l = 0u;
   int c = 0;
 
-  // ReLU(.) * w summed over the lane's 16 heads of each block (four independent
-  // partial sums), then across the two lane halves; admit into the buffer.
-  auto epilogue = [&](const f32x16* acc, int eb, float sk) {
+  // ReLU(.) * w summed over the lane's 16 heads of a block (four independent partial
+  // sums); the two lane halves hold the two 16-head halves of each entry.
+  auto partial = [&](const f32x16* acc) -> float {
     float v4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) v4[i & 3] = fmaf(w[hb][i], relu(acc[hb][i]), v4[i & 3]);
-    const float v = (v4[0] + v4[1]) + (v4[2] + v4[3]);
+    return (v4[0] + v4[1]) + (v4[2] + v4[3]);
+  };
+  // Admit two blocks at once: vlo holds the partials of entries elo + 0..31, vhi those
+  // of ehi + 0..31 (elo's block comes first in entry order).  One v_permlane32_swap
+  // gives the low lanes vlo's two halves and the high lanes vhi's, so lane l scores
+  // entry elo + l (l < 32) or ehi + l - 32 and the key and admission bookkeeping run
+  // once for 64 entries, in entry order across the lanes.
+  // One block alone (fp32 activations without fp8, whose query fragments leave no
+  // registers for the paired order): the two lane halves' sums meet in both halves
+  // and the low half admits.
+  auto admit_one = [&](float v, int eb, float sk) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if constexpr (F8) s *= sk;  // the entry's scale (sq is folded into w)
+    if constexpr (F8) s *= sk;
     const int e = eb + l32;
     const uint32_t key = score_key(s);
     const bool admit = g == 0 && e >= 0 && e < n_t && key > theta;
     const uint64_t bm = __ballot(admit);
     const int nadm = __popcll(bm);
-    // branch-free append: an admitted lane writes after the admitted lanes below it
-    // (only lanes < 32 admit, so the low half of the mask counts them); refused lanes
-    // all write the first free slot (c + 32 < CAP holds here, see make_room)
     const int pos = c + (admit ? (int)__builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u) : nadm);
+    my_key[pos] = key;
+    my_idx[pos] = e;
+    kmax_l = admit ? max(kmax_l, key) : kmax_l;
+    kmn_l = admit ? min(kmn_l, key) : kmn_l;
+    c += nadm;
+  };
+  auto admit_pair = [&](float vlo, float vhi, int elo, int ehi, float sklo, float skhi) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(vlo), __float_as_uint(vhi), false, false);
+    float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (F8) s *= g ? skhi : sklo;  // the entry's scale (sq is folded into w)
+    const int e = (g ? ehi : elo) + l32;
+    const uint32_t key = score_key(s);
+    const bool admit = e >= 0 && e < n_t && key > theta;
+    const uint64_t bm = __ballot(admit);
+    const int nadm = __popcll(bm);
+    // branch-free append: an admitted lane writes after the admitted lanes below it;
+    // refused lanes all write the first free slot (c + 64 < CAP holds here, see
+    // make_room)
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+    const int pos = c + (admit ? below : nadm);
     my_key[pos] = key;
     my_idx[pos] = e;
     kmax_l = admit ? max(kmax_l, key) : kmax_l;
@@ -928,8 +960,8 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       }
   }
 
-  // Prune when fewer than `need` + 1 slots are free (each epilogue admits up to 32
-  // keys and may write one spare slot past them), or, with `early`, once the buffer
+  // Prune when fewer than `need` + 1 slots are free (each admission step admits up to
+  // 64 keys and may write one spare slot past them), or, with `early`, once the buffer
   // is more than half way from K to full.  A prune stalls the whole workgroup at the
   // next barrier, so the waves announce an upcoming prune one tile ahead (vote) and
   // then prune together: the stalls overlap instead of adding up.
@@ -953,9 +985,10 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
 #pragma unroll
     for (int i = 0; i < 16; ++i) accB[hb][i] = 0.f;
   // One tile: wait for its stage, refill the stage read two tiles ago, then
-  // MFMA(block 0) | epilogue(block 1 of the previous tile) | MFMA(block 1) |
-  // epilogue(block 0).  Blocks past n_t are multiplied too (their rows are valid
-  // data) and refused by the epilogue's mask; at it == 0 there is no previous block.
+  // MFMA(block 0) | partial sums of block 1 of the previous tile | MFMA(block 1) |
+  // partial sums of block 0, and both blocks admitted together.  Blocks past n_t are
+  // multiplied too (their rows are valid data) and refused by the admission mask; at
+  // it == 0 there is no previous block (its entries are negative).
   if (lane == 0) vote[wave] = -2;
   auto step = [&](int it, const unsigned char* cur, unsigned char* refill) {
     if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, false>();
@@ -966,17 +999,25 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       const int4 v0 = *reinterpret_cast<const int4*>(&vote[0]);
       const int4 v1 = *reinterpret_cast<const int4*>(&vote[4]);
       const int vmax = max(max(max(v0.x, v0.y), max(v0.z, v0.w)), max(max(v1.x, v1.y), max(v1.z, v1.w)));
-      make_room(2 * 32, vmax >= it - 1);
+      make_room(64, vmax >= it - 1);
     }
     if (it + 2 < ntiles) issue(it + 2, refill);
     if (select_all) return;
     const int e0 = it * FT_TILE;
-    if constexpr (F8) mfma_block8(cur, 0, accA, skA);
-    else mfma_block(cur, 0, accA);
-    epilogue(accB, e0 - 32, skB);
-    if constexpr (F8) mfma_block8(cur, 1, accB, skB);
-    else mfma_block(cur, 1, accB);
-    epilogue(accA, e0, skA);
+    if constexpr (PAIR) {
+      if constexpr (F8) mfma_block8(cur, 0, accA, skA);
+      else mfma_block(cur, 0, accA);
+      const float vb = partial(accB);
+      const float skb = skB;
+      if constexpr (F8) mfma_block8(cur, 1, accB, skB);
+      else mfma_block(cur, 1, accB);
+      admit_pair(vb, partial(accA), e0 - 32, e0, skb, skA);
+    } else {
+      mfma_block(cur, 0, accA);
+      admit_one(partial(accB), e0 - 32, 0.f);
+      mfma_block(cur, 1, accB);
+      admit_one(partial(accA), e0, 0.f);
+    }
     // two more tiles could fill the buffer: ask every wave to prune at the next tile
     if (c > CAP - 3 * FT_TILE - 1 && lane == 0) vote[wave] = it;
   };
@@ -985,9 +1026,10 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     if (it + 1 < ntiles) step(it + 1, st1, st0);
     if (it + 2 < ntiles) step(it + 2, st2, st1);
   }
-  if (!select_all && ntiles > 0) {
-    make_room(32, false);
-    epilogue(accB, ntiles * FT_TILE - 32, skB);
+  if (!select_all && ntiles > 0) {  // block 1 of the last tile, alone (the high lanes' entries are negative)
+    make_room(64, false);
+    if constexpr (PAIR) admit_pair(partial(accB), 0.f, ntiles * FT_TILE - 32, -64, skB, 0.f);
+    else admit_one(partial(accB), ntiles * FT_TILE - 32, 0.f);
   }
 
   if (!q_ok) return;
