@@ -345,12 +345,362 @@ __global__ __launch_bounds__(256, 2) void kl_target_hd_kernel(KlArgs a) {
   for (int k = nsel + (int)threadIdx.x; k < a.topk; k += 256) orow[k] = 0.f;
 }
 
+// ---------------------------------------------------------------------------------
+// bf16 fast path for D = 512, up to 64 heads and at most 512 selected entries: one pass
+// over the keys, one workgroup per CU.  Wave w = (hg, dh) owns heads 32hg .. 32hg+31
+// and latent half dh (dims 256dh .. 256dh+255), as in the attention forward; the
+// logits are S[head, key] = Q . K^T on v_mfma_f32_32x32x16_bf16 with the rotated
+// query's head rows as A (head row r is head 32hg + (r ^ 16dh), so rows 0..15 are
+// the wave's own 16 heads) and the tile's key rows as B (key = column = lane % 32).
+// The partner waves (same hg, other dh) swap the partial sums of each other's heads
+// through LDS, so each wave ends a tile with the full logits of its own 16 heads for
+// all 32 keys: 8 per lane, keys across lanes.
+//
+// Every probability is kept until the end of the query: e = 2^(z - m_ref) with the
+// first tile's per-head maximum as the reference (shift invariance; the exact
+// maximum and a second pass take over when a later logit is more than 64 log2 units
+// away), 8 registers per tile, 128 for 512 keys.  At the end each head's sum l is
+// reduced across the lanes, and T[key] = (1/H) sum_h e[h, key] / l_h is summed over
+// the lane's 8 heads, the two lane halves (v_permlane32_swap) and the four waves (LDS).
+// So the keys are gathered and multiplied once, with no statistics pass.
+//
+// The selected rows are copied straight into a four-stage LDS ring (32 rows of 1 KB
+// per stage, chunks XOR-swizzled as in the attention forward) by assembly
+// global_load_lds copies: three tiles are in flight while one is multiplied.  One
+// barrier per tile serves as the partner exchange of tile t, the arrival of tile t+1
+// and the release of tile t's stage; tile t+1's products are issued before tile t's
+// exponentials, so the two overlap.
+// ---------------------------------------------------------------------------------
+constexpr int KLP_KT = 32;       // keys per tile
+constexpr int KLP_STAGES = 4;
+constexpr int KLP_MAX_TILES = 16;  // 512 selected entries
+
+// Reductions over the 32 lanes of each lane half (lanes 0..31 and 32..63), the result
+// in every lane of the half, with no LDS round trip: DPP swaps within quads, the
+// 8-lane and 16-lane mirrors, then v_permlane16_swap exchanges the two 16-lane rows of
+// the half (each operand copy comes back holding one row's values in both rows).
+__device__ inline float klp_dpp(float x, int ctrl) {
+  switch (ctrl) {  // the control must be an immediate
+    case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  }
+}
+template <bool MAX> __device__ inline void klp_reduce32(float (&x)[8]) {
+  constexpr int ctrl[4] = {0xB1, 0x4E, 0x141, 0x140};  // xor 1, xor 2, half-row mirror, row mirror
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = klp_dpp(x[i], ctrl[st]);
+      x[i] = MAX ? fmaxf(x[i], y) : x[i] + y;
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
+    const float a0 = __uint_as_float(r[0]), a1 = __uint_as_float(r[1]);
+    x[i] = MAX ? fmaxf(a0, a1) : a0 + a1;
+  }
+}
+// Values kept in AGPRs for the whole key loop (the probabilities of every tile), so the
+// VGPRs stay free for the fragment read-ahead.  The value usually comes straight from
+// v_exp_f32: a VALU instruction may read a transcendental's result only after one wait
+// state, and the compiler does not pad for an instruction inside inline assembly (without
+// the s_nop the write picks up the exponential's argument), so the assembly pads itself.
+__device__ inline float klp_to_agpr(float v) {
+  float a;
+  asm volatile("s_nop 1\n\tv_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+__device__ inline float klp_from_agpr(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+// Wait until at most n of this wave's vector-memory operations are outstanding, then
+// for every wave (LDS accesses completed too).
+template <int N> __device__ inline void klp_wait_barrier() {
+  static_assert(N == 0 || N == 8 || N == 16 || N == 24, "vmcnt values used by the ring");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
+  constexpr int D = 512, ROWB = 1024, KT = KLP_KT, NS = KLP_STAGES;
+  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * KT * ROWB];
+  // partner exchange, [parity][wave][lane] x 8 floats; the RoPE table borrows it
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[2 * 4 * 64 * 32];
+  __shared__ int ovf;
+  float2* cs = reinterpret_cast<float2*>(xbuf);
+
+  const int gi = a.B * a.S - 1 - (int)blockIdx.x;  // latest queries first
+  const int b = gi / a.S, t = gi % a.S;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave >> 1, dh = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n_t = visible_entries(t, a.ratio);
+  const int nsel = min(a.topk, n_t);
+  const int ntiles = (nsel + KT - 1) / KT;
+  float* orow = a.target + ((int64_t)b * a.S + t) * a.topk;
+  if (ntiles == 0) {
+    for (int k = threadIdx.x; k < a.topk; k += 256) orow[k] = 0.f;
+    return;
+  }
+  const int32_t* irow = a.idx + ((int64_t)b * a.S + t) * a.topk;
+  const unsigned char* qg = static_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
+  const unsigned char* kvb = static_cast<const unsigned char*>(a.kv_c) + (int64_t)b * a.n_entries * ROWB;
+
+  if (threadIdx.x < a.R / 2) {
+    float c, s;
+    rope_cos_sin(a.pos0 + t, rope_inv_freq(threadIdx.x, a.R, a.theta), &c, &s);
+    cs[threadIdx.x] = make_float2(c, s);
+  }
+
+  // Entry indices: lane (l32, g) holds key l32 of tile 2m + g in sidx[m] (-1 past the
+  // selection).  Every lane loads (from a clamped position), with no branch, so the
+  // loads are in flight together.
+  int sidx[KLP_MAX_TILES / 2];
+#pragma unroll
+  for (int m = 0; m < KLP_MAX_TILES / 2; ++m) sidx[m] = irow[min((2 * m + g) * KT + l32, nsel - 1)];
+#pragma unroll
+  for (int m = 0; m < KLP_MAX_TILES / 2; ++m)
+    if ((2 * m + g) * KT + l32 >= nsel) sidx[m] = -1;
+  // A operand: head row l32 is head 32hg + (l32 ^ 16dh); k-step k holds dims
+  // 256dh + 16k + 8g .. +7.  Heads past H load head H-1 (their sums are never used).
+  const int hrow = 32 * hg + (l32 ^ (16 * dh));
+  bf16x8 qf[16];
+  {
+    const unsigned char* q0 = qg + (int64_t)min(hrow, a.H - 1) * ROWB + 2 * (256 * dh + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q0 + 32 * k));
+  }
+  __syncthreads();  // the RoPE table is written; q and the indices have arrived
+  {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const int rlo = D - a.R;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int d0 = 256 * dh + 16 * k + 8 * g;
+      if (d0 + 8 > rlo) {
+        u32x4 w = __builtin_bit_cast(u32x4, qf[k]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = d0 + 2 * j;
+          if (d >= rlo) {
+            const float2 r = cs[(d - rlo) >> 1];
+            const float x0 = __uint_as_float(w[j] << 16), x1 = __uint_as_float(w[j] & 0xffff0000u);
+            const float y0 = x0 * r.x - x1 * r.y, y1 = x0 * r.y + x1 * r.x;
+            w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{y0, y1}, bf16x2_t));
+          }
+        }
+        qf[k] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+  // q and the indices have landed; the explicit wait tells the compiler so, since
+  // otherwise it keeps waits for them in the first products, and in hardware those
+  // waits would drain the copies issued after them
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding of vmcnt(0), expcnt and lgkmcnt not waited
+
+  // Row addresses of tiles 2m (lanes 0..31) and 2m+1 (lanes 32..63); an index outside
+  // 0 .. n_t-1 reads the query's own q row instead (finite data, masked out).
+  auto row_src = [&](int m, uint32_t* lo, uint32_t* hi) -> uint64_t {
+    const int s = sidx[m];
+    const bool ok = s >= 0 && s < n_t;
+    const uint64_t sp = reinterpret_cast<uint64_t>(ok ? kvb + (int64_t)s * ROWB : qg);
+    *lo = (uint32_t)sp;
+    *hi = (uint32_t)(sp >> 32);
+    return __ballot(ok);
+  };
+  const uint32_t dma_off0 = (uint32_t)(lane ^ (2 * (wave & 3))) << 4;
+  const uint32_t dma_off1 = (uint32_t)(lane ^ (2 * (wave & 3) + 1)) << 4;
+  uint32_t kmask[KLP_MAX_TILES];
+  // Copy tile `tile` into stage tile % NS: wave w copies rows w, w+4, ... (8 rows, one
+  // 1 KB wave load each); the compiler does not see these loads, so it adds no waits
+  // for them; klp_wait_barrier is the only wait.
+  auto issue = [&](int tile) {
+    uint32_t lo, hi;
+    const uint64_t bits = row_src(tile >> 1, &lo, &hi);
+    kmask[tile] = (uint32_t)(bits >> (32 * (tile & 1)));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(ring + (tile % NS) * KT * ROWB);
+#pragma unroll
+    for (int m = 0; m < KT / 4; ++m) {
+      const int r = wave + 4 * m;
+      const int src_lane = 32 * (tile & 1) + r;
+      const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, src_lane) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, src_lane);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      // s_nop 4: the row base was just written to SGPRs by v_readlane, which a vector
+      // memory instruction may read only 5 wait states later (and M0 needs 1).
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(m & 1 ? dma_off1 : dma_off0), "s"(row),
+                   "{m0}"(lds) : "memory");
+    }
+  };
+
+  // B operand reads: key row l32, chunk 32dh + 2k + g at 32dh + 8(k>>2) + ((2(k&3)+g) ^ swz)
+  int kb_base[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) kb_base[m] = l32 * ROWB + ((32 * dh + ((2 * m + g) ^ swz(l32))) << 4);
+  // The fragment reads run KA ahead of the MFMAs that consume them, pinned with
+  // scheduling groups (the compiler otherwise waits for each read just before its MFMA).
+  constexpr int KA = 3;
+  auto qk = [&](int tile) -> f32x16 {
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)(ring + (tile % NS) * KT * ROWB);
+    auto ld = [&](int k) {
+      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + kb_base[k & 3] + 128 * (k >> 2)));
+    };
+    bf16x8 kf[KA + 1];
+#pragma unroll
+    for (int k = 0; k < KA; ++k) kf[k] = ld(k);
+    f32x16 s = {};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k + KA < 16) kf[(k + KA) % (KA + 1)] = ld(k + KA);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[k], kf[k % (KA + 1)], s, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+#pragma unroll
+    for (int k = 0; k < 16 - KA; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KA, 0);
+    return s;
+  };
+  // exchange slot of (parity, wave, lane): the partner's is xo ^ 2048
+  const int xo = 2048 * wave + 32 * lane;
+  auto send = [&](int tile, const f32x16& s) {
+    CSA_LDS unsigned char* xb = (CSA_LDS unsigned char*)xbuf + 8192 * (tile & 1) + xo;
+    *(CSA_LDS f32x4*)xb = f32x4{s[8], s[9], s[10], s[11]};
+    *(CSA_LDS f32x4*)(xb + 16) = f32x4{s[12], s[13], s[14], s[15]};
+  };
+
+  const float sl2 = a.scale_log2;
+  float e[KLP_MAX_TILES][8];
+  float m_ref[8], m_seen[8], l[8];
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m_seen[i] = -INFINITY;
+      l[i] = 0.f;
+    }
+    __syncthreads();  // the exchange area (RoPE table) is free; the ring is idle
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (j < ntiles) issue(j);
+    if (ntiles > 3) klp_wait_barrier<24>();  // tile 0 landed; tiles 1..3 in flight
+    else if (ntiles == 3) klp_wait_barrier<16>();
+    else if (ntiles == 2) klp_wait_barrier<8>();
+    else klp_wait_barrier<0>();
+    f32x16 s = qk(0);
+    send(0, s);
+#pragma unroll
+    for (int tl = 0; tl < KLP_MAX_TILES; ++tl) {
+      if (tl < ntiles) {
+        // tile tl+1 landed (tiles up to tl+3 were issued); the partials of tile tl are
+        // in LDS; every wave is done reading stage tl % NS
+        const int after = min(ntiles - 1, tl + 3) - (tl + 1);
+        if (after >= 2) klp_wait_barrier<16>();
+        else if (after == 1) klp_wait_barrier<8>();
+        else klp_wait_barrier<0>();
+        if (tl + NS < ntiles) issue(tl + NS);
+        const CSA_LDS unsigned char* xr = (const CSA_LDS unsigned char*)xbuf + 8192 * (tl & 1) + (xo ^ 2048);
+        const f32x4 p0 = *(const CSA_LDS f32x4*)xr, p1 = *(const CSA_LDS f32x4*)(xr + 16);
+        __builtin_amdgcn_sched_barrier(0);  // the partner's sums are read before the fragments
+        f32x16 sn = {};
+        if (tl + 1 < ntiles) sn = qk(tl + 1);
+        float z[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[i] = s[i] + p0[i];
+          z[4 + i] = s[4 + i] + p1[i];
+        }
+        const uint32_t km = kmask[tl];
+        if (km != 0xffffffffu) {
+          const bool ok = (km >> l32) & 1u;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) z[i] = ok ? z[i] : -INFINITY;
+        }
+        if (tl == 0 && pass == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m_ref[i] = z[i];
+          klp_reduce32<true>(m_ref);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) m_ref[i] = m_ref[i] == -INFINITY ? 0.f : m_ref[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          m_seen[i] = fmaxf(m_seen[i], z[i]);
+          const float ev = __builtin_amdgcn_exp2f((z[i] - m_ref[i]) * sl2);
+          l[i] += ev;
+          e[tl][i] = klp_to_agpr(ev);
+        }
+        if (tl + 1 < ntiles) send(tl + 1, sn);
+        s = sn;
+      }
+    }
+    // a second pass with the exact maximum if some probability could have overflowed or
+    // (reference taken as 0 after an all-masked first tile) underflowed
+    bool bad = false;
+    klp_reduce32<true>(m_seen);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bad |= m_seen[i] != -INFINITY && fabsf((m_seen[i] - m_ref[i]) * sl2) > 64.0f;
+    if (threadIdx.x == 0) ovf = 0;
+    __syncthreads();
+    if (__any(bad) && lane == 0) atomicOr(&ovf, 1);
+    __syncthreads();
+    if (!ovf || pass == 1) break;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m_ref[i] = m_seen[i];
+  }
+
+  // T[key] = (1/H) sum_h e[h, key] / l_h: the lane's 8 heads, the two lane halves (the
+  // wave's 16 heads), then the four waves through LDS (the ring is idle now)
+  float inv[8];
+  klp_reduce32<false>(l);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int h = 32 * hg + ((8 * (i >> 2) + 4 * g + (i & 3)) ^ (16 * dh));
+    inv[i] = (h < a.H && l[i] > 0.f) ? 1.f / l[i] : 0.f;
+  }
+  float* part = reinterpret_cast<float*>(ring);  // [wave][512]
+#pragma unroll
+  for (int tl = 0; tl < KLP_MAX_TILES; ++tl) {
+    if (tl < ntiles) {
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v = fmaf(klp_from_agpr(e[tl][i]), inv[i], v);
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      if (g == 0) part[wave * 512 + tl * KT + l32] = v;
+    }
+  }
+  __syncthreads();
+  const float inv_h = 1.f / (float)a.H;
+  for (int k = threadIdx.x; k < a.topk; k += 256) {
+    float v = 0.f;
+    if (k < nsel) v = ((part[k] + part[512 + k]) + (part[1024 + k] + part[1536 + k])) * inv_h;
+    orow[k] = v;
+  }
+}
+
 hipError_t launch_kl_target(const csa_params_t& p, const void* q, const void* kv_c, const int32_t* idx,
                             float* target, hipStream_t st) {
   KlArgs a{q, kv_c, idx, target, p.B, p.S, p.H, p.rope_dim, p.ratio, p.topk, p.S / p.ratio,
            p.rope_theta, p.pos0, p.softmax_scale * 1.4426950408889634f};
   const int grid = p.B * p.S;
   if (grid == 0) return hipSuccess;
+  if (p.dtype == CSA_BF16 && p.D == 512 && p.topk <= KLP_MAX_TILES * KLP_KT) {
+    hipLaunchKernelGGL(kl_target_pipe_kernel, dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (p.dtype == CSA_BF16 && p.D == 512) {
     hipLaunchKernelGGL(kl_target_hd_kernel, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
