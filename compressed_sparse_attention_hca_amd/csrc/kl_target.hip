@@ -585,6 +585,9 @@ __global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
   const float sl2 = a.scale_log2;
   float e[KLP_MAX_TILES][8];
   float m_ref[8], m_seen[8], l[8];
+  bool forced = false;  // some head's reference was taken as 0 (its first tile all masked)
+  if (threadIdx.x == 0) ovf = 0;
+  float* part = reinterpret_cast<float*>(ring);  // [wave][512], once the ring is idle
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -633,7 +636,10 @@ __global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
           for (int i = 0; i < 8; ++i) m_ref[i] = z[i];
           klp_reduce32<true>(m_ref);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) m_ref[i] = m_ref[i] == -INFINITY ? 0.f : m_ref[i];
+          for (int i = 0; i < 8; ++i) {
+            forced |= m_ref[i] == -INFINITY;
+            m_ref[i] = m_ref[i] == -INFINITY ? 0.f : m_ref[i];
+          }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -646,44 +652,53 @@ __global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
         s = sn;
       }
     }
-    // a second pass with the exact maximum if some probability could have overflowed or
-    // (reference taken as 0 after an all-masked first tile) underflowed
+    // A second pass with the exact maximum is needed if some probability could have
+    // overflowed or (reference taken as 0 after an all-masked first tile) underflowed.
+    // The reference is each head's maximum over a subset of its keys, so unless it was
+    // forced to 0 only overflow is possible, and the lane's own maximum tells: no
+    // reduction across lanes.  The targets are formed before the decision (and formed
+    // again after a second pass), so one barrier serves both.
     bool bad = false;
-    klp_reduce32<true>(m_seen);
+    if (__any(forced)) {
+      float mall[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bad |= m_seen[i] != -INFINITY && fabsf((m_seen[i] - m_ref[i]) * sl2) > 64.0f;
-    if (threadIdx.x == 0) ovf = 0;
-    __syncthreads();
-    if (__any(bad) && lane == 0) atomicOr(&ovf, 1);
-    __syncthreads();
-    if (!ovf || pass == 1) break;
+      for (int i = 0; i < 8; ++i) mall[i] = m_seen[i];
+      klp_reduce32<true>(mall);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m_ref[i] = m_seen[i];
+      for (int i = 0; i < 8; ++i) bad |= mall[i] != -INFINITY && fabsf((mall[i] - m_ref[i]) * sl2) > 64.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bad |= (m_seen[i] - m_ref[i]) * sl2 > 64.0f;
+    }
+    if (pass == 0 && __any(bad) && lane == 0) ovf = 1;
+    // T[key] = (1/H) sum_h e[h, key] / l_h: the lane's 8 heads, the two lane halves (the
+    // wave's 16 heads), then the four waves through LDS (the ring is idle now)
+    float inv[8];
+    klp_reduce32<false>(l);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = 32 * hg + ((8 * (i >> 2) + 4 * g + (i & 3)) ^ (16 * dh));
+      inv[i] = (h < a.H && l[i] > 0.f) ? __builtin_amdgcn_rcpf(l[i]) : 0.f;
+    }
+#pragma unroll
+    for (int tl = 0; tl < KLP_MAX_TILES; ++tl) {
+      if (tl < ntiles) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v = fmaf(klp_from_agpr(e[tl][i]), inv[i], v);
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        if (g == 0) part[wave * 512 + tl * KT + l32] = v;
+      }
+    }
+    __syncthreads();
+    if (pass == 1 || !ovf) break;
+    klp_reduce32<true>(m_seen);  // the exact maximum
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m_ref[i] = m_seen[i] == -INFINITY ? 0.f : m_seen[i];
   }
 
-  // T[key] = (1/H) sum_h e[h, key] / l_h: the lane's 8 heads, the two lane halves (the
-  // wave's 16 heads), then the four waves through LDS (the ring is idle now)
-  float inv[8];
-  klp_reduce32<false>(l);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int h = 32 * hg + ((8 * (i >> 2) + 4 * g + (i & 3)) ^ (16 * dh));
-    inv[i] = (h < a.H && l[i] > 0.f) ? 1.f / l[i] : 0.f;
-  }
-  float* part = reinterpret_cast<float*>(ring);  // [wave][512]
-#pragma unroll
-  for (int tl = 0; tl < KLP_MAX_TILES; ++tl) {
-    if (tl < ntiles) {
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v = fmaf(klp_from_agpr(e[tl][i]), inv[i], v);
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-      v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      if (g == 0) part[wave * 512 + tl * KT + l32] = v;
-    }
-  }
-  __syncthreads();
-  const float inv_h = 1.f / (float)a.H;
+  const float inv_h = __builtin_amdgcn_rcpf((float)a.H);
   for (int k = threadIdx.x; k < a.topk; k += 256) {
     float v = 0.f;
     if (k < nsel) v = ((part[k] + part[512 + k]) + (part[1024 + k] + part[1536 + k])) * inv_h;
