@@ -462,15 +462,17 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
   // exchange area, 1 KB per wave and block: partial logits xh[q][wave][lane] at
   // 4096q + 1024 wave + 16 lane (8 KB), probabilities xp[wave][lane] at 8192 + 1024 wave
-  // + 16 lane (4 KB), per-head maxima and sums xm (1 KB); the RoPE table, the overflow
-  // flag and the sink logits borrow it outside the key loop.  A wave's own exchange
-  // slots and its partner's (wave ^ 1) differ by 1024, so two address registers cover
-  // them all.
+  // + 16 lane (4 KB), per-head maxima and sums xm (1 KB); past them the overflow flag,
+  // the sink logits [H] and the RoPE table, which the loop leaves alone (a table of
+  // more than 224 pairs borrows the start of the area and is formed again for the
+  // output).  A wave's own exchange slots and its partner's (wave ^ 1) differ by 1024,
+  // so two address registers cover them all.
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[16384];
   float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
-  float2* cs = reinterpret_cast<float2*>(xbuf);  // RoPE table outside the loop
   int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
-  float* sk = reinterpret_cast<float*>(xbuf + 14336);  // softmax-sink logits [H]
+  float* sk = reinterpret_cast<float*>(xbuf + 13568);  // softmax-sink logits [H]
+  const bool cs_kept = a.R / 2 <= 224;
+  float2* cs = reinterpret_cast<float2*>(xbuf + (cs_kept ? 14592 : 0));  // RoPE table
 
   // workgroup -> query: as sparse_mqa_kernel (32 consecutive queries per XCD visit)
   const int total = a.B * a.S;
@@ -604,6 +606,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     if (ntiles > 0) km0 = issue(0, sv0, st0);
     sv = load_idx(1);
     if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = a.sinks[threadIdx.x];
+    if (threadIdx.x == 0) *ovf = 0;
   }
   copies_barrier();  // the RoPE table and sinks are written; q and key tile 0 have landed
   rotate_q();
@@ -701,6 +704,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
       lds_barrier();
       const float m0 = fmaxf(mt, xm[wave ^ 1][lane]);
       m_ref = m0 == -INFINITY ? 0.f : m0;
+      // a reference forced to 0 may lie far above every logit: the end of the pass
+      // then takes the exact maximum and runs again
+      if (__any(m0 == -INFINITY) && lane == 0) *ovf = 1;
     }
     const float nbias = -m_ref * a.scale_log2;
     bf16x8 pm;
@@ -767,19 +773,19 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
         copies_barrier();
       }
     }
-    // the pair's maximum; run again with it as the reference if some probability could
-    // have overflowed, or (reference taken as 0 after an all-masked first tile) underflowed
+    // Run again with the pair's exact maximum as the reference if some probability could
+    // have overflowed, or (reference forced to 0 after an all-masked first tile, flagged
+    // there) underflowed.  The reference is the maximum over a subset of the head's
+    // keys, so otherwise only overflow is possible, and the lane's own maximum tells.
+    if (pass == 1) break;
+    if (__any(m_seen != -INFINITY && (m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0) *ovf = 1;
+    lds_barrier();
+    if (!*ovf) break;
     xm[wave][lane] = m_seen;
-    if (threadIdx.x == 0) *ovf = 0;
     lds_barrier();
     const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
-    const float dev = (mall - m_ref) * a.scale_log2;
-    if (__any(mall != -INFINITY && fabsf(dev) > 64.0f) && lane == 0) atomicOr(ovf, 1);
-    lds_barrier();
-    const int again = *ovf;
-    lds_barrier();
-    if (!again) break;
-    m_ref = mall;  // exact reference for the second pass
+    m_ref = mall == -INFINITY ? 0.f : mall;  // exact reference for the second pass
+    lds_barrier();  // xm is read
   }
 
   // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced
@@ -791,8 +797,10 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   if (a.sinks && h < a.H)  // the sink joins the denominator, same reference
     l_run += __builtin_amdgcn_exp2f(sk[h] * kLog2e - m_ref * a.scale_log2);
   const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  lds_barrier();
-  rope_table();
+  if (!cs_kept) {
+    lds_barrier();
+    rope_table();
+  }
   lds_barrier();
   {
     unsigned char* os = hg == 0 ? st0 : st1;
