@@ -573,14 +573,21 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
     const uint32_t bits = (uint32_t)__ballot(ok && lane < 32);
     const uint64_t sp = reinterpret_cast<uint64_t>(src);
     const uint32_t sp_lo = (uint32_t)sp, sp_hi = (uint32_t)(sp >> 32);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)sb;
 #pragma unroll
     for (int m = 0; m < KT / 4; ++m) {
       const int r = wave + 4 * m;  // swz(r) = 2 wave | (m & 1)
       const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
-      const unsigned char* gp = reinterpret_cast<const unsigned char*>(row) + (m & 1 ? dma_off1 : dma_off0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gp),
-                                       (CSA_LDS void*)(sb + r * ROWB), 16, 0, 0);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      // In assembly, so the compiler does not track the copies: it cannot tell their LDS
+      // destinations from the exchange slots and would otherwise wait for every copy in
+      // flight before each exchange write and fragment read, draining the four-stage
+      // ring; the explicit vm_wait_barrier waits are the only ones.  s_nop 4: the row
+      // base was just written to SGPRs by v_readlane, which a vector memory instruction
+      // may read only 5 wait states later (and M0 needs 1).
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"((uint32_t)(m & 1 ? dma_off1 : dma_off0)),
+                   "s"(row), "{m0}"(lds) : "memory");
     }
     return bits;
   };
@@ -634,6 +641,11 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
   lds_barrier2();
   delta += xm[wave ^ 1][lane];
   lds_barrier2();  // xm is free again
+  // q, du and o have landed (and with them the first tiles, requested before them); the
+  // explicit wait tells the compiler so: otherwise it keeps waits for the registers that
+  // the divergent head test and rotation left untouched on some path, before the first
+  // product of every tile, and in hardware those waits drain the ring
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding of vmcnt(0), expcnt and lgkmcnt not waited
 
   // Per-lane LDS offsets, as in the forward's head-group kernel.
   const int kr = l32 ^ (16 * dh);
@@ -697,6 +709,9 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
       lds_barrier2();
       const float m0 = fmaxf(mt, xm[wave ^ 1][lane]);
       m_ref = m0 == -INFINITY ? 0.f : m0;
+      // a reference forced to 0 may lie far above every logit: the end of the pass
+      // then takes the exact maximum and runs again
+      if (__any(m0 == -INFINITY) && lane == 0) *ovf = 1;
     }
     const float nbias = -m_ref * a.scale_log2;
     bf16x8 dzm;
@@ -764,17 +779,19 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
       if (tile + 2 < ntiles) iter(tile + 2, st2, km2, st3, st1, km1, false, sA, dA, sB, dB);
       if (tile + 3 < ntiles) iter(tile + 3, st3, km3, st0, st2, km2, false, sB, dB, sA, dA);
     }
+    // Run again with the pair's exact maximum as the reference if some probability could
+    // have overflowed, or (reference forced to 0 after an all-masked first tile, flagged
+    // there) underflowed.  The reference is the maximum over a subset of the head's
+    // keys, so otherwise only overflow is possible, and the lane's own maximum tells.
+    if (pass == 1) break;
+    if (__any(m_seen != -INFINITY && (m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0) *ovf = 1;
     __syncthreads();  // every wave is done with the stages and the exchange area
+    if (!*ovf) break;
     xm[wave][lane] = m_seen;
     __syncthreads();
     const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
-    const float dev = (mall - m_ref) * a.scale_log2;
-    if (__any(mall != -INFINITY && fabsf(dev) > 64.0f) && lane == 0) atomicOr(ovf, 1);
-    __syncthreads();
-    const int again = *ovf;
-    __syncthreads();
-    if (!again || pass == 1) break;
-    m_ref = mall;  // exact reference for the second pass
+    m_ref = mall == -INFINITY ? 0.f : mall;  // exact reference for the second pass
+    __syncthreads();  // xm is read
   }
 
   // ---- dq = RoPE(scale / l * acc, -P), staged by head rows, written coalesced
