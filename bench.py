@@ -95,6 +95,7 @@ KERNEL_SOURCES = {
     "index_topk": ("index_topk_kernel", ["indexer.hip"]),
     "topk": ("topk_kernel", ["topk.hip"]),
     "attention": ("sparse_mqa", ["sparse_mqa.hip"]),
+    "kl_target": ("kl_target", ["kl_target.hip"]),
     "bwd_dq": ("mqa_bwd_dq", ["mqa_bwd.hip", "mqa_bwd.hpp"]),
     "bwd_dkv": ("mqa_bwd_dkv", ["mqa_bwd_dkv.hip", "mqa_bwd_dkv.hpp", "validate.hpp"]),
 }
