@@ -619,20 +619,31 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
       }
     }
   };
+  // Every lane loads, with no branch, so all 48 loads are in flight together (a head
+  // test around them made the compiler wait for each k-step's loads before the next,
+  // sixteen memory round trips per query).  Lanes of heads past H load head H-1: their
+  // logits, probabilities and accumulator columns copy that head's, and their dq rows
+  // are never written.
+  {
+    const int64_t hrow = (int64_t)min(h, a.H - 1) * ROWB;
+    u32x4 ov[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int64_t eo = hrow + 2 * (256 * dh + 16 * k + 8 * g);
+      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + eo));
+      uf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dog + eo));
+      ov[k] = *reinterpret_cast<const u32x4*>(og + eo);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, ov[k]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) delta = fmaf((float)uf[k][i], (float)o8[i], delta);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int d0 = 256 * dh + 16 * k + 8 * g;
-    const int64_t eo = (int64_t)h * ROWB + 2 * d0;
-    if (h < a.H) {
-      qf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qg + eo));
-      uf[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dog + eo));
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(og + eo));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) delta = fmaf((float)uf[k][i], (float)ov[i], delta);
-    } else {
-      qf[k] = bf16x8{};
-      uf[k] = bf16x8{};
-    }
     rot(qf[k], d0);
     rot(uf[k], d0);
   }
