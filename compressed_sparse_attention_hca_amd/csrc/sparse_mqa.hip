@@ -449,6 +449,15 @@ __device__ inline void copies_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding of vmcnt(0), expcnt and lgkmcnt not waited
 }
 
+// The lane's index within the wave, formed by instructions the compiler cannot merge with
+// an earlier copy, so a value needed only after a long loop is formed again there instead
+// of being kept in (or spilled from) a register across it.
+__device__ inline int lane_id_fresh() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 // Scheduling groups (LLVM's AMDGPU sched_group_barrier masks): MFMA, LDS read.
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
@@ -507,7 +516,6 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
       cs[threadIdx.x] = make_float2(c, sn);
     }
   };
-  rope_table();
 
   const unsigned char* qg =
       reinterpret_cast<const unsigned char*>(a.q) + ((int64_t)b * a.S + t) * a.H * ROWB;
@@ -596,7 +604,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     }
   };
 
-  // Pass 0's first tile is requested before q, so both latencies overlap.
+  // Pass 0's first tile is requested before q, so both latencies overlap, and the RoPE
+  // table (a chain of fp64 operations in the first wave) is formed while they are in
+  // flight.
   const int ntiles = (nk + KT - 1) / KT;
   uint32_t km0 = 0u, km1 = 0u;
   int sv = 0;
@@ -605,12 +615,16 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     load_q();
     if (ntiles > 0) km0 = issue(0, sv0, st0);
     sv = load_idx(1);
-    if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = a.sinks[threadIdx.x];
+    const float skv = a.sinks && threadIdx.x < a.H ? a.sinks[threadIdx.x] : 0.f;
+    rope_table();
+    if (a.sinks && threadIdx.x < a.H) sk[threadIdx.x] = skv;
     if (threadIdx.x == 0) *ovf = 0;
   }
   copies_barrier();  // the RoPE table and sinks are written; q and key tile 0 have landed
   rotate_q();
-  lds_barrier();  // the table is read; the exchange buffer may be reused
+  // A table of more than 224 pairs sits where the loop exchanges partial logits: every
+  // wave must have read it first.
+  if (!cs_kept) lds_barrier();
 
   // Per-lane LDS offsets.  QK: lane row l32 holds key kr = l32 ^ 16dh (this wave's own
   // keys 16dh .. 16dh+15 become accumulator rows 0..15, the partner's rows 16..31);
@@ -777,59 +791,71 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     // have overflowed, or (reference forced to 0 after an all-masked first tile, flagged
     // there) underflowed.  The reference is the maximum over a subset of the head's
     // keys, so otherwise only overflow is possible, and the lane's own maximum tells.
-    if (pass == 1) break;
-    if (__any(m_seen != -INFINITY && (m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0) *ovf = 1;
+    // The pass's row sums go out with the overflow flag behind one barrier; the partner
+    // adds them unless the pass runs again.
+    xm[wave][lane] = l_run;
+    if (pass == 0 && __any(m_seen != -INFINITY && (m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0)
+      *ovf = 1;
     lds_barrier();
-    if (!*ovf) break;
-    xm[wave][lane] = m_seen;
+    if (pass == 1 || !*ovf) break;
+    xm[wave][lane] = m_seen;  // every wave takes this path, so no wave reads the row sums
     lds_barrier();
     const float mall = fmaxf(m_seen, xm[wave ^ 1][lane]);
     m_ref = mall == -INFINITY ? 0.f : mall;  // exact reference for the second pass
     lds_barrier();  // xm is read
   }
 
-  // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced
-  xm[wave][lane] = l_run;
-  lds_barrier();
-  l_run = halves_sum(l_run + xm[wave ^ 1][lane]);
-  if (a.lse && dh == 0 && g == 0 && h < a.H)
-    a.lse[((int64_t)b * a.S + t) * a.H + h] = head_lse(m_ref * a.scale_log2, l_run, a.sinks, h);
-  if (a.sinks && h < a.H)  // the sink joins the denominator, same reference
-    l_run += __builtin_amdgcn_exp2f(sk[h] * kLog2e - m_ref * a.scale_log2);
-  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced.  The lane's
+  // indices are formed again here rather than kept (or spilled) across the key loop.
+  const int ln = lane_id_fresh();
+  const int l32e = ln & 31, ge = ln >> 5, he = 32 * hg + l32e;
+  l_run = halves_sum(l_run + xm[wave ^ 1][ln]);
+  if (a.lse && dh == 0 && ge == 0 && he < a.H)
+    a.lse[((int64_t)b * a.S + t) * a.H + he] = head_lse(m_ref * a.scale_log2, l_run, a.sinks, he);
+  if (a.sinks && he < a.H)  // the sink joins the denominator, same reference
+    l_run += __builtin_amdgcn_exp2f(sk[he] * kLog2e - m_ref * a.scale_log2);
+  const float inv = l_run > 0.f ? __builtin_amdgcn_rcpf(l_run) : 0.f;
   if (!cs_kept) {
     lds_barrier();
     rope_table();
+    lds_barrier();
   }
-  lds_barrier();
   {
     unsigned char* os = hg == 0 ? st0 : st1;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < 8; ++db) {
+      // the table entries of a rotated dims block are read together: one LDS round trip
+      const bool rot = 256 * dh + 32 * db + 32 > rlo;  // wave-uniform
+      float2 r[8];
+      if (rot) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = cs[max(256 * dh + 32 * db + 8 * (e >> 1) + 4 * ge + 2 * (e & 1) - rlo, 0) >> 1];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 256 * dh + 32 * db + 8 * j + 4 * g;
+        const int d0 = 256 * dh + 32 * db + 8 * j + 4 * ge;
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = O[db][4 * j + i] * inv;
-        if (d0 >= rlo) {
+        if (rot && d0 >= rlo) {
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
-            const float2 r = cs[(d0 + i - rlo) >> 1];
+            const float2 c = r[2 * j + (i >> 1)];
             const float x0 = x[i], x1 = x[i + 1];
-            x[i] = x0 * r.x + x1 * r.y;
-            x[i + 1] = -x0 * r.y + x1 * r.x;
+            x[i] = x0 * c.x + x1 * c.y;
+            x[i + 1] = -x0 * c.y + x1 * c.x;
           }
         }
         T y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = from_f32<T>(x[i]);
-        *reinterpret_cast<uint2*>(os + off(l32, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
+        *reinterpret_cast<uint2*>(os + off(l32e, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
       }
+    }
   }
   lds_barrier();
   unsigned char* og = reinterpret_cast<unsigned char*>(a.o) + ((int64_t)b * a.S + t) * a.H * ROWB;
-  for (int c = threadIdx.x; c < a.H * (ROWB / 16); c += NT) {
+  for (int c = 64 * wave + ln; c < a.H * (ROWB / 16); c += NT) {
     const int row = c >> 6, col = (c & 63) * 16;
     *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) =
         *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + off(row & 31, col));
