@@ -531,7 +531,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   const bool gather = a.mode == MQA_SELECTED && nsel > 0;
   const int32_t* irow = gather ? a.idx + ((int64_t)b * a.S + t) * a.topk : reinterpret_cast<const int32_t*>(qg);
   const int ilast = gather ? nsel - 1 : 0;
-  auto load_idx = [&](int tile) -> int { return irow[min(tile * KT + l32, ilast)]; };
+  // The lane index inside the per-tile address arithmetic is formed afresh at each use:
+  // otherwise the compiler precomputes the first tiles' per-lane addresses at the start
+  // and spills them across the key loop (each spill a scratch store and a reload per
+  // query).
+  auto load_idx = [&](int tile) -> int { return irow[min(tile * KT + (lane_id_fresh() & 31), ilast)]; };
   // Row r = wave + 4m of a tile has swz(r) = 2 wave | (m & 1): the lane's 16-byte piece
   // of the row comes from chunk lane ^ swz(r) and lands at LDS position `lane`.
   const uint32_t dma_off0 = (uint32_t)(lane ^ (2 * (wave & 3))) << 4;
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   // returns the tile's key-validity bits.  The copies are written in assembly, so the
   // compiler adds no waits for them; copies_barrier() is the only wait.
   auto issue = [&](int tile, int sv, unsigned char* sb) -> uint32_t {
-    const int kk = tile * KT + l32;
+    const int kk = tile * KT + (lane_id_fresh() & 31);
     const unsigned char* src = qg;  // masked keys read finite data that is never used
     bool ok = false;
     if (kk < nsel) {
