@@ -182,6 +182,15 @@ __global__ __launch_bounds__(KL_WAVES * 64) void kl_target_kernel(KlArgs a) {
 // the probabilities [64 keys x 64 heads] over the tile it has finished with, and one
 // thread per key sums its row of heads.  64 KB of LDS: two workgroups per CU.
 // ---------------------------------------------------------------------------------
+// The lane's index within the wave, formed by instructions the compiler cannot merge with
+// an earlier copy (so a value needed only after the key loop is formed there instead of
+// being kept in, or spilled from, a register across the loop).
+__device__ inline int lane_id_fresh() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 __global__ __launch_bounds__(256, 2) void kl_target_hd_kernel(KlArgs a) {
   constexpr int D = 512, ROWB = 1024, KT = 64;
   __shared__ __attribute__((aligned(1024))) unsigned char tile[KT * ROWB];
@@ -192,6 +201,7 @@ __global__ __launch_bounds__(256, 2) void kl_target_hd_kernel(KlArgs a) {
   const int gi = a.B * a.S - 1 - (int)blockIdx.x;  // latest queries first
   const int b = gi / a.S, t = gi % a.S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int hg = wave >> 1, kh = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
   const int h = 32 * hg + l32;
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void kl_target_hd_kernel(KlArgs a) {
     }
     __syncthreads();  // the sums are read before the next tile lands
   }
-  for (int k = nsel + (int)threadIdx.x; k < a.topk; k += 256) orow[k] = 0.f;
+  for (int k = nsel + 64 * wave_u + lane_id_fresh(); k < a.topk; k += 256) orow[k] = 0.f;
 }
 
 // ---------------------------------------------------------------------------------
