@@ -730,7 +730,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   const int b = id / a.qblocks;
   const int qb = id % a.qblocks;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: SGPR arithmetic
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int t = qb * FT_WAVES + wave;
@@ -785,24 +785,35 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   const unsigned char* kbase =
       static_cast<const unsigned char*>(a.k_idx) + (int64_t)b * a.n_entries * SH::ROWB;
   int dma_row[SH::LPW], dma_off[SH::LPW];
+  uint32_t lane_off[SH::LPW];  // the lane's byte offset within a tile's rows
 #pragma unroll
   for (int j = 0; j < SH::LPW; ++j) {
     const int slot = (wave + j * FT_WAVES) * 64 + lane;
     const int ch = slot % SH::SPR;
     dma_row[j] = slot / SH::SPR;
     dma_off[j] = ch < SH::CPR ? ch * 16 : 0;  // a pad slot reloads chunk 0
+    lane_off[j] = (uint32_t)dma_row[j] * SH::ROWB + dma_off[j];
   }
+  // Copies of tile `tile`, written in assembly (the compiler adds no conservative waits
+  // for the LDS writes; the waits are the explicit vmcnt waits before each tile's
+  // barrier).  A tile wholly inside the visible entries takes its row base in the scalar
+  // address (scalar arithmetic) and the lane's fixed offset; the last tile clamps each
+  // row past the end to a valid one.
   auto issue = [&](int tile, unsigned char* st) {
+    const bool whole = (tile + 1) * FT_TILE <= n_blk;  // wave-uniform
+    const unsigned char* tbase = kbase + (int64_t)tile * FT_TILE * SH::ROWB;
 #pragma unroll
     for (int j = 0; j < SH::LPW; ++j) {
       const int L = wave + j * FT_WAVES;
       if (L < SH::NI) {  // wave-uniform
-        const int row = min(tile * FT_TILE + dma_row[j], n_blk - 1);  // past the end: a valid row
-        // written in assembly, so the compiler adds no conservative waits for the LDS
-        // writes; the waits are the explicit vmcnt waits before each tile's barrier
-        const uint32_t voff = (uint32_t)row * SH::ROWB + dma_off[j];
         const uint32_t lds = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(st + L * 1024);
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(kbase), "{m0}"(lds) : "memory");
+        if (whole) {
+          asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off[j]), "s"(tbase), "{m0}"(lds) : "memory");
+        } else {
+          const int row = min(tile * FT_TILE + dma_row[j], n_blk - 1);  // past the end: a valid row
+          const uint32_t voff = (uint32_t)row * SH::ROWB + dma_off[j];
+          asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(kbase), "{m0}"(lds) : "memory");
+        }
       }
     }
   };
