@@ -726,10 +726,33 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(RedArgs a, int max_seg
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   const T* src = reinterpret_cast<const T*>(a.interm);
-  for (int p = p0; p < p1; ++p) {
-    const T* row = src + (int64_t)a.list[p] * D + lane * V;
+  // The pair indices of up to 64 rows come in one load (a lane each) and go to the row
+  // loads through v_readlane, and the rows are loaded RB at a time, kept in their storage
+  // type, before they are added (in list order, as one at a time would): RB rows in
+  // flight per wave instead of one dependent index-then-row chain per row.
+  constexpr int RB = sizeof(T) == 2 ? 16 : 8;
+  for (int pb = p0; pb < p1; pb += 64) {
+    const int n = min(64, p1 - pb);
+    const int lidx = a.list[pb + min(lane, n - 1)];
+    int j = 0;
+    for (; j + RB <= n; j += RB) {
+      T r[RB][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] += to_f32(row[i]);
+      for (int u = 0; u < RB; ++u) {
+        const T* row = src + (int64_t)__builtin_amdgcn_readlane(lidx, j + u) * D + lane * V;
+#pragma unroll
+        for (int i = 0; i < V; ++i) r[u][i] = row[i];
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += to_f32(r[u][i]);
+    }
+    for (; j < n; ++j) {
+      const T* row = src + (int64_t)__builtin_amdgcn_readlane(lidx, j) * D + lane * V;
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += to_f32(row[i]);
+    }
   }
   const int ns = a.segbase[key + 1] - a.segbase[key];
   float* dst = ns == 1 ? a.dkv_c + ((int64_t)a.key_lo + key) * D : a.partial + (int64_t)seg * D;
@@ -785,10 +808,27 @@ __global__ __launch_bounds__(256) void window_reduce_kernel(WinArgs a) {
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
   const T* src = reinterpret_cast<const T*>(a.interm);
-  for (int64_t r = rlo; r < rhi; ++r) {
+  auto row_of = [&](int64_t r) -> const T* {
     const int t = (int)(r - bS);
     const int slot = a.kmax + tp - window_lo(t, a.window);
-    const T* row = src + ((r - a.r0) * a.kw + slot) * D + lane * V;
+    return src + ((r - a.r0) * a.kw + slot) * D + lane * V;
+  };
+  int64_t r = rlo;
+  for (; r + 8 <= rhi; r += 8) {  // eight rows in flight, added in row order
+    float v[8][V];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const T* row = row_of(r + u);
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[u][i] = to_f32(row[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += v[u][i];
+  }
+  for (; r < rhi; ++r) {
+    const T* row = row_of(r);
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] += to_f32(row[i]);
   }
