@@ -414,10 +414,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_mqa_kernel(MqaArgs a) {
 //     k-step 0 takes the wave's own keys, k-step 1 the partner's: keys {4g..4g+3,
 //     8+4g..8+4g+3} of that half; V^T for them comes from two transposing LDS reads.
 // Splitting the softmax halves its exponentials and VALU work per wave, for one more
-// barrier per tile.  LDS is exactly two 32 KB key stages plus a 16 KB exchange area
-// (two workgroups per CU); the RoPE table and the overflow flag borrow the exchange
-// area outside the key loop, and the key indices are read from global memory one tile
-// ahead.
+// barrier per tile.  LDS is exactly two 32.5 KB key stages (rows padded to 1040 B for
+// conflict-free reads) plus a 15 KB exchange area (two workgroups per CU); the RoPE
+// table and the overflow flag borrow the exchange area outside the key loop, and the
+// key indices are read from global memory one tile ahead.
 // ---------------------------------------------------------------------------------
 // Combine lane l with lane l ^ 32 (v_permlane32_swap: no LDS traffic, no address
 // register).  The swap yields both halves' values in every lane, in the same order in
@@ -464,24 +464,32 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   typedef bf16 T;
   constexpr int D = 512, ROWB = 1024, KT = 32, NT = 256;
-  // 16-byte chunk c of row r sits at chunk position c ^ swz(r) (see sparse_mqa_kernel)
-  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
-  auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
+  // LDS rows are padded to RP = 1040 bytes, so row r starts 4r banks (mod 64) further
+  // on, and key x of each 16-key half of a tile sits in row slot pi(x) = 4(x&3) + (x>>2)
+  // of that half.  On gfx950 a 16-byte read serves 16 lanes a cycle from 64 banks:
+  // the QK reads (16 lanes = 16 consecutive keys at one chunk) then meet 16 distinct
+  // bank quads, and the transposing PV reads (16 lanes = keys 4g..4g+3, 32 bytes each,
+  // in slots 4a+g) meet 4 disjoint 8-bank runs.  (An XOR swizzle of 3 bits left every
+  // QK read 2-way conflicted; a 4-bit one would need 8 base registers.)
+  constexpr int RP = ROWB + 16;
+  auto slot = [](int key) -> int { return (key & 16) | ((key & 3) << 2) | ((key >> 2) & 3); };
+  __shared__ __attribute__((aligned(16))) unsigned char st0[KT * RP];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[KT * RP];
   // exchange area, 1 KB per wave and block: partial logits xh[q][wave][lane] at
   // 4096q + 1024 wave + 16 lane (8 KB), probabilities xp[wave][lane] at 8192 + 1024 wave
   // + 16 lane (4 KB), per-head maxima and sums xm (1 KB); past them the overflow flag,
   // the sink logits [H] and the RoPE table, which the loop leaves alone (a table of
-  // more than 224 pairs borrows the start of the area and is formed again for the
+  // more than 192 pairs borrows the start of the area and is formed again for the
   // output).  A wave's own exchange slots and its partner's (wave ^ 1) differ by 1024,
-  // so two address registers cover them all.
-  __shared__ __attribute__((aligned(16))) unsigned char xbuf[16384];
+  // so two address registers cover them all.  Stages and exchange area fill 80 KB, so two
+  // workgroups share a CU.
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[15360];
+  static_assert(2 * KT * RP + 15360 == 80 * 1024, "two workgroups per CU");
   float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
   int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
   float* sk = reinterpret_cast<float*>(xbuf + 13568);  // softmax-sink logits [H]
-  const bool cs_kept = a.R / 2 <= 224;
-  float2* cs = reinterpret_cast<float2*>(xbuf + (cs_kept ? 14592 : 0));  // RoPE table
+  const bool cs_kept = a.R / 2 <= 192;
+  float2* cs = reinterpret_cast<float2*>(xbuf + (cs_kept ? 13824 : 0));  // RoPE table
 
   // workgroup -> query: as sparse_mqa_kernel (32 consecutive queries per XCD visit)
   const int total = a.B * a.S;
@@ -536,14 +544,13 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   // and spills them across the key loop (each spill a scratch store and a reload per
   // query).
   auto load_idx = [&](int tile) -> int { return irow[min(tile * KT + (lane_id_fresh() & 31), ilast)]; };
-  // Row r = wave + 4m of a tile has swz(r) = 2 wave | (m & 1): the lane's 16-byte piece
-  // of the row comes from chunk lane ^ swz(r) and lands at LDS position `lane`.
-  const uint32_t dma_off0 = (uint32_t)(lane ^ (2 * (wave & 3))) << 4;
-  const uint32_t dma_off1 = (uint32_t)(lane ^ (2 * (wave & 3) + 1)) << 4;
+  // The lane's 16-byte piece of a key row lands at byte 16 lane of the row's slot.
+  const uint32_t dma_off = (uint32_t)lane << 4;
   // Direct-to-LDS copy of tile `tile` (index values `sv` from load_idx): wave w loads
-  // rows w, w+4, ..., one 1 KB wave load per row (scalar row base, 32-bit lane offset);
-  // returns the tile's key-validity bits.  The copies are written in assembly, so the
-  // compiler adds no waits for them; copies_barrier() is the only wait.
+  // keys w, w+4, ..., one 1 KB wave load per key (scalar row base, 32-bit lane offset),
+  // key w + 4m into slot 16(m>>2) + 4w + (m&3); returns the tile's key-validity bits.
+  // The copies are written in assembly, so the compiler adds no waits for them;
+  // copies_barrier() is the only wait.
   auto issue = [&](int tile, int sv, unsigned char* sb) -> uint32_t {
     const int kk = tile * KT + (lane_id_fresh() & 31);
     const unsigned char* src = qg;  // masked keys read finite data that is never used
@@ -567,13 +574,12 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
       const int r = wave + 4 * m;
       const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)slot(r) * RP);
       // The row base was just written to SGPRs by v_readlane (a VALU op); a vector-memory
       // instruction may read such an SGPR only 5 wait states later, and the compiler
       // does not pad for an instruction inside inline assembly: s_nop 4 gives the 5 (and
       // the 1 that the M0 write needs before the copy).
-      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(m & 1 ? dma_off1 : dma_off0),
-                   "s"(row), "{m0}"(lds) : "memory");
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_off), "s"(row), "{m0}"(lds) : "memory");
     }
     return bits;
   };
@@ -632,24 +638,16 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
 
   // Per-lane LDS offsets.  QK: lane row l32 holds key kr = l32 ^ 16dh (this wave's own
   // keys 16dh .. 16dh+15 become accumulator rows 0..15, the partner's rows 16..31);
-  // chunk 32dh + 2k + g of key row kr sits at 32dh + 8(k>>2) + ((2(k&3) + g) ^ swz(kr)):
-  // four bases, 128(k>>2) an immediate.
+  // dims 256dh + 16k + 8g .. +7 of key kr sit at slot(kr) RP + 512dh + 16g + 32k: one
+  // base, 32k an immediate.
   const int kr = l32 ^ (16 * dh);
-  int qk_base[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) qk_base[m] = kr * ROWB + ((32 * dh + ((2 * m + g) ^ swz(kr))) << 4);
+  const int qk_base = slot(kr) * RP + 512 * dh + 16 * g;
   // PV: 16-lane group hq = lane/16 covers dims 256dh + 32db + 16(hq&1) .. +15; lane j of
-  // the group addresses key row 16kh + 4g + j/4 (and +8), dims + 4(j%4).  With
-  // a4 = j/4 the row's swizzle is 2a4 | g for every kh and for the +8 row, and the
-  // chunk position is 32dh + 8(db>>1) + 2((2(db&1) + hh) ^ a4) + (((j>>1)&1) ^ g):
-  // two bases (db even / odd); 128(db>>1), 16 KB for key half kh and 8 KB for the +8
-  // row are immediates.
+  // the group addresses key 16kh + 4g + j/4 (and +8), dims + 4(j%4).  Key 4g + a (a =
+  // j/4) of a half sits in slot 4a + g and key 8 + 4g + a in slot 4a + 2 + g: one base,
+  // 64db, 16 RP for key half kh and 2 RP for the +8 keys are immediates.
   const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
-  int pv_base[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    pv_base[m] = (4 * g + a4) * ROWB +
-                 ((32 * dh + 2 * ((2 * m + hh) ^ a4) + (((hj >> 1) & 1) ^ g)) << 4) + 8 * (hj & 1);
+  const int pv_base = (4 * a4 + g) * RP + 512 * dh + 32 * hh + 8 * (hj & 3);
   const int xo = 1024 * wave + 16 * lane;  // this wave's exchange slot (its partner's: xo ^ 1024)
   typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -673,7 +671,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)sb;
     CSA_LDS unsigned char* xb = (CSA_LDS unsigned char*)xbuf;
     auto ld_k = [&](int k) {
-      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
+      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base + 32 * k));
     };
     f32x16 s = {};
     {
@@ -745,9 +743,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     {
       auto ld_v = [&](int i) {
         const int db = i >> 1, kh = i & 1;
-        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + 16 * ROWB * (kh ^ dh);
+        const CSA_LDS unsigned char* p = lb + pv_base + 64 * db + 16 * RP * (kh ^ dh);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 2 * RP));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8 vb[VA + 1];
@@ -853,7 +851,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
         T y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = from_f32<T>(x[i]);
-        *reinterpret_cast<uint2*>(os + off(l32e, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
+        *reinterpret_cast<uint2*>(os + l32e * RP + 2 * d0) = *reinterpret_cast<const uint2*>(y);
       }
     }
   }
@@ -862,7 +860,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   for (int c = 64 * wave + ln; c < a.H * (ROWB / 16); c += NT) {
     const int row = c >> 6, col = (c & 63) * 16;
     *reinterpret_cast<uint4*>(og + (int64_t)row * ROWB + col) =
-        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + off(row & 31, col));
+        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + (row & 31) * RP + col);
   }
 }
 
