@@ -486,6 +486,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[15360];
   static_assert(2 * KT * RP + 15360 == 80 * 1024, "two workgroups per CU");
   float (*xm)[64] = reinterpret_cast<float (*)[64]>(xbuf + 12288);
+  float (*mr)[64] = reinterpret_cast<float (*)[64]>(xbuf + 4096);  // references, after the loop
   int* ovf = reinterpret_cast<int*>(xbuf + 13312);  // overflow flag
   float* sk = reinterpret_cast<float*>(xbuf + 13568);  // softmax-sink logits [H]
   const bool cs_kept = a.R / 2 <= 192;
@@ -642,12 +643,12 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   // base, 32k an immediate.
   const int kr = l32 ^ (16 * dh);
   const int qk_base = slot(kr) * RP + 512 * dh + 16 * g;
-  // PV: 16-lane group hq = lane/16 covers dims 256dh + 32db + 16(hq&1) .. +15; lane j of
+  // PV: 16-lane group hq = lane/16 covers dims 128 wave + 32db + 16(hq&1) .. +15; lane j of
   // the group addresses key 16kh + 4g + j/4 (and +8), dims + 4(j%4).  Key 4g + a (a =
   // j/4) of a half sits in slot 4a + g and key 8 + 4g + a in slot 4a + 2 + g: one base,
   // 64db, 16 RP for key half kh and 2 RP for the +8 keys are immediates.
   const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
-  const int pv_base = (4 * a4 + g) * RP + 512 * dh + 32 * hh + 8 * (hj & 3);
+  const int pv_base = (4 * a4 + g) * RP + 256 * wave + 32 * hh + 8 * (hj & 3);
   const int xo = 1024 * wave + 16 * lane;  // this wave's exchange slot (its partner's: xo ^ 1024)
   typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -736,33 +737,46 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     l_run += ls;
     *(CSA_LDS u32x4*)(xb + xo + 8192) = __builtin_bit_cast(u32x4, pm);
     lds_barrier();
-    const bf16x8 po = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(xb + (xo ^ 1024) + 8192));
-    // O^T += V^T . P^T: MFMA i = 2 db + kh reads V^T of this wave's keys (kh = 0, with
-    // pm) or the partner's (kh = 1, with po), dims block db, with two transposing reads
-    // (keys 16(kh ^ dh) + 4g + j/4 and +8)
+    // O^T[dims of quarter `wave`, heads 32hb ..] += V^T . P^T: V^T fragment (db, key
+    // half kh) feeds both head groups, so each transposing read serves two MFMAs.  The
+    // probabilities of head group hb and key half kh are wave 2hb + kh's (this wave's
+    // own read back like the others).  Step jj = 0, 1 takes key half jj ^ (wave >> 1):
+    // the accumulation order of a dims half is that of the waves that owned it whole.
+    const int kfirst = wave >> 1;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        pf[hb][jj] = __builtin_bit_cast(
+            bf16x8, *(const CSA_LDS u32x4*)(xb + 8192 + 1024 * (2 * hb + (jj ^ kfirst)) + 16 * lane));
     {
-      auto ld_v = [&](int i) {
-        const int db = i >> 1, kh = i & 1;
-        const CSA_LDS unsigned char* p = lb + pv_base + 64 * db + 16 * RP * (kh ^ dh);
+      // fragment j: dims block j & 3 of the quarter, key half (j >> 2) ^ kfirst; two
+      // transposing reads (keys 16kh + 4g + j/4 and +8)
+      auto ld_v = [&](int j) {
+        const CSA_LDS unsigned char* p = lb + pv_base + 64 * (j & 3) + 16 * RP * ((j >> 2) ^ kfirst);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 2 * RP));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8 vb[VA + 1];
 #pragma unroll
-      for (int i = 0; i < VA; ++i) vb[i] = ld_v(i);
+      for (int j = 0; j < VA; ++j) vb[j] = ld_v(j);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + VA < 16) vb[(i + VA) % (VA + 1)] = ld_v(i + VA);
-        O[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % (VA + 1)], (i & 1) ? po : pm, O[i >> 1], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        if (j + VA < 8) vb[(j + VA) % (VA + 1)] = ld_v(j + VA);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          O[4 * hb + (j & 3)] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[j % (VA + 1)], pf[hb][j >> 2], O[4 * hb + (j & 3)], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VA, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4 + 2 * VA, 0);
 #pragma unroll
-      for (int i = 0; i < 16 - VA; ++i) {
+      for (int j = 0; j < 8 - VA; ++j) {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, VA, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * VA, 0);
     }
   };
 
@@ -796,6 +810,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
     // The pass's row sums go out with the overflow flag behind one barrier; the partner
     // adds them unless the pass runs again.
     xm[wave][lane] = l_run;
+    mr[wave][lane] = m_ref;  // the epilogue normalises both head groups
     if (pass == 0 && __any(m_seen != -INFINITY && (m_seen - m_ref) * a.scale_log2 > 64.0f) && lane == 0)
       *ovf = 1;
     lds_barrier();
@@ -809,36 +824,47 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
 
   // normalise, de-rotate at -P, stage by head rows, write o[b,t] coalesced.  The lane's
   // indices are formed again here rather than kept (or spilled) across the key loop.
+  // Head h's denominator sums both lane halves of both key-half waves of its group;
+  // its reference is that group's (published with the sums).
   const int ln = lane_id_fresh();
-  const int l32e = ln & 31, ge = ln >> 5, he = 32 * hg + l32e;
-  l_run = halves_sum(l_run + xm[wave ^ 1][ln]);
-  if (a.lse && dh == 0 && ge == 0 && he < a.H)
-    a.lse[((int64_t)b * a.S + t) * a.H + he] = head_lse(m_ref * a.scale_log2, l_run, a.sinks, he);
-  if (a.sinks && he < a.H)  // the sink joins the denominator, same reference
-    l_run += __builtin_amdgcn_exp2f(sk[he] * kLog2e - m_ref * a.scale_log2);
-  const float inv = l_run > 0.f ? __builtin_amdgcn_rcpf(l_run) : 0.f;
+  const int l32e = ln & 31, ge = ln >> 5;
+  float inv[2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int he = 32 * hb + l32e;
+    const float l = halves_sum(xm[2 * hb][ln] + xm[2 * hb + 1][ln]);
+    const float mh = mr[2 * hb][ln];
+    if (a.lse && wave == hb && ge == 0 && he < a.H)
+      a.lse[((int64_t)b * a.S + t) * a.H + he] = head_lse(mh * a.scale_log2, l, a.sinks, he);
+    float lt = l;
+    if (a.sinks && he < a.H)  // the sink joins the denominator, same reference
+      lt += __builtin_amdgcn_exp2f(sk[he] * kLog2e - mh * a.scale_log2);
+    inv[hb] = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+  }
   if (!cs_kept) {
     lds_barrier();
     rope_table();
     lds_barrier();
   }
-  {
-    unsigned char* os = hg == 0 ? st0 : st1;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+  for (int hb = 0; hb < 2; ++hb) {
+    unsigned char* os = hb == 0 ? st0 : st1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int dbase = 128 * wave + 32 * db;
       // the table entries of a rotated dims block are read together: one LDS round trip
-      const bool rot = 256 * dh + 32 * db + 32 > rlo;  // wave-uniform
+      const bool rot = dbase + 32 > rlo;  // wave-uniform
       float2 r[8];
       if (rot) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = cs[max(256 * dh + 32 * db + 8 * (e >> 1) + 4 * ge + 2 * (e & 1) - rlo, 0) >> 1];
+        for (int e = 0; e < 8; ++e) r[e] = cs[max(dbase + 8 * (e >> 1) + 4 * ge + 2 * (e & 1) - rlo, 0) >> 1];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 256 * dh + 32 * db + 8 * j + 4 * ge;
+        const int d0 = dbase + 8 * j + 4 * ge;
         float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = O[db][4 * j + i] * inv;
+        for (int i = 0; i < 4; ++i) x[i] = O[4 * hb + db][4 * j + i] * inv[hb];
         if (rot && d0 >= rlo) {
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
