@@ -723,7 +723,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   __shared__ __attribute__((aligned(16))) uint32_t ckey[FT_WAVES][CAP];
   __shared__ __attribute__((aligned(16))) int cidx[FT_WAVES][CAP];
   __shared__ __attribute__((aligned(16))) int hist[FT_WAVES][256];
-  __shared__ __attribute__((aligned(16))) int vote[FT_WAVES];  // last tile a wave asked for a prune
+  __shared__ int vote;  // latest tile at which some wave asked for a prune (LDS max)
 
   // latest (heaviest) query blocks first
   const int id = a.B * a.qblocks - 1 - (int)blockIdx.x;
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   // Prune when fewer than `need` + 1 slots are free (each admission step admits up to
   // 64 keys and may write one spare slot past them), or, with `early`, once the buffer
   // is more than half way from K to full.  A prune stalls the whole workgroup at the
-  // next barrier, so the waves announce an upcoming prune one tile ahead (vote) and
+  // next barrier, so the waves announce an upcoming prune two tiles ahead (vote) and
   // then prune together: the stalls overlap instead of adding up.
   constexpr int PRUNE_EARLY = (FT_MAXK + CAP) / 2;
   auto make_room = [&](int need, bool early) {
@@ -1000,20 +1000,21 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   // partial sums of block 0, and both blocks admitted together.  Blocks past n_t are
   // multiplied too (their rows are valid data) and refused by the admission mask; at
   // it == 0 there is no previous block (its entries are negative).
-  if (lane == 0) vote[wave] = -2;
+  // The votes are read after a tile's barrier and acted on at the next tile, so the
+  // read's latency hides behind this tile's copies and products: a vote cast at the end
+  // of tile it-1 prunes every wave at tile it+1.
+  if (threadIdx.x == 0) vote = -4;
+  int vseen = -4;
   auto step = [&](int it, const unsigned char* cur, unsigned char* refill) {
     if (it + 1 < ntiles) wait_vmcnt<SH::NI / FT_WAVES, false>();
     else wait_vmcnt<0, false>();
     lds_only_barrier();
-    if (!select_all) {  // prune before the refill is issued: the prune's LDS atomics wait
-                        // for every copy in flight, and the older one has likely landed
-      const int4 v0 = *reinterpret_cast<const int4*>(&vote[0]);
-      const int4 v1 = *reinterpret_cast<const int4*>(&vote[4]);
-      const int vmax = max(max(max(v0.x, v0.y), max(v0.z, v0.w)), max(max(v1.x, v1.y), max(v1.z, v1.w)));
-      make_room(64, vmax >= it - 1);
-    }
+    // prune before the refill is issued: the prune's LDS atomics wait for every copy in
+    // flight, and the older one has likely landed
+    if (!select_all) make_room(64, vseen >= it - 2);
     if (it + 2 < ntiles) issue(it + 2, refill);
     if (select_all) return;
+    const int vnow = vote;
     const int e0 = it * FT_TILE;
     if constexpr (PAIR) {
       if constexpr (F8) mfma_block8(cur, 0, accA, skA);
@@ -1029,8 +1030,9 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       mfma_block(cur, 1, accB);
       admit_one(partial(accA), e0, 0.f);
     }
-    // two more tiles could fill the buffer: ask every wave to prune at the next tile
-    if (c > CAP - 3 * FT_TILE - 1 && lane == 0) vote[wave] = it;
+    vseen = vnow;
+    // three more tiles could fill the buffer: ask every wave to prune (two tiles on)
+    if (c > CAP - 4 * FT_TILE - 1 && lane == 0) atomicMax(&vote, it);
   };
   for (int it = 0; it < ntiles; it += 3) {
     step(it, st0, st2);
