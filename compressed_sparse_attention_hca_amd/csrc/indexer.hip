@@ -526,27 +526,37 @@ __device__ inline uint32_t score_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+// Wave-wide scan and reductions without LDS round trips.  Exclusive prefix sum:
+// Hillis-Steele steps over row_shr 1, 2, 4, 8 within each 16-lane row (lanes with no
+// source add 0), then the last lane of row 0 / 2 is broadcast into rows 1 / 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).
 __device__ inline int wave_excl_scan(int v) {
-  const int lane = threadIdx.x & 63;
   int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return x - v;
 }
 
-__device__ inline uint32_t wave_min(uint32_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m, 64));
-  return x;
+// Minimum / maximum over the wave, in every lane: DPP swaps within quads, the 8-lane
+// and 16-lane mirrors, then v_permlane16_swap (row pairs) and v_permlane32_swap (halves).
+template <bool MAX>
+__device__ inline uint32_t wave_minmax(uint32_t x) {
+  auto f = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  x = f(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // quad xor 1
+  x = f(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad xor 2
+  x = f(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));  // half-row mirror
+  x = f(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));  // row mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = f(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return f(r32[0], r32[1]);
 }
-__device__ inline uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, m, 64));
-  return x;
-}
+__device__ inline uint32_t wave_min(uint32_t x) { return wave_minmax<false>(x); }
+__device__ inline uint32_t wave_max(uint32_t x) { return wave_minmax<true>(x); }
 
 #define CSA_WAVE_FENCE() __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront")
 
@@ -575,13 +585,14 @@ struct Pruned {
 // the prefix of the k-th largest key.  EXACT keeps exactly the top K by (key desc,
 // buffer position asc); otherwise the wave may stop as soon as the keys at or above
 // the current prefix number at most `target` (>= K), and keeps all of them.
-// Lane l handles buffer positions 4(l + 64j) .. +3 (one 16-byte LDS access each for
-// keys and indices, made only when the first of them is below c; the buffers are
-// 16-byte aligned and their capacity is a multiple of 4, so such an access stays in
-// the buffer).  Positions >= c are ignored.
+// Lane l handles buffer positions 4(l + 64j) .. +3 of batch j (one 16-byte LDS access
+// each for keys and indices, made only when the first of them is below c; the buffers
+// are 16-byte aligned and their capacity is a multiple of 4, so such an access stays in
+// the buffer).  Positions >= c are ignored.  Each batch's reads are issued one batch
+// ahead, so their latency overlaps the previous batch's atomics or stores.
 template <bool EXACT>
-__device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K, int target,
-                              uint32_t kmin, uint32_t kmax) {
+__device__ __forceinline__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K, int target,
+                                              uint32_t kmin, uint32_t kmax) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const uint32_t diff = kmin ^ kmax;
@@ -591,17 +602,18 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
   uint32_t pbits = kmin & hmask;
   int rem = K;           // slots left among keys matching the decided bits
   bool keep_eq = false;  // keep every matching key (no tie cut needed)
-  const int nb = (c + 255) >> 8;  // 256-key batches
+  const int nb = (c + 255) >> 8;  // 256-key batches (wave-uniform)
   while (shift > 0) {
     const int w = shift >= 8 ? 8 : shift;
     const int lo = shift - w;
     const uint32_t dmask = (1u << w) - 1u;
     *reinterpret_cast<int4*>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
     CSA_WAVE_FENCE();
+    uint4 kn = 4 * lane < c ? *reinterpret_cast<const uint4*>(&ckey[4 * lane]) : make_uint4(0, 0, 0, 0);
     for (int jb = 0; jb < nb; ++jb) {
       const int base = 4 * (lane + 64 * jb);
-      const uint4 k4 = base < c ? *reinterpret_cast<const uint4*>(&ckey[base]) : make_uint4(0, 0, 0, 0);
-      const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      const uint32_t kk[4] = {kn.x, kn.y, kn.z, kn.w};
+      if (base + 256 < c) kn = *reinterpret_cast<const uint4*>(&ckey[base + 256]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool m = base + u < c && (kk[u] & hmask) == pbits;
@@ -625,10 +637,10 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
       above += cnt[j];
     }
     const uint64_t who = __ballot(sel >= 0);
-    const int src = __ffsll((unsigned long long)who) - 1;
-    sel = __shfl(sel, src, 64);
-    sel_above = __shfl(sel_above, src, 64);
-    sel_cnt = __shfl(sel_cnt, src, 64);
+    const int src = __ffsll((unsigned long long)who) - 1;  // wave-uniform
+    sel = __builtin_amdgcn_readlane(sel, src);
+    sel_above = __builtin_amdgcn_readlane(sel_above, src);
+    sel_cnt = __builtin_amdgcn_readlane(sel_cnt, src);
     rem -= sel_above;
     pbits |= (uint32_t)sel << lo;
     hmask = ~0u << lo;
@@ -641,19 +653,25 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
     }
   }
   if (shift == 0) hmask = ~0u;
-  // stable in-place compaction; track the smallest kept key
+  // stable in-place compaction; track the smallest kept key.  A batch's kept entries
+  // land below the batch's end, so the next batch, read before they are stored, is
+  // still intact.
   int out = 0, eq_seen = 0;
   uint32_t nmin = 0xffffffffu;
+  uint4 kn = make_uint4(0, 0, 0, 0);
+  int4 in4 = make_int4(0, 0, 0, 0);
+  if (4 * lane < c) {
+    kn = *reinterpret_cast<const uint4*>(&ckey[4 * lane]);
+    in4 = *reinterpret_cast<const int4*>(&cidx[4 * lane]);
+  }
   for (int jb = 0; jb < nb; ++jb) {
     const int base = 4 * (lane + 64 * jb);
-    uint4 k4 = make_uint4(0, 0, 0, 0);
-    int4 i4 = make_int4(0, 0, 0, 0);
-    if (base < c) {
-      k4 = *reinterpret_cast<const uint4*>(&ckey[base]);
-      i4 = *reinterpret_cast<const int4*>(&cidx[base]);
+    const uint32_t kk[4] = {kn.x, kn.y, kn.z, kn.w};
+    const int ii[4] = {in4.x, in4.y, in4.z, in4.w};
+    if (base + 256 < c) {
+      kn = *reinterpret_cast<const uint4*>(&ckey[base + 256]);
+      in4 = *reinterpret_cast<const int4*>(&cidx[base + 256]);
     }
-    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
-    const int ii[4] = {i4.x, i4.y, i4.z, i4.w};
     bool gt[4], eq[4];
     uint64_t be[4];
 #pragma unroll
@@ -679,7 +697,6 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
     int pos = out;
 #pragma unroll
     for (int u = 0; u < 4; ++u) pos += __popcll(bk[u] & lt);
-    CSA_WAVE_FENCE();  // all reads of this batch precede the writes below
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (keep[u]) {
@@ -694,8 +711,8 @@ __device__ Pruned wave_select(uint32_t* ckey, int* cidx, int* hist, int c, int K
       out += __popcll(bk[u]);
       eq_seen += __popcll(be[u]);
     }
-    CSA_WAVE_FENCE();
   }
+  CSA_WAVE_FENCE();
   Pruned r;
   r.c = out;
   // keep_eq: every kept key is >= pbits and at least K of them are kept, so a later key
@@ -776,7 +793,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
     const float* wrow = wave_uniform(a.w_idx + ((int64_t)b * a.S + min(t, a.S - 1)) * a.HI);
     const uint32_t voff = (uint32_t)min(lane, a.HI - 1) * 4u;
     const uint32_t lds = (uint32_t)(uintptr_t)(CSA_LDS int*)cidx[wave];
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(wrow), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(wrow), "{m0}"(lds) : "memory");
   }
 
   // Stage layout: row r at r * ROWP, chunk c of the row at slot r * SPR + c; the DMA
@@ -796,9 +813,12 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   }
   // Copies of tile `tile`, written in assembly (the compiler adds no conservative waits
   // for the LDS writes; the waits are the explicit vmcnt waits before each tile's
-  // barrier).  A tile wholly inside the visible entries takes its row base in the scalar
-  // address (scalar arithmetic) and the lane's fixed offset; the last tile clamps each
-  // row past the end to a valid one.
+  // barrier).  A vector-memory instruction may read an SGPR only 5 wait states after a
+  // VALU instruction wrote it (v_readfirstlane, or v_readlane restoring a spilled SGPR),
+  // and the compiler pads for its own instructions but not for assembly: s_nop 4.  A
+  // tile wholly inside the visible entries takes its row base in the scalar address
+  // (scalar arithmetic) and the lane's fixed offset; the last tile clamps each row past
+  // the end to a valid one.
   auto issue = [&](int tile, unsigned char* st) {
     const bool whole = (tile + 1) * FT_TILE <= n_blk;  // wave-uniform
     const unsigned char* tbase = kbase + (int64_t)tile * FT_TILE * SH::ROWB;
@@ -808,11 +828,11 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
       if (L < SH::NI) {  // wave-uniform
         const uint32_t lds = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(st + L * 1024);
         if (whole) {
-          asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off[j]), "s"(tbase), "{m0}"(lds) : "memory");
+          asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off[j]), "s"(tbase), "{m0}"(lds) : "memory");
         } else {
           const int row = min(tile * FT_TILE + dma_row[j], n_blk - 1);  // past the end: a valid row
           const uint32_t voff = (uint32_t)row * SH::ROWB + dma_off[j];
-          asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(kbase), "{m0}"(lds) : "memory");
+          asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(kbase), "{m0}"(lds) : "memory");
         }
       }
     }
@@ -977,7 +997,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void index_topk_kernel(IndexTopkArgs
   // next barrier, so the waves announce an upcoming prune two tiles ahead (vote) and
   // then prune together: the stalls overlap instead of adding up.
   constexpr int PRUNE_EARLY = (FT_MAXK + CAP) / 2;
-  auto make_room = [&](int need, bool early) {
+  auto make_room = [&](int need, bool early) __attribute__((always_inline)) {
     if (c > CAP - need - 1 || (early && c > max(K, PRUNE_EARLY))) {
       CSA_WAVE_FENCE();
       const Pruned pr = wave_select<false>(my_key, my_idx, my_hist, c, K, (K + CAP) / 2,
