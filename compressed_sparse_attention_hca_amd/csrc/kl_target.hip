@@ -441,8 +441,12 @@ template <int N> __device__ inline void klp_wait_barrier() {
 
 __global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
   constexpr int D = 512, ROWB = 1024, KT = KLP_KT, NS = KLP_STAGES;
-  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * KT * ROWB];
+  // Key rows padded to RP = 1040 bytes and key x of each 16-key half in row slot
+  // 4(x&3) + (x>>2): the 16-byte B-operand reads (16 lanes = 16 consecutive keys at one
+  // chunk) then meet 16 distinct bank groups of gfx950's 64 banks.
+  constexpr int RP = ROWB + 16, STG = KT * RP;
+  auto slot = [](int key) -> int { return (key & 16) | ((key & 3) << 2) | ((key >> 2) & 3); };
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS * STG];
   // partner exchange, [parity][wave][lane] x 8 floats; the RoPE table borrows it
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[2 * 4 * 64 * 32];
   __shared__ int ovf;
@@ -529,42 +533,39 @@ __global__ __launch_bounds__(256, 1) void kl_target_pipe_kernel(KlArgs a) {
     *hi = (uint32_t)(sp >> 32);
     return __ballot(ok);
   };
-  const uint32_t dma_off0 = (uint32_t)(lane ^ (2 * (wave & 3))) << 4;
-  const uint32_t dma_off1 = (uint32_t)(lane ^ (2 * (wave & 3) + 1)) << 4;
+  const uint32_t dma_off = (uint32_t)lane << 4;
   uint32_t kmask[KLP_MAX_TILES];
-  // Copy tile `tile` into stage tile % NS: wave w copies rows w, w+4, ... (8 rows, one
-  // 1 KB wave load each); the compiler does not see these loads, so it adds no waits
-  // for them; klp_wait_barrier is the only wait.
+  // Copy tile `tile` into stage tile % NS: wave w copies keys w, w+4, ... (8 rows, one
+  // 1 KB wave load each; key w + 4m into slot 16(m>>2) + 4w + (m&3)); the compiler does
+  // not see these loads, so it adds no waits for them; klp_wait_barrier is the only
+  // wait.
   auto issue = [&](int tile) {
     uint32_t lo, hi;
     const uint64_t bits = row_src(tile >> 1, &lo, &hi);
     kmask[tile] = (uint32_t)(bits >> (32 * (tile & 1)));
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(ring + (tile % NS) * KT * ROWB);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)(ring + (tile % NS) * STG);
 #pragma unroll
     for (int m = 0; m < KT / 4; ++m) {
       const int r = wave + 4 * m;
       const int src_lane = 32 * (tile & 1) + r;
       const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, src_lane) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)lo, src_lane);
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)slot(r) * RP);
       // s_nop 4: the row base was just written to SGPRs by v_readlane, which a vector
       // memory instruction may read only 5 wait states later (and M0 needs 1).
-      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(m & 1 ? dma_off1 : dma_off0), "s"(row),
-                   "{m0}"(lds) : "memory");
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_off), "s"(row), "{m0}"(lds) : "memory");
     }
   };
 
-  // B operand reads: key row l32, chunk 32dh + 2k + g at 32dh + 8(k>>2) + ((2(k&3)+g) ^ swz)
-  int kb_base[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) kb_base[m] = l32 * ROWB + ((32 * dh + ((2 * m + g) ^ swz(l32))) << 4);
+  // B operand reads: key l32, dims 256dh + 16k + 8g .. +7 at slot(l32) RP + 512dh + 16g + 32k
+  const int kb_base = slot(l32) * RP + 512 * dh + 16 * g;
   // The fragment reads run KA ahead of the MFMAs that consume them, pinned with
   // scheduling groups (the compiler otherwise waits for each read just before its MFMA).
   constexpr int KA = 3;
   auto qk = [&](int tile) -> f32x16 {
-    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)(ring + (tile % NS) * KT * ROWB);
+    const CSA_LDS unsigned char* lb = (const CSA_LDS unsigned char*)(ring + (tile % NS) * STG);
     auto ld = [&](int k) {
-      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + kb_base[k & 3] + 128 * (k >> 2)));
+      return __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + kb_base + 32 * k));
     };
     bf16x8 kf[KA + 1];
 #pragma unroll

@@ -490,12 +490,15 @@ __device__ inline void lds_barrier2() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_
 
 __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
   constexpr int D = 512, ROWB = 1024, KT = 32, NT = 256, LPT = 8;
-  auto swz = [](int r) -> int { return ((r & 3) << 1) | ((r >> 2) & 1); };
-  auto off = [&](int r, int byte) -> int { return r * ROWB + ((((byte >> 4) ^ swz(r)) << 4) | (byte & 15)); };
-  __shared__ __attribute__((aligned(1024))) unsigned char st0[KT * ROWB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st1[KT * ROWB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st2[KT * ROWB];
-  __shared__ __attribute__((aligned(1024))) unsigned char st3[KT * ROWB];
+  // Key rows padded to RP = 1040 bytes and key x of each 16-key half in row slot
+  // 4(x&3) + (x>>2), as in the forward's head-group kernel: the 16-byte K reads and the
+  // transposing reads are then free of bank conflicts on gfx950's 64 banks.
+  constexpr int RP = ROWB + 16;
+  auto slot = [](int key) -> int { return (key & 16) | ((key & 3) << 2) | ((key >> 2) & 3); };
+  __shared__ __attribute__((aligned(16))) unsigned char st0[KT * RP];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[KT * RP];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[KT * RP];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[KT * RP];
   // exchange: partial logits xh (8 KB), partial dP xd (8 KB), dz xp (4 KB), per-head
   // values xm (1 KB); then the RoPE table, the sink logits and the overflow flag
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[22304];
@@ -552,10 +555,10 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
   const unsigned char* kv_w = reinterpret_cast<const unsigned char*>(a.kv_w);
   __syncthreads();  // table, sinks, indices and flag are in LDS
 
-  const int dma_off0 = (lane ^ (2 * (wave & 3))) << 4, dma_off1 = (lane ^ (2 * (wave & 3) + 1)) << 4;
+  const uint32_t dma_off = (uint32_t)lane << 4;
   // Direct-to-LDS copy of tile `tile`: lane l < 32 resolves key tile*32 + l, wave w
-  // loads rows w, w+4, ... (one 1 KB wave load per row, LPT per wave); returns the
-  // tile's key-validity bits.
+  // loads keys w, w+4, ... (one 1 KB wave load per key, LPT per wave; key w + 4m into
+  // slot 16(m>>2) + 4w + (m&3)); returns the tile's key-validity bits.
   auto issue = [&](int tile, unsigned char* sb) -> uint32_t {
     const int kk = tile * KT + l32;
     const unsigned char* src = qg;  // masked keys read finite data that is never used
@@ -576,18 +579,17 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(CSA_LDS unsigned char*)sb;
 #pragma unroll
     for (int m = 0; m < KT / 4; ++m) {
-      const int r = wave + 4 * m;  // swz(r) = 2 wave | (m & 1)
+      const int r = wave + 4 * m;
       const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sp_hi, r) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane((int)sp_lo, r);
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)r * ROWB);
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)slot(r) * RP);
       // In assembly, so the compiler does not track the copies: it cannot tell their LDS
       // destinations from the exchange slots and would otherwise wait for every copy in
       // flight before each exchange write and fragment read, draining the four-stage
       // ring; the explicit vm_wait_barrier waits are the only ones.  s_nop 4: the row
       // base was just written to SGPRs by v_readlane, which a vector memory instruction
       // may read only 5 wait states later (and M0 needs 1).
-      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"((uint32_t)(m & 1 ? dma_off1 : dma_off0)),
-                   "s"(row), "{m0}"(lds) : "memory");
+      asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_off), "s"(row), "{m0}"(lds) : "memory");
     }
     return bits;
   };
@@ -660,17 +662,13 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
 
   // Per-lane LDS offsets, as in the forward's head-group kernel.
   const int kr = l32 ^ (16 * dh);
-  int qk_base[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) qk_base[m] = kr * ROWB + ((32 * dh + ((2 * m + g) ^ swz(kr))) << 4);
+  const int qk_base = slot(kr) * RP + 512 * dh + 16 * g;  // + 32k for k-step k
+  // transposing reads: key 4g + a4 of a half in slot 4a4 + g, key 8 + 4g + a4 in slot
+  // 4a4 + 2 + g; dims 256dh + 32db + 16hh + 4(hj&3)
   const int hj = lane & 15, hh = (lane >> 4) & 1, a4 = hj >> 2;
-  int pv_base[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-    pv_base[m] = (4 * g + a4) * ROWB +
-                 ((32 * dh + 2 * ((2 * m + hh) ^ a4) + (((hj >> 1) & 1) ^ g)) << 4) + 8 * (hj & 1);
+  const int pv_base = (4 * a4 + g) * RP + 512 * dh + 32 * hh + 8 * (hj & 3);
   typedef short i16x4 __attribute__((ext_vector_type(4)));
-  const int pv_mine = 16 * ROWB * dh, pv_other = 16 * ROWB * (dh ^ 1);
+  const int pv_mine = 16 * RP * dh, pv_other = 16 * RP * (dh ^ 1);
 
   float m_seen = -INFINITY, m_ref = -INFINITY, l_run = 0.f;
   f32x16 O[8];
@@ -682,7 +680,7 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
     dp = f32x16{};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base[k & 3] + 128 * (k >> 2)));
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const CSA_LDS u32x4*)(lb + qk_base + 32 * k));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[k], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, uf[k], dp, 0, 0, 0);
     }
@@ -741,9 +739,9 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const CSA_LDS unsigned char* p = lb + pv_base[db & 1] + 128 * (db >> 1) + (ks ? pv_other : pv_mine);
+        const CSA_LDS unsigned char* p = lb + pv_base + 64 * db + (ks ? pv_other : pv_mine);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 8 * ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CSA_LDS i16x4*)(p + 2 * RP));
         const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ks ? dzo : dzm, O[db], 0, 0, 0);
       }
@@ -833,7 +831,7 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
         bf16 y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = (bf16)x[i];
-        *reinterpret_cast<uint2*>(os + off(l32, 2 * d0)) = *reinterpret_cast<const uint2*>(y);
+        *reinterpret_cast<uint2*>(os + l32 * RP + 2 * d0) = *reinterpret_cast<const uint2*>(y);
       }
   }
   __syncthreads();
@@ -841,7 +839,7 @@ __global__ __launch_bounds__(256, 1) void mqa_bwd_dq_hd_kernel(DqArgs a) {
   for (int c = threadIdx.x; c < a.H * (ROWB / 16); c += NT) {
     const int row = c >> 6, col = (c & 63) * 16;
     *reinterpret_cast<uint4*>(dqg + (int64_t)row * ROWB + col) =
-        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + off(row & 31, col));
+        *reinterpret_cast<const uint4*>((row < 32 ? st0 : st1) + (row & 31) * RP + col);
   }
 }
 
