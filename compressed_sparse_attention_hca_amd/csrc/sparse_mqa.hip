@@ -622,9 +622,20 @@ __global__ __launch_bounds__(256, 2) void sparse_mqa_hd_kernel(MqaArgs a) {
   uint32_t km0 = 0u, km1 = 0u;
   int sv = 0;
   {
-    const int sv0 = load_idx(0);
-    load_q();
-    if (ntiles > 0) km0 = issue(0, sv0, st0);
+    // Without a gather the first copies need no index: they are issued without waiting
+    // for one (the dense and window-only layers then pay one memory latency per query
+    // before their first tile instead of two).
+    if (gather) {
+      // The index load goes out first (the empty asm keeps the compiler from moving the
+      // q loads ahead of it), so the copies wait for it alone, not for q as well.
+      const int sv0 = load_idx(0);
+      asm volatile("" ::: "memory");
+      load_q();
+      if (ntiles > 0) km0 = issue(0, sv0, st0);
+    } else {
+      load_q();
+      if (ntiles > 0) km0 = issue(0, 0, st0);
+    }
     sv = load_idx(1);
     const float skv = a.sinks && threadIdx.x < a.H ? a.sinks[threadIdx.x] : 0.f;
     rope_table();
