@@ -99,7 +99,7 @@ __device__ inline float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.
 template <typename T, int WPE>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform
   const int total = a.B * a.n_entries;
   const int e = (WPE == 1) ? (int)blockIdx.x * 4 + wave : (int)blockIdx.x;
   const bool entry_ok = e < total;
@@ -126,25 +126,25 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 
   if (WPE == 1 && span == 8) {
     // 8 slots (CSA at ratio 4): every load is issued first, then a two-pass softmax
-    // per channel (one exponential per slot instead of the online form's two)
+    // per channel (one exponential per slot instead of the online form's two).  The
+    // loads take no branch, so all of them are in flight together instead of one slot
+    // at a time: a slot before token 0 (CSA entry 0's missing previous group) reads
+    // token 0 and gets logit -inf, i.e. weight exactly 0 (its finite values then add 0;
+    // they are left unmasked, or the compiler would skip, and branch around, their load).
     if (lane_ok) {
       float lg[8][8], v[8][8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int tok = a.overlap ? s * r - r + j : s * r + j;  // wave-uniform
-        if (tok >= 0) {
-          const bool prev = a.overlap && j < r;
-          const int64_t off = ((int64_t)b * a.S + tok) * a.D + c0;
-          float g[8], bias[8];
-          load8<T>((prev ? gb : ga) + off, g);
-          load8<T>((prev ? vb : va) + off, v[j]);
-          load8<float>(a.bias + (int64_t)j * a.D + c0, bias);
+        const bool prev = a.overlap && j < r;
+        const int64_t off = ((int64_t)b * a.S + max(tok, 0)) * a.D + c0;
+        const float pen = tok >= 0 ? 0.f : -INFINITY;
+        float g[8], bias[8];
+        load8<T>((prev ? gb : ga) + off, g);
+        load8<T>((prev ? vb : va) + off, v[j]);
+        load8<float>(a.bias + (int64_t)j * a.D + c0, bias);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) lg[j][i] = g[i] + bias[i];
-        } else {  // CSA entry 0: no previous group
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { lg[j][i] = -INFINITY; v[j][i] = 0.f; }
-        }
+        for (int i = 0; i < 8; ++i) lg[j][i] = g[i] + bias[i] + pen;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -226,9 +226,33 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] *= inv;
   if (!lane_ok) return;
-  double f[4];
-  rope8_freq(f, c0, a.D, a.R, a.theta);
-  rope8(p, c0, a.D, a.R, entry_position(a.pos0, s, r), f, false);
+  const int64_t P = entry_position(a.pos0, s, r);
+  if (a.D == 512 && a.R == 64) {
+    // The V4 shape: every lane is here (lane_ok is the wave's entry_ok).  Lanes 0..31
+    // form the 32 pairs' cos / sin once into LDS, and the 8 lanes holding the last 64
+    // channels read theirs, instead of those 8 lanes forming 4 each (an fp64 pow and a
+    // sincosf apiece) while the rest of the wave waits.
+    __shared__ float2 ctab[4][32];
+    if (lane < 32) {
+      float c, sn;
+      rope_cos_sin(P, rope_inv_freq(lane, 64, a.theta), &c, &sn);
+      ctab[wave][lane] = make_float2(c, sn);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the table is read by other lanes
+    if (lane >= 56) {  // channels 448 + 8(lane - 56) ..: pairs 4(lane - 56) .. +3
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 cs = ctab[wave][4 * (lane - 56) + k];
+        const float x0 = p[2 * k], x1 = p[2 * k + 1];
+        p[2 * k] = x0 * cs.x - x1 * cs.y;
+        p[2 * k + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+  } else {
+    double f[4];
+    rope8_freq(f, c0, a.D, a.R, a.theta);
+    rope8(p, c0, a.D, a.R, P, f, false);
+  }
   store8<T>(static_cast<T*>(a.kv_c) + ((int64_t)b * a.n_entries + s) * a.D + c0, p);
 }
 
@@ -241,28 +265,81 @@ struct WindowArgs {
   int64_t pos0;
 };
 
+// Eight elements as loaded (one 16-byte vector for bf16, two for fp32), converted only
+// when used, so a load can stay in flight past the code that follows it.
+template <typename T>
+struct Raw8 {
+  Vec16<T> v[sizeof(T) / 2];
+};
+template <typename T>
+__device__ inline Raw8<T> load_raw8(const T* p) {
+  Raw8<T> r;
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 2); ++k) r.v[k] = load16(p + k * (16 / (int)sizeof(T)));
+  return r;
+}
+template <typename T>
+__device__ inline void unpack8(const Raw8<T>& r, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = to_f32(r.v[0].v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = r.v[0].v[i]; x[4 + i] = r.v[1].v[i]; }
+  }
+}
+
 // Raw window latents rotated at their own positions pos0 + t (optionally normalised
 // first).  One wave rotates WR_TOKENS consecutive tokens (one 16-byte chunk per lane per
 // token), so the inverse frequencies (an fp64 pow each) are worked out once per wave.
+// Rows are loaded one token ahead, into two alternating registers: a row is in flight
+// while the wave rotates and stores the one before (the compiler itself would not move
+// a load above a store to memory that may alias it).
+// FULL: D == 512 and R == 64 (the V4 layer shape).  Every lane holds 8 channels, so no
+// store is masked (a masked store sits behind a branch, and the compiler's wait for the
+// next row then also waits for it); and the wave's WR_TOKENS x 32 rotation angles are
+// formed once, four per lane with every lane busy, into an LDS table that the 8 lanes
+// holding the last 64 channels read, instead of those 8 lanes forming 32 each while
+// the rest of the wave waits.
 constexpr int WR_TOKENS = 8;
-template <typename T>
+template <typename T, bool FULL>
 __global__ __launch_bounds__(256) void window_rope_kernel(WindowArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * WR_TOKENS;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform
+  const int64_t tok0 = ((int64_t)blockIdx.x * 4 + wave) * WR_TOKENS;
   const int64_t total = (int64_t)a.B * a.S;
   if (tok0 >= total) return;
   const int c0 = lane * 8;
-  const bool lane_ok = c0 < a.D;
+  const bool lane_ok = FULL || c0 < a.D;
+  const int nt = (int)min((int64_t)WR_TOKENS, total - tok0);  // at least 1
+  // lanes past D read channel 0 of the row (their values are never stored); a token
+  // past nt reads token nt - 1 again
+  const T* src = static_cast<const T*>(a.kv_raw) + tok0 * a.D + (lane_ok ? c0 : 0);
+  T* dst = static_cast<T*>(a.kv_w) + tok0 * a.D + c0;
+  auto load_tok = [&](int j) { return load_raw8(src + (int64_t)min(j, nt - 1) * a.D); };
+  Raw8<T> ra = load_tok(0);
+  __shared__ float2 tab[4][FULL ? WR_TOKENS * 32 : 1];
   double f[4];
-  rope8_freq(f, c0, a.D, a.R, a.theta);
-  for (int j = 0; j < WR_TOKENS; ++j) {
-    const int64_t tok = tok0 + j;
-    if (tok >= total) break;  // wave-uniform
-    const int t = (int)(tok % a.S);
+  if constexpr (FULL) {
+    // entry 32 j + p: token j's cos / sin of pair p (lane l forms pair l % 32 of tokens
+    // l / 32 + 2m; a token past nt repeats token nt - 1)
+    const double fp = rope_inv_freq(lane & 31, 64, a.theta);
+#pragma unroll
+    for (int m = 0; m < WR_TOKENS / 2; ++m) {
+      const int j = (lane >> 5) + 2 * m;
+      float c, sn;
+      rope_cos_sin(a.pos0 + (tok0 + min(j, nt - 1)) % a.S, fp, &c, &sn);
+      tab[wave][32 * j + (lane & 31)] = make_float2(c, sn);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // the table is read by other lanes
+  } else {
+    rope8_freq(f, c0, a.D, a.R, a.theta);
+  }
+  auto rotate_store = [&](const Raw8<T>& r, int j) {
+    const int t = (int)((tok0 + j) % a.S);
     float x[8];
-    const int64_t off = tok * a.D + c0;
-    if (lane_ok) load8<T>(static_cast<const T*>(a.kv_raw) + off, x);
-    else {
+    unpack8(r, x);
+    if (!lane_ok) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = 0.f;
     }
@@ -275,10 +352,28 @@ __global__ __launch_bounds__(256) void window_rope_kernel(WindowArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] *= inv;
     }
-    if (lane_ok) {
+    if constexpr (FULL) {
+      if (lane >= 56) {  // channels 448 + 8(lane - 56) ..: pairs 4(lane - 56) .. +3
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float2 r = tab[wave][32 * j + 4 * (lane - 56) + k];
+          const float x0 = x[2 * k], x1 = x[2 * k + 1];
+          x[2 * k] = x0 * r.x - x1 * r.y;
+          x[2 * k + 1] = x0 * r.y + x1 * r.x;
+        }
+      }
+    } else {
+      // every lane rotates (lanes past D hold zeros), so only the store is masked
       rope8(x, c0, a.D, a.R, a.pos0 + t, f, false);
-      store8<T>(static_cast<T*>(a.kv_w) + off, x);
     }
+    if (lane_ok) store8<T>(dst + (int64_t)j * a.D, x);
+  };
+  for (int j = 0; j < nt; j += 2) {
+    const Raw8<T> rb = load_tok(j + 1);
+    rotate_store(ra, j);
+    if (j + 1 >= nt) break;
+    ra = load_tok(j + 2);
+    rotate_store(rb, j + 1);
   }
 }
 
@@ -308,8 +403,14 @@ hipError_t launch_window_rope(const csa_params_t& p, const void* kv_raw, void* k
   if (total == 0) return hipSuccess;
   const int64_t waves = ((int64_t)total + WR_TOKENS - 1) / WR_TOKENS;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  if (p.dtype == CSA_BF16) hipLaunchKernelGGL((window_rope_kernel<bf16>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((window_rope_kernel<float>), grid, block, 0, st, a);
+  const bool full = p.D == 512 && p.rope_dim == 64;
+  if (p.dtype == CSA_BF16) {
+    if (full) hipLaunchKernelGGL((window_rope_kernel<bf16, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((window_rope_kernel<bf16, false>), grid, block, 0, st, a);
+  } else {
+    if (full) hipLaunchKernelGGL((window_rope_kernel<float, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((window_rope_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
