@@ -291,6 +291,14 @@ EDGE = [
     dict(kind="hca", B=1, S=256, H=3, D=64, rope_dim=0, ratio=128, window=4, topk=0, dtype=wl.F32),
     # window-only layer, fp32
     dict(kind="swa", B=1, S=70, H=17, D=64, rope_dim=16, window=11, topk=0, dtype=wl.F32),
+    # the V4 shape (D 512, rope dim 64: the pooling and window kernels' LDS angle tables)
+    # at a ragged length: the last wave of the window kernel holds 4 tokens
+    dict(kind="csa", B=1, S=204, H=64, D=512, rope_dim=64, ratio=4, window=128, topk=32,
+         idx_heads=64, idx_dim=128, dtype=wl.BF16, pos0=77),
+    # the same, window-only and normalised, three batches of 37: window-kernel waves
+    # that cross a batch boundary, and a last wave of 7 tokens
+    dict(kind="swa", B=3, S=37, H=64, D=512, rope_dim=64, window=16, topk=0, dtype=wl.BF16,
+         norm_window=True),
 ]
 
 
