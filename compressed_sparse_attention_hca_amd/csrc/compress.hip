@@ -95,6 +95,9 @@ __device__ inline void rope8(float (&x)[8], int c0, int D, int R, int64_t P, con
 // pooling is otherwise bound by the accurate expf's instruction count.
 __device__ inline float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Lowest finite float: the online softmax's starting maximum.
+constexpr float kLowest = -3.40282346638528859812e+38f;
+
 // WPE = waves per entry (1: one entry per wave; 4: the workgroup splits one entry).
 template <typename T, int WPE>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
@@ -120,9 +123,12 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   const T* vb = static_cast<const T*>(a.vb);
   const T* gb = static_cast<const T*>(a.gb);
 
+  // m starts at the lowest finite float rather than -inf, so a slot with logit -inf leaves the online
+  // update below unchanged (scale 1, weight 0) instead of producing a NaN; for a real
+  // logit the first update gives the same values as from -inf (scale exactly 0).
   float m[8], l[8], acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { m[i] = -INFINITY; l[i] = 0.f; acc[i] = 0.f; }
+  for (int i = 0; i < 8; ++i) { m[i] = kLowest; l[i] = 0.f; acc[i] = 0.f; }
 
   if (WPE == 1 && span == 8) {
     // 8 slots (CSA at ratio 4): every load is issued first, then a two-pass softmax
@@ -163,18 +169,21 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       }
     }
   } else if (lane_ok) {
+    // Online softmax over the wave's slots, branch-free as above (a slot before token 0
+    // reads token 0 with logit -inf), unrolled so that several slots' loads are in flight.
+#pragma unroll 4
     for (int j = j0; j < j1; ++j) {
       const int tok = a.overlap ? s * r - r + j : s * r + j;
-      if (tok < 0) continue;  // CSA entry 0: no previous group
       const bool prev = a.overlap && j < r;
-      const int64_t off = ((int64_t)b * a.S + tok) * a.D + c0;
+      const int64_t off = ((int64_t)b * a.S + max(tok, 0)) * a.D + c0;
+      const float pen = tok >= 0 ? 0.f : -INFINITY;
       float g[8], v[8], bias[8];
       load8<T>((prev ? gb : ga) + off, g);
       load8<T>((prev ? vb : va) + off, v);
       load8<float>(a.bias + (int64_t)j * a.D + c0, bias);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float lg = g[i] + bias[i];
+        const float lg = g[i] + bias[i] + pen;
         const float mn = fmaxf(m[i], lg);
         const float sc = exp_fast(m[i] - mn);
         const float ex = exp_fast(lg - mn);
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
       for (int w = 0; w < WPE; ++w) {
         const float mw = part[w][0][i][lane];
-        const float f = (mw == -INFINITY) ? 0.f : exp_fast(mw - M);
+        const float f = (mw == kLowest) ? 0.f : exp_fast(mw - M);  // a wave with no slot: 0
         L += part[w][1][i][lane] * f;
         A += part[w][2][i][lane] * f;
       }
